@@ -1,0 +1,86 @@
+"""Pins for the oracle's block-sparse attention (blog page sections 4-5)
+against torch's scaled_dot_product_attention on the CPU in fp64."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_hand_example():
+    with open(os.path.join(GOLD, "attention_small.json")) as f:
+        g = json.load(f)
+    Q, K, V = (np.array(g[x], float) for x in "QKV")
+    for key in ("dense", "sparse"):
+        lists = [np.array(x) for x in g[key]["lists"]]
+        o, lse = O.sparse_attention(Q, K, V, lists, g["B"], scale=1.0)
+        np.testing.assert_allclose(o, g[key]["O"], atol=1e-14)
+        np.testing.assert_allclose(lse, g[key]["lse"], atol=1e-14)
+
+
+def _sdpa_masked(Q, K, V, mask, scale):
+    q = torch.from_numpy(Q)[None, None]
+    k = torch.from_numpy(K)[None, None]
+    v = torch.from_numpy(V)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=torch.from_numpy(mask)[None, None], scale=scale)
+    z = (torch.from_numpy(Q) @ torch.from_numpy(K).T) * scale
+    z = z.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    return o[0, 0].numpy(), torch.logsumexp(z, dim=1).numpy()
+
+
+@pytest.mark.parametrize("n,B,d", [(64, 8, 16), (70, 16, 8), (33, 32, 4)])
+def test_dense_lists_equal_causal_sdpa(n, B, d):
+    rng = np.random.default_rng(n + d)
+    Q, K, V = (rng.normal(size=(n, d)) for _ in range(3))
+    b = O.n_blocks(n, B)
+    lists = O.select(np.zeros((b, b)), 100)
+    o, lse = O.sparse_attention(Q, K, V, lists, B)
+    q = torch.from_numpy(Q)[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, torch.from_numpy(K)[None, None], torch.from_numpy(V)[None, None], is_causal=True)
+    np.testing.assert_allclose(o, ref[0, 0].numpy(), rtol=1e-12, atol=1e-12)
+    mask = np.tril(np.ones((n, n), bool))
+    _, lse_ref = _sdpa_masked(Q, K, V, mask, 1 / math.sqrt(d))
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sparse_lists_equal_masked_sdpa(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.choice([4, 8]))
+    n = int(rng.integers(B, 12 * B))
+    d = 8
+    Q, K, V = (rng.normal(size=(n, d)) for _ in range(3))
+    b = O.n_blocks(n, B)
+    R = O.rownorm(np.tril(rng.normal(size=(b, b))))
+    lists = O.select(R, int(rng.integers(0, 60)))
+    mask = np.zeros((n, n), bool)
+    for i, lst in enumerate(lists):
+        for j in lst:
+            mask[i * B:(i + 1) * B, j * B:(j + 1) * B] = True
+    mask &= np.tril(np.ones((n, n), bool))
+    o, lse = O.sparse_attention(Q, K, V, lists, B)
+    o_ref, lse_ref = _sdpa_masked(Q, K, V, mask, 1 / math.sqrt(d))
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_single_block_list_is_plain_attention_over_that_block():
+    rng = np.random.default_rng(1)
+    B, d = 8, 4
+    Q, K, V = (rng.normal(size=(40, d)) for _ in range(3))
+    lists = [np.array([i]) for i in range(5)]
+    o, _ = O.sparse_attention(Q, K, V, lists, B)
+    for i in range(5):
+        sl = slice(i * B, (i + 1) * B)
+        z = Q[sl] @ K[sl].T / 2.0
+        z = np.where(np.tril(np.ones((B, B), bool)), z, -np.inf)
+        p = np.exp(z - z.max(1, keepdims=True))
+        np.testing.assert_allclose(o[sl], (p / p.sum(1, keepdims=True)) @ V[sl], atol=1e-13)

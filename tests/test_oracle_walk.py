@@ -1,0 +1,124 @@
+"""Pins for the oracle's walk state (blog page section 4)."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import gen
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lower(rng, b, diag_boost=0.0):
+    return np.tril(rng.normal(size=(b, b))) + diag_boost * np.eye(b)
+
+
+def test_walk_hand_cases():
+    with open(os.path.join(GOLD, "walk_small.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        Rp = None if c["R_prev"] is None else np.array(c["R_prev"], float)
+        got = O.walk_update(Rp, np.array(c["M"], float), c["s"])
+        np.testing.assert_allclose(got, c["R"], atol=1e-15)
+
+
+@pytest.mark.parametrize("b,s", [(3, 1), (4, 2), (5, 3), (6, 2)])
+def test_walk_is_sum_over_causal_paths(b, s):
+    """(M^s)[i, m] = sum over block paths i = j0 >= j1 >= ... >= js = m of the
+    product of scores, enumerated by brute force."""
+    rng = np.random.default_rng(b * 10 + s)
+    M = _lower(rng, b)
+    P = np.zeros((b, b))
+    for path in itertools.product(range(b), repeat=s + 1):
+        if all(path[t + 1] <= path[t] for t in range(s)):
+            w = 1.0
+            for t in range(s):
+                w *= M[path[t], path[t + 1]]
+            P[path[0], path[-1]] += w
+    np.testing.assert_allclose(O.walk_update(None, M, s), O.rownorm(P), rtol=1e-12, atol=1e-12)
+
+
+def test_eight_hops_equal_repeated_squaring():
+    rng = np.random.default_rng(2)
+    M = _lower(rng, 12, 1.5)
+    M2 = M @ M
+    M8 = (M2 @ M2) @ (M2 @ M2)
+    np.testing.assert_allclose(O.walk_update(None, M, 8), O.rownorm(M8), rtol=1e-10, atol=1e-12)
+
+
+def test_one_hop_one_layer_is_rownormed_scores():
+    rng = np.random.default_rng(4)
+    M = _lower(rng, 9)
+    np.testing.assert_allclose(O.walk_update(None, M, 1), O.rownorm(M), atol=1e-15)
+    assert np.allclose(np.abs(O.walk_update(None, M, 1)).max(axis=1), 1.0)
+
+
+def test_layerwise_normalisation_commutes():
+    """Normalising rows after every layer gives the same state as one
+    normalisation of the raw product R^(-1) M_0^s M_1^s M_2^s."""
+    rng = np.random.default_rng(6)
+    Ms = [_lower(rng, 10, 1.0) for _ in range(3)]
+    R = None
+    raw = np.eye(10)
+    for M in Ms:
+        R = O.walk_update(R, M, 3)
+        raw = raw @ np.linalg.matrix_power(M, 3)
+    np.testing.assert_allclose(R, O.rownorm(raw), rtol=1e-10, atol=1e-12)
+
+
+def test_diagonal_scores_keep_state_diagonal_and_lower_triangular():
+    rng = np.random.default_rng(8)
+    D = np.diag(rng.normal(size=7))
+    R = O.walk_update(None, D, 5)
+    assert np.count_nonzero(R - np.diag(np.diag(R))) == 0
+    R2 = O.walk_update(R, _lower(rng, 7), 4)
+    assert np.count_nonzero(np.triu(R2, 1)) == 0
+
+
+def test_walk_row_equals_matrix_row():
+    rng = np.random.default_rng(9)
+    M = _lower(rng, 11, 0.5)
+    R = O.walk_update(None, M, 8)
+    for i in range(11):
+        np.testing.assert_allclose(O.walk_row(None, M, i, 8), R[i], rtol=1e-12, atol=1e-13)
+    M2 = _lower(rng, 11, 0.5)
+    R2 = O.walk_update(R, M2, 8)
+    for i in (0, 5, 10):
+        np.testing.assert_allclose(O.walk_row(R[i], M2, i, 8), R2[i], rtol=1e-12, atol=1e-13)
+
+
+def test_positive_scaling_of_queries_keeps_selection():
+    cfg = gen.CONFIGS["C1"]
+    q, k, v, _ = gen.layer_inputs(cfg, 0)
+    Q = q[:, 0].double().numpy()
+    K = k[:, 0].double().numpy()
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    lists = []
+    for c in (1.0, 3.7):
+        M = O.sketched_scores(O.sketch(c * Q, cfg.B, signs, cols), O.sketch(K, cfg.B, signs, cols))
+        lists.append(O.select(O.walk_update(None, M, cfg.s), cfg.rho))
+    for a, b in zip(*lists):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_planted_two_hop_chain_reached_by_walk():
+    """Generator sanity: for a chain i -> j -> m the walk row of block i puts
+    m above the median of its candidates although the direct score
+    M[i, m] carries no planted term."""
+    cfg = gen.CONFIGS["C2"].with_(seqlens=(4096,), hq=8, hkv=2)
+    q, k, _, _ = gen.layer_inputs(cfg, 0)
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    Q = q[:, 0].double().numpy()
+    K = k[:, 0].double().numpy()
+    M = O.sketched_scores(O.sketch(Q, cfg.B, signs, cols), O.sketch(K, cfg.B, signs, cols))
+    R = O.walk_update(None, M, 2)
+    # chain 0 of group 0 (persistent): recover its blocks from the generator's own draw
+    import numpy.random as npr
+    b = O.n_blocks(4096, cfg.B)
+    r = npr.default_rng(gen.seed_for(cfg.cfg_id, 5, 0, 0, 0, 0xFFFF))
+    i, j, m = sorted(r.choice(b, size=3, replace=False).tolist(), reverse=True)
+    assert R[i, j] > np.median(R[i, :i])
+    assert R[i, m] > np.median(R[i, :i])
