@@ -1,0 +1,243 @@
+// Top-tau key-block selection per query block (blog page "Scout Before You
+// Attend", section 4: the tau best blocks from the query block's row of the
+// walk state; the diagonal block is always kept).
+//
+// One wavefront owns one row.  Scores become order-preserving unsigned keys
+// (-0 folded onto +0 first), held in registers, 64 candidates per register.
+// The tau-th largest key T is found by a most-significant-bit-first search,
+// each step counting keys >= candidate with wave ballots.  Then every key > T
+// is kept, plus the lowest-index keys equal to T until tau are kept; the
+// kept indices are compacted in ascending order with ballot prefix counts, so
+// the result is exactly the (score descending, index ascending) top tau.
+#include "sws_common.h"
+
+namespace sws {
+namespace {
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const float y = (x == 0.0f) ? 0.0f : x;   // -0 -> +0
+  const uint32_t u = __float_as_uint(y);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Selection flags for row values row[0 .. n) (n candidates), keeping tau of
+// them.  key[] holds the keys of candidates e * 64 + lane (0 if absent).
+// Returns the threshold and the number of threshold ties to keep.
+template <int E>
+__device__ __forceinline__ void threshold(const uint32_t (&key)[E], int n, int tau,
+                                          uint32_t& T, int& need_eq) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e * 64 < n) c += popc64(__ballot(key[e] >= cand));
+    }
+    if (c >= tau) t = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e * 64 < n) gt += popc64(__ballot(key[e] > t));
+  }
+  T = t;
+  need_eq = tau - gt;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ R, int hq,
+                                                     const int32_t* __restrict__ cu_blocks,
+                                                     int n_seqs, int total_blocks, int rho,
+                                                     int dense, int width,
+                                                     int32_t* __restrict__ idx,
+                                                     int32_t* __restrict__ cnt) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int b0 = cu_blocks[seq];
+  const int b = cu_blocks[seq + 1] - b0;
+  if (i >= b) return;
+  const int gb = b0 + i;
+  int32_t* out = idx + ((int64_t)h * total_blocks + gb) * width;
+  const int tau = (int)(((int64_t)rho * b) / 100);
+  if (dense || i <= tau) {
+    for (int m = lane; m <= i; m += 64) out[m] = m;
+    if (lane == 0) cnt[(int64_t)h * total_blocks + gb] = i + 1;
+    return;
+  }
+  const float* row = R + walk_seq_offset(cu_blocks, seq, hq) + ((int64_t)h * b + i) * b;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int m = e * 64 + lane;
+    key[e] = (m < i) ? order_key(row[m]) : 0u;
+  }
+  uint32_t T;
+  int need;
+  threshold<E>(key, i, tau, T, need);
+  int base = 0, eq_seen = 0;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e * 64 < i) {
+      const int m = e * 64 + lane;
+      const bool valid = m < i;
+      const bool eq = valid && key[e] == T;
+      const uint64_t eqm = __ballot(eq);
+      const bool sel = valid && (key[e] > T || (eq && eq_seen + popc64(eqm & lt) < need));
+      eq_seen += popc64(eqm);
+      const uint64_t sm = __ballot(sel);
+      if (sel) out[base + popc64(sm & lt)] = m;
+      base += popc64(sm);
+    }
+  }
+  if (lane == 0) {
+    out[tau] = i;
+    cnt[(int64_t)h * total_blocks + gb] = tau + 1;
+  }
+}
+
+// Decode: the open block c of each sequence; one workgroup per (sequence, KV
+// group), one wave per query head of the group; union through an LDS mask.
+constexpr int kRowBmax = 8192;
+
+template <int E>
+__global__ __launch_bounds__(1024) void select_row_kernel(
+    const float* __restrict__ r, int hq, int hkv, const int32_t* __restrict__ cur_block,
+    int b_max, int rho, int dense, int width, int32_t* __restrict__ idx,
+    int32_t* __restrict__ cnt, int32_t* __restrict__ union_idx,
+    int32_t* __restrict__ union_cnt, uint32_t* __restrict__ union_mask, int union_width) {
+  __shared__ uint32_t umask[kRowBmax];
+  const int g = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int G = hq / hkv;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nthreads = blockDim.x;
+  const int c = cur_block[seq];
+  const int b = c + 1;
+  const int tau = (int)(((int64_t)rho * b) / 100);
+  const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
+  for (int m = threadIdx.x; m < b; m += nthreads) umask[m] = (dense || m == c) ? all : 0u;
+  __syncthreads();
+  if (w < G && !dense) {
+    const int h = g * G + w;
+    int32_t* out = idx ? idx + ((int64_t)seq * hq + h) * width : nullptr;
+    if (c <= tau) {
+      for (int m = lane; m < c; m += 64) atomicOr(&umask[m], 1u << w);
+      if (out) for (int m = lane; m <= c; m += 64) out[m] = m;
+      if (out && lane == 0) cnt[(int64_t)seq * hq + h] = c + 1;
+    } else {
+      const float* row = r + ((int64_t)seq * hq + h) * b_max;
+      uint32_t key[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int m = e * 64 + lane;
+        key[e] = (m < c) ? order_key(row[m]) : 0u;
+      }
+      uint32_t T;
+      int need;
+      threshold<E>(key, c, tau, T, need);
+      int base = 0, eq_seen = 0;
+      const uint64_t lt = lanemask_lt();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (e * 64 < c) {
+          const int m = e * 64 + lane;
+          const bool valid = m < c;
+          const bool eq = valid && key[e] == T;
+          const uint64_t eqm = __ballot(eq);
+          const bool sel = valid && (key[e] > T || (eq && eq_seen + popc64(eqm & lt) < need));
+          eq_seen += popc64(eqm);
+          const uint64_t sm = __ballot(sel);
+          if (sel) {
+            atomicOr(&umask[m], 1u << w);
+            if (out) out[base + popc64(sm & lt)] = m;
+          }
+          base += popc64(sm);
+        }
+      }
+      if (out && lane == 0) {
+        out[tau] = c;
+        cnt[(int64_t)seq * hq + h] = tau + 1;
+      }
+    }
+  } else if (w < G && dense && idx) {
+    const int h = g * G + w;
+    int32_t* out = idx + ((int64_t)seq * hq + h) * width;
+    for (int m = lane; m <= c; m += 64) out[m] = m;
+    if (lane == 0) cnt[(int64_t)seq * hq + h] = c + 1;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int32_t* uo = union_idx + ((int64_t)seq * hkv + g) * union_width;
+    uint32_t* um = union_mask + ((int64_t)seq * hkv + g) * union_width;
+    const uint64_t lt = lanemask_lt();
+    int base = 0;
+    for (int m0 = 0; m0 < b; m0 += 64) {
+      const int m = m0 + lane;
+      const uint32_t mk = (m < b) ? umask[m] : 0u;
+      const uint64_t bm = __ballot(mk != 0u);
+      if (mk) {
+        const int p = base + popc64(bm & lt);
+        uo[p] = m;
+        um[p] = mk;
+      }
+      base += popc64(bm);
+    }
+    if (lane == 0) union_cnt[(int64_t)seq * hkv + g] = base;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const float* R, int hq, const int32_t* cu_blocks, int n_seqs,
+                         int total_blocks, int max_blocks, int rho, int dense, int width,
+                         int32_t* idx, int32_t* cnt, hipStream_t st) {
+  if (total_blocks == 0 || max_blocks == 0) return hipSuccess;
+  dim3 grid((max_blocks + 3) / 4, hq, n_seqs);
+  if (max_blocks <= 256)
+    hipLaunchKernelGGL((select_kernel<4>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
+                       total_blocks, rho, dense, width, idx, cnt);
+  else if (max_blocks <= 1024)
+    hipLaunchKernelGGL((select_kernel<16>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
+                       total_blocks, rho, dense, width, idx, cnt);
+  else
+    hipLaunchKernelGGL((select_kernel<64>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
+                       total_blocks, rho, dense, width, idx, cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_row(const float* r, int hq, int hkv, int n_seqs,
+                             const int32_t* cur_block, int b_max, int rho, int dense, int width,
+                             int32_t* idx, int32_t* cnt, int32_t* union_idx, int32_t* union_cnt,
+                             uint32_t* union_mask, int union_width, hipStream_t st) {
+  if (n_seqs == 0) return hipSuccess;
+  const int G = hq / hkv;
+  dim3 grid(hkv, n_seqs);
+  dim3 block(64 * G);
+  if (b_max <= 1024)
+    hipLaunchKernelGGL((select_row_kernel<16>), grid, block, 0, st, r, hq, hkv, cur_block, b_max,
+                       rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,
+                       union_width);
+  else if (b_max <= 4096)
+    hipLaunchKernelGGL((select_row_kernel<64>), grid, block, 0, st, r, hq, hkv, cur_block, b_max,
+                       rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,
+                       union_width);
+  else
+    hipLaunchKernelGGL((select_row_kernel<128>), grid, block, 0, st, r, hq, hkv, cur_block,
+                       b_max, rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,
+                       union_width);
+  return hipGetLastError();
+}
+
+}  // namespace sws

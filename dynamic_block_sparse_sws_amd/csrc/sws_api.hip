@@ -1,0 +1,282 @@
+// C ABI of the Sketch&Walk library: host-side argument validation (before any
+// HIP call), dispatch to the kernel launchers, error reporting.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sws_common.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return code;
+}
+
+int ok() {
+  g_detail.clear();
+  return SWS_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SWS_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int dt) { return dt == SWS_F32 || dt == SWS_BF16; }
+
+int tau_of(int rho, int b) { return (int)(((int64_t)rho * b) / 100); }
+
+}  // namespace
+
+#define REQUIRE_PTR(p) \
+  if (!(p)) return fail(SWS_ERR_NULL, "%s: argument '%s' is NULL", fn, #p)
+
+extern "C" {
+
+int sws_version(void) { return 100; }
+
+const char* sws_status_string(int status) {
+  switch (status) {
+    case SWS_OK: return "SWS_OK";
+    case SWS_ERR_NULL: return "SWS_ERR_NULL";
+    case SWS_ERR_SHAPE: return "SWS_ERR_SHAPE";
+    case SWS_ERR_UNSUPPORTED: return "SWS_ERR_UNSUPPORTED";
+    case SWS_ERR_WORKSPACE: return "SWS_ERR_WORKSPACE";
+    case SWS_ERR_LAUNCH: return "SWS_ERR_LAUNCH";
+    default: return "SWS_ERR_UNKNOWN";
+  }
+}
+
+const char* sws_last_error_detail(void) { return g_detail.c_str(); }
+
+int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
+               int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
+               int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
+               int64_t ld_head, float* sum_out, void* stream) {
+  const char* fn = "sws_sketch";
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(cu_seqlens);
+  REQUIRE_PTR(cu_blocks);
+  REQUIRE_PTR(signs);
+  REQUIRE_PTR(cols);
+  REQUIRE_PTR(sketch_out);
+  if (!dtype_ok(dtype)) return fail(SWS_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
+  if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
+  if (k < 1 || k > d || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1, min(d,64)]", fn, k);
+  if (n_seqs < 1 || total_blocks < 0 || n_heads < 1)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d n_heads=%d", fn, n_seqs, total_blocks, n_heads);
+  if (ld_head < (int64_t)total_blocks * k)
+    return fail(SWS_ERR_SHAPE, "%s: ld_head=%lld < total_blocks*k", fn, (long long)ld_head);
+  if (!aligned16(x)) return fail(SWS_ERR_SHAPE, "%s: x is not 16-byte aligned", fn);
+  return launched(sws::launch_sketch(x, dtype, cu_seqlens, cu_blocks, n_seqs, total_blocks,
+                                     n_heads, d, B, k, signs, cols, sketch_out, ld_head, sum_out,
+                                     (hipStream_t)stream),
+                  fn);
+}
+
+int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t n_seqs,
+                      int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
+                      const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
+                      void* stream) {
+  const char* fn = "sws_sketch_append";
+  REQUIRE_PTR(x_new);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(signs);
+  REQUIRE_PTR(cols);
+  REQUIRE_PTR(run_sum);
+  REQUIRE_PTR(sketch_cache);
+  if (!dtype_ok(dtype)) return fail(SWS_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
+  if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
+  if (k < 1 || k > d || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1, min(d,64)]", fn, k);
+  if (n_seqs < 0 || n_heads < 1 || b_max < 1)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d n_heads=%d b_max=%d", fn, n_seqs, n_heads, b_max);
+  if (!aligned16(x_new) || !aligned16(run_sum))
+    return fail(SWS_ERR_SHAPE, "%s: x_new / run_sum not 16-byte aligned", fn);
+  return launched(sws::launch_sketch_append(x_new, dtype, pos, n_seqs, n_heads, d, B, k, signs,
+                                            cols, run_sum, sketch_cache, b_max,
+                                            (hipStream_t)stream),
+                  fn);
+}
+
+int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv, int32_t k,
+                    const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
+                    int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
+                    void* stream) {
+  const char* fn = "sws_walk_update";
+  REQUIRE_PTR(q_sk);
+  REQUIRE_PTR(k_sk);
+  REQUIRE_PTR(cu_blocks);
+  REQUIRE_PTR(R_out);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
+  if (n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d max_blocks=%d", fn, n_seqs, total_blocks, max_blocks);
+  if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
+  return launched(sws::launch_walk(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks,
+                                   max_blocks, s, R_prev, R_out, (hipStream_t)stream),
+                  fn);
+}
+
+int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                        int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
+                        int32_t b_max, int32_t s, const float* r_prev, float* r_out,
+                        void* stream) {
+  const char* fn = "sws_walk_update_row";
+  REQUIRE_PTR(q_sk_cache);
+  REQUIRE_PTR(k_sk_cache);
+  REQUIRE_PTR(cur_block);
+  REQUIRE_PTR(r_out);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
+  if (n_seqs < 0 || b_max < 1 || b_max > 8192)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,8192])", fn, n_seqs, b_max);
+  if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
+  return launched(sws::launch_walk_row(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs, cur_block,
+                                       b_max, s, r_prev, r_out, (hipStream_t)stream),
+                  fn);
+}
+
+int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
+                    int32_t total_blocks, int32_t max_blocks, int32_t rho_percent, int32_t dense,
+                    int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
+  const char* fn = "sws_select_topk";
+  if (!dense) REQUIRE_PTR(R);
+  REQUIRE_PTR(cu_blocks);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(cnt);
+  if (hq < 1 || n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d n_seqs=%d total_blocks=%d max_blocks=%d", fn, hq, n_seqs, total_blocks, max_blocks);
+  if (max_blocks > 4096) return fail(SWS_ERR_UNSUPPORTED, "%s: max_blocks=%d > 4096", fn, max_blocks);
+  if (rho_percent < 0 || rho_percent > 100)
+    return fail(SWS_ERR_SHAPE, "%s: rho_percent=%d outside [0,100]", fn, rho_percent);
+  const int need = dense ? max_blocks : std::min(max_blocks, tau_of(rho_percent, max_blocks) + 1);
+  if (width < need || width < 1)
+    return fail(SWS_ERR_SHAPE, "%s: width=%d < required %d", fn, width, need);
+  return launched(sws::launch_select(R, hq, cu_blocks, n_seqs, total_blocks, max_blocks,
+                                     rho_percent, dense, width, idx, cnt, (hipStream_t)stream),
+                  fn);
+}
+
+int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
+                        const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
+                        int32_t dense, int32_t width, int32_t* idx, int32_t* cnt,
+                        int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
+                        int32_t union_width, void* stream) {
+  const char* fn = "sws_select_topk_row";
+  if (!dense) REQUIRE_PTR(r);
+  REQUIRE_PTR(cur_block);
+  REQUIRE_PTR(union_idx);
+  REQUIRE_PTR(union_cnt);
+  REQUIRE_PTR(union_mask);
+  if ((idx == nullptr) != (cnt == nullptr))
+    return fail(SWS_ERR_NULL, "%s: idx and cnt must both be set or both be NULL", fn);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (hq / hkv > 16) return fail(SWS_ERR_UNSUPPORTED, "%s: hq/hkv=%d > 16", fn, hq / hkv);
+  if (n_seqs < 0 || b_max < 1 || b_max > 8192)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,8192])", fn, n_seqs, b_max);
+  if (rho_percent < 0 || rho_percent > 100)
+    return fail(SWS_ERR_SHAPE, "%s: rho_percent=%d outside [0,100]", fn, rho_percent);
+  const int tmax = tau_of(rho_percent, b_max);
+  const int need = dense ? b_max : std::min(b_max, tmax + 1);
+  const int uneed = dense ? b_max : std::min(b_max, (hq / hkv) * tmax + 1);
+  if (idx && width < need) return fail(SWS_ERR_SHAPE, "%s: width=%d < required %d", fn, width, need);
+  if (union_width < uneed)
+    return fail(SWS_ERR_SHAPE, "%s: union_width=%d < required %d", fn, union_width, uneed);
+  return launched(sws::launch_select_row(r, hq, hkv, n_seqs, cur_block, b_max, rho_percent,
+                                         dense, width, idx, cnt, union_idx, union_cnt,
+                                         union_mask, union_width, (hipStream_t)stream),
+                  fn);
+}
+
+int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
+                            const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
+                            int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
+                            int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
+                            int32_t width, float scale, void* out, float* lse, void* stream) {
+  const char* fn = "sws_sparse_attn_prefill";
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(cu_seqlens);
+  REQUIRE_PTR(cu_blocks);
+  REQUIRE_PTR(out);
+  if (idx && !cnt) return fail(SWS_ERR_NULL, "%s: idx given without cnt", fn);
+  if (!dtype_ok(dtype)) return fail(SWS_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
+  if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d max_blocks=%d", fn, n_seqs, total_blocks, max_blocks);
+  if ((int64_t)total_blocks * hq > 0x7fffffffLL)
+    return fail(SWS_ERR_SHAPE, "%s: total_blocks*hq too large", fn);
+  if (idx && width < 1) return fail(SWS_ERR_SHAPE, "%s: width=%d", fn, width);
+  if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(SWS_ERR_SHAPE, "%s: q/k/v/out must be 16-byte aligned", fn);
+  return launched(sws::launch_attn_prefill(q, k, v, dtype, cu_seqlens, cu_blocks, n_seqs,
+                                           total_blocks, max_blocks, hq, hkv, d, B, idx, cnt,
+                                           width, scale, out, lse, (hipStream_t)stream),
+                  fn);
+}
+
+size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                 int32_t union_width) {
+  if (n_seqs < 0 || hq < 1 || (d != 64 && d != 128) || (B != 64 && B != 128) || union_width < 0)
+    return 0;
+  return sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, union_width);
+}
+
+int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                           const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
+                           int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
+                           const int32_t* union_cnt, const uint32_t* union_mask,
+                           int32_t union_width, float scale, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  const char* fn = "sws_sparse_attn_decode";
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(ctx_len);
+  REQUIRE_PTR(out);
+  if (union_idx && (!union_cnt || !union_mask))
+    return fail(SWS_ERR_NULL, "%s: union_idx given without union_cnt / union_mask", fn);
+  if (!dtype_ok(dtype)) return fail(SWS_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
+  if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (hq / hkv > 16) return fail(SWS_ERR_UNSUPPORTED, "%s: hq/hkv=%d > 16", fn, hq / hkv);
+  if (n_seqs < 0 || max_ctx < 1)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d max_ctx=%d", fn, n_seqs, max_ctx);
+  const int uw = union_idx ? union_width : (max_ctx + B - 1) / B;
+  if (union_idx && union_width < 1) return fail(SWS_ERR_SHAPE, "%s: union_width=%d", fn, union_width);
+  if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(SWS_ERR_SHAPE, "%s: q/k_cache/v_cache must be 16-byte aligned", fn);
+  const size_t need = sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, uw);
+  if (!ws || ws_bytes < need)
+    return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+  return launched(sws::launch_attn_decode(q, k_cache, v_cache, dtype, ctx_len, n_seqs, max_ctx,
+                                          hq, hkv, d, B, union_idx, union_cnt, union_mask, uw,
+                                          scale, out, lse, ws, (hipStream_t)stream),
+                  fn);
+}
+
+}  // extern "C"

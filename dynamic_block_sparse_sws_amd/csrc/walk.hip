@@ -1,0 +1,355 @@
+// Walk state (blog page "Scout Before You Attend", section 4):
+//   R^l = rownorm(R^(l-1) M^s),  M[i][j] = qs_i . ks_j / sqrt(k) for j <= i.
+//
+// Rows of R are independent, and one hop of a row is the product of a row
+// vector with the lower-triangular rank-k matrix M, which factorises into a
+// suffix scan:
+//   y[m] = ks_m . S_m / sqrt(k),   S_m = sum_{j >= m} x[j] qs_j.
+// So a hop costs 2 b k multiply-adds per row instead of b^2, and the walk of
+// all b rows costs s b^2 k per head instead of forming M^s.
+//
+// Prefill: a workgroup owns a chunk of rows of one head and runs all s hops
+// on them, streaming the rows through LDS tile by tile from the last column
+// down (the scan order), overwriting each tile in place in R_out.  Lanes of a
+// row split the k components of S and combine their partial dot products with
+// cross-lane shuffles.  Every hop rescales its rows by their largest
+// magnitude (positive row scaling commutes with the right-multiplication, so
+// only the final division is visible), which keeps s * layers hops in fp32.
+//
+// Decode: one workgroup per (sequence, query head) walks the single row of
+// the open block; the j range is cut into segments, one per lane group, with
+// the segment's sketch rows held in registers for all s hops, and the suffix
+// carry across segments comes from a wave scan plus an LDS scan of the wave
+// totals.
+#include "sws_common.h"
+
+namespace sws {
+namespace {
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  // sum over the LPR consecutive lanes of a row (LPR in {2, 4, 8})
+  v += __shfl_xor(v, 1);
+  if (LPR >= 4) v += __shfl_xor(v, 2);
+  if (LPR >= 8) v += __shfl_xor(v, 4);
+  return v;
+}
+
+constexpr int kWalkThreads = 256;
+constexpr int kTileJ = 64;
+
+template <int KP>
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(
+    const float* __restrict__ q_sk, const float* __restrict__ k_sk, int hq, int hkv, int k,
+    const int32_t* __restrict__ cu_blocks, int n_seqs, int total_blocks, int s,
+    const float* R_prev, float* R_out, float inv_sqrt_k) {
+  constexpr int LPR = KP / 8;                  // lanes per row
+  constexpr int ROWS = kWalkThreads / LPR;     // rows per workgroup
+  __shared__ __attribute__((aligned(16))) float sq[kTileJ][KP + 4];
+  __shared__ __attribute__((aligned(16))) float sk[kTileJ][KP + 4];
+  __shared__ float sx[ROWS][kTileJ + 1];
+  __shared__ float smax[ROWS];
+
+  const int seq = blockIdx.z;
+  const int h = blockIdx.y;
+  const int b0 = cu_blocks[seq];
+  const int b = cu_blocks[seq + 1] - b0;
+  const int i0 = blockIdx.x * ROWS;
+  if (i0 >= b) return;
+  const int64_t roff = walk_seq_offset(cu_blocks, seq, hq) + (int64_t)h * b * b;
+  float* Rh = R_out + roff;
+  const float* Rp = R_prev ? R_prev + roff : nullptr;
+  const int grp = hq / hkv;
+  const float* qs = q_sk + ((int64_t)h * total_blocks + b0) * k;
+  const float* ks = k_sk + ((int64_t)(h / grp) * total_blocks + b0) * k;
+
+  const int tid = threadIdx.x;
+  const int r = tid / LPR;
+  const int part = tid % LPR;
+  const int i = i0 + r;
+  const int jmax = min(b, i0 + ROWS) - 1;
+  const int top_tile = (jmax / kTileJ) * kTileJ;
+
+  float sc = 1.0f;   // rescale of this row's input for the current hop
+  float mx = 0.0f;
+  for (int hop = 0; hop < s; ++hop) {
+    const float* src = (hop == 0) ? Rp : Rh;
+    const bool ident = (hop == 0) && (Rp == nullptr);
+    float S[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) S[c] = 0.f;
+    mx = 0.0f;
+    for (int jt = top_tile; jt >= 0; jt -= kTileJ) {
+      __syncthreads();
+      // stage sketch rows jt .. jt + 63 (zero beyond the sequence / beyond k)
+      for (int e = tid; e < kTileJ * KP; e += kWalkThreads) {
+        const int jj = e / KP, c = e % KP;
+        const int j = jt + jj;
+        const bool ok = (j < b) && (c < k);
+        sq[jj][c] = ok ? qs[(int64_t)j * k + c] : 0.f;
+        sk[jj][c] = ok ? ks[(int64_t)j * k + c] : 0.f;
+      }
+      // stage the X tile: rows i0 .. i0 + ROWS - 1, columns jt .. jt + 63
+      for (int e = tid; e < ROWS * kTileJ; e += kWalkThreads) {
+        const int rr = e / kTileJ, jj = e % kTileJ;
+        const int ii = i0 + rr, j = jt + jj;
+        float v = 0.f;
+        if (ii < b && j <= ii) {
+          if (ident) v = (j == ii) ? 1.f : 0.f;
+          else v = src[(int64_t)ii * b + j];
+        }
+        sx[rr][jj] = v;
+      }
+      __syncthreads();
+      for (int jj = kTileJ - 1; jj >= 0; --jj) {
+        const float x = sx[r][jj] * sc;
+        const float4 qa = *reinterpret_cast<const float4*>(&sq[jj][part * 8]);
+        const float4 qb = *reinterpret_cast<const float4*>(&sq[jj][part * 8 + 4]);
+        const float4 ka = *reinterpret_cast<const float4*>(&sk[jj][part * 8]);
+        const float4 kb = *reinterpret_cast<const float4*>(&sk[jj][part * 8 + 4]);
+        S[0] += x * qa.x; S[1] += x * qa.y; S[2] += x * qa.z; S[3] += x * qa.w;
+        S[4] += x * qb.x; S[5] += x * qb.y; S[6] += x * qb.z; S[7] += x * qb.w;
+        float y = ka.x * S[0] + ka.y * S[1] + ka.z * S[2] + ka.w * S[3] +
+                  kb.x * S[4] + kb.y * S[5] + kb.z * S[6] + kb.w * S[7];
+        y = group_sum<LPR>(y) * inv_sqrt_k;
+        if (part == 0) sx[r][jj] = y;
+        mx = fmaxf(mx, fabsf(y));
+      }
+      __syncthreads();
+      for (int e = tid; e < ROWS * kTileJ; e += kWalkThreads) {
+        const int rr = e / kTileJ, jj = e % kTileJ;
+        const int ii = i0 + rr, j = jt + jj;
+        if (ii < b && j <= ii) Rh[(int64_t)ii * b + j] = sx[rr][jj];
+      }
+    }
+    sc = (mx > 0.f) ? 1.0f / mx : 1.0f;
+  }
+  if (part == 0) smax[r] = mx;
+  __syncthreads();
+  // final pass: divide by the row maximum, zero the upper triangle
+  for (int rr = 0; rr < ROWS; ++rr) {
+    const int ii = i0 + rr;
+    if (ii >= b) break;
+    const float m = smax[rr];
+    float* row = Rh + (int64_t)ii * b;
+    for (int j = tid; j < b; j += kWalkThreads) {
+      float v = 0.f;
+      if (j <= ii && m > 0.f) v = row[j] / m;
+      row[j] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode: one row per (sequence, query head)
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 1024;
+constexpr int kRowLmax = 5;     // sketch rows per segment held in registers
+constexpr int kRowBmax = 8192;
+
+template <int KP>
+__global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
+    const float* __restrict__ q_cache, const float* __restrict__ k_cache, int hq, int hkv,
+    int k, const int32_t* __restrict__ cur_block, int b_max, int s, const float* r_prev,
+    float* r_out, float inv_sqrt_k) {
+  constexpr int LPR = KP / 8;
+  constexpr int NSEG = kRowThreads / LPR;
+  constexpr int SPW = 64 / LPR;              // segments per wave
+  constexpr int NWAVE = kRowThreads / 64;
+  __shared__ float xs[kRowBmax];
+  __shared__ float wtot[NWAVE][KP];
+  __shared__ float wmax[NWAVE];
+
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int grp = hq / hkv;
+  const int c = cur_block[seq];
+  const int b = c + 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int seg = tid / LPR;
+  const int seg_in_wave = lane / LPR;
+  const int part = tid % LPR;
+  const int L = (b + NSEG - 1) / NSEG;
+  const int j0 = min(b, seg * L);
+  const int j1 = min(b, j0 + L);
+  const bool in_regs = (L <= kRowLmax);
+
+  const float* qrow = q_cache + ((int64_t)seq * hq + h) * b_max * k;
+  const float* krow = k_cache + ((int64_t)seq * hkv + h / grp) * b_max * k;
+  const float* rin = r_prev ? r_prev + ((int64_t)seq * hq + h) * b_max : nullptr;
+  float* rout = r_out + ((int64_t)seq * hq + h) * b_max;
+
+  float qv[kRowLmax][8], kv[kRowLmax][8];
+#pragma unroll
+  for (int l = 0; l < kRowLmax; ++l) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + l;
+      const int cc = part * 8 + e;
+      const bool ok = in_regs && (j < j1) && (cc < k);
+      qv[l][e] = ok ? qrow[(int64_t)j * k + cc] : 0.f;
+      kv[l][e] = ok ? krow[(int64_t)j * k + cc] : 0.f;
+    }
+  }
+  for (int j = tid; j < b; j += kRowThreads)
+    xs[j] = rin ? rin[j] : (j == c ? 1.0f : 0.0f);
+  __syncthreads();
+
+  float sc = 1.0f;
+  float gmax = 0.0f;
+  for (int hop = 0; hop < s; ++hop) {
+    // pass 1: segment totals T = sum_j x_j qs_j (this lane's 8 components)
+    float T[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) T[e] = 0.f;
+    if (in_regs) {
+#pragma unroll
+      for (int l = 0; l < kRowLmax; ++l) {
+        if (j0 + l < j1) {
+          const float x = xs[j0 + l] * sc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) T[e] += x * qv[l][e];
+        }
+      }
+    } else {
+      for (int j = j0; j < j1; ++j) {
+        const float x = xs[j] * sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int cc = part * 8 + e;
+          T[e] += x * (cc < k ? qrow[(int64_t)j * k + cc] : 0.f);
+        }
+      }
+    }
+    // inclusive suffix scan over the segments of this wave
+    float incl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = T[e];
+#pragma unroll
+      for (int off = 1; off < SPW; off <<= 1) {
+        const float o = __shfl_down(v, off * LPR);
+        if (seg_in_wave + off < SPW) v += o;
+      }
+      incl[e] = v;
+    }
+    if (seg_in_wave == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wtot[wave][part * 8 + e] = incl[e];
+    }
+    __syncthreads();
+    // carry from later waves + exclusive suffix within the wave
+    float S[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float cw = 0.f;
+      for (int w2 = NWAVE - 1; w2 > wave; --w2) cw += wtot[w2][part * 8 + e];
+      const float nxt = __shfl_down(incl[e], LPR);
+      S[e] = cw + ((seg_in_wave + 1 < SPW) ? nxt : 0.f);
+    }
+    // pass 2: y_j = ks_j . S_j / sqrt(k), scanning j downwards
+    float lmax = 0.f;
+    if (in_regs) {
+#pragma unroll
+      for (int l = kRowLmax - 1; l >= 0; --l) {
+        if (j0 + l < j1) {
+          const float x = xs[j0 + l] * sc;
+          float y = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            S[e] += x * qv[l][e];
+            y += kv[l][e] * S[e];
+          }
+          y = group_sum<LPR>(y) * inv_sqrt_k;
+          if (part == 0) xs[j0 + l] = y;
+          lmax = fmaxf(lmax, fabsf(y));
+        }
+      }
+    } else {
+      for (int j = j1 - 1; j >= j0; --j) {
+        const float x = xs[j] * sc;
+        float y = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int cc = part * 8 + e;
+          const bool ok = cc < k;
+          S[e] += x * (ok ? qrow[(int64_t)j * k + cc] : 0.f);
+          y += (ok ? krow[(int64_t)j * k + cc] : 0.f) * S[e];
+        }
+        y = group_sum<LPR>(y) * inv_sqrt_k;
+        if (part == 0) xs[j] = y;
+        lmax = fmaxf(lmax, fabsf(y));
+      }
+    }
+    // row maximum
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
+    if (lane == 0) wmax[wave] = lmax;
+    __syncthreads();
+    gmax = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
+    sc = (gmax > 0.f) ? 1.0f / gmax : 1.0f;
+    __syncthreads();
+  }
+  for (int j = tid; j < b_max; j += kRowThreads) {
+    float v = 0.f;
+    if (j < b && gmax > 0.f) v = xs[j] / gmax;
+    rout[j] = v;
+  }
+}
+
+template <int KP>
+hipError_t run_walk(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
+                    const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks, int s,
+                    const float* R_prev, float* R_out, hipStream_t st) {
+  constexpr int ROWS = kWalkThreads / (KP / 8);
+  dim3 grid((max_blocks + ROWS - 1) / ROWS, hq, n_seqs);
+  hipLaunchKernelGGL((walk_kernel<KP>), grid, dim3(kWalkThreads), 0, st, q_sk, k_sk, hq, hkv, k,
+                     cu_blocks, n_seqs, total_blocks, s, R_prev, R_out, 1.0f / sqrtf((float)k));
+  return hipGetLastError();
+}
+
+template <int KP>
+hipError_t run_walk_row(const float* q_sk, const float* k_sk, int hq, int hkv, int k, int n_seqs,
+                        const int32_t* cur_block, int b_max, int s, const float* r_prev,
+                        float* r_out, hipStream_t st) {
+  dim3 grid(hq, n_seqs);
+  hipLaunchKernelGGL((walk_row_kernel<KP>), grid, dim3(kRowThreads), 0, st, q_sk, k_sk, hq, hkv,
+                     k, cur_block, b_max, s, r_prev, r_out, 1.0f / sqrtf((float)k));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
+                       const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks,
+                       int s, const float* R_prev, float* R_out, hipStream_t st) {
+  if (total_blocks == 0 || max_blocks == 0) return hipSuccess;
+  if (k <= 16)
+    return run_walk<16>(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks, s,
+                        R_prev, R_out, st);
+  if (k <= 32)
+    return run_walk<32>(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks, s,
+                        R_prev, R_out, st);
+  return run_walk<64>(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks, s,
+                      R_prev, R_out, st);
+}
+
+hipError_t launch_walk_row(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
+                           int n_seqs, const int32_t* cur_block, int b_max, int s,
+                           const float* r_prev, float* r_out, hipStream_t st) {
+  if (n_seqs == 0) return hipSuccess;
+  if (k <= 16)
+    return run_walk_row<16>(q_sk, k_sk, hq, hkv, k, n_seqs, cur_block, b_max, s, r_prev, r_out,
+                            st);
+  if (k <= 32)
+    return run_walk_row<32>(q_sk, k_sk, hq, hkv, k, n_seqs, cur_block, b_max, s, r_prev, r_out,
+                            st);
+  return run_walk_row<64>(q_sk, k_sk, hq, hkv, k, n_seqs, cur_block, b_max, s, r_prev, r_out,
+                          st);
+}
+
+}  // namespace sws

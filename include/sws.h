@@ -1,0 +1,243 @@
+/*
+ * sws.h - C ABI of the Sketch&Walk sparse-attention hot path for AMD MI355X
+ * (gfx950).
+ *
+ * The method is the one described on the deep-reading page "Scout Before You
+ * Attend: Sketch-and-Walk Sparse Attention for Efficient LLM Inference"
+ * (arXiv 2602.07397): Small-World Sketching of Q and K (block means, then a
+ * subsampled randomized Hadamard projection d -> k), a walk state carried
+ * from layer to layer, top-tau key blocks per query block, and block-sparse
+ * attention on the original Q/K/V for prefill and for single-token decode.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees or keeps a pointer after it returns.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on it and never synchronises.
+ * - Arguments are validated on the host before any launch; on error nothing
+ *   is launched and the outputs are untouched.  Device-side array contents
+ *   (offsets, positions, index lists) are trusted: they must be consistent
+ *   with the host sizes passed alongside them.
+ * - Return value: SWS_OK (0) or an sws_status error code.  sws_status_string
+ *   names a code; sws_last_error_detail gives a per-thread message for the
+ *   most recent failed call.
+ * - Activations are token-major and contiguous: X[t][h][e] for token t, head
+ *   h, feature e.  A ragged batch packs its sequences one after the other;
+ *   cu_seqlens[s] is the first token of sequence s (cu_seqlens[n_seqs] = T)
+ *   and cu_blocks[s] its first block (b_s = ceil(n_s / B) blocks; blocks never
+ *   straddle sequences).
+ * - GQA: query head h reads KV head h / (hq / hkv).
+ * - The library holds no state and no random generator: the Hadamard sign
+ *   vector and column subset are inputs.
+ */
+#ifndef SWS_H
+#define SWS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sws_status {
+  SWS_OK = 0,
+  SWS_ERR_NULL = 1,         /* a required pointer is NULL                        */
+  SWS_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes                */
+  SWS_ERR_UNSUPPORTED = 3,  /* a size or dtype this build has no kernel for      */
+  SWS_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required           */
+  SWS_ERR_LAUNCH = 5        /* the HIP runtime rejected a kernel launch          */
+} sws_status;
+
+typedef enum sws_dtype {
+  SWS_F32 = 0,
+  SWS_BF16 = 1
+} sws_dtype;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int sws_version(void);
+
+/* Static string naming a status code. */
+const char* sws_status_string(int status);
+
+/* Message describing the most recent failed call on this thread ("" if none). */
+const char* sws_last_error_detail(void);
+
+/*
+ * sws_sketch - Small-World Sketching of one activation tensor (blog page,
+ * section 3.1 block means and section 3.2 Hadamard projection).
+ *
+ * For every sequence s, block i (tokens [iB, min((i+1)B, n_s))) and head h:
+ *   xbar = mean of x[t][h][:] over the tokens the block holds (a partial last
+ *          block is averaged over its own token count);
+ *   sketch[c] = (1/sqrt(k)) * sum_r signs[r] * H[r][cols[c]] * xbar[r],
+ *   with H the natural-order d x d Sylvester-Hadamard matrix, c < k.
+ * Called once for Q (n_heads = hq) and once for K (n_heads = hkv).
+ *
+ *   x           [T][n_heads][d], dtype `dtype` (SWS_F32 or SWS_BF16)
+ *   cu_seqlens  [n_seqs + 1] int32, cu_blocks [n_seqs + 1] int32 (device)
+ *   total_blocks  host copy of cu_blocks[n_seqs]
+ *   d in {64, 128}; B in {64, 128}; 1 <= k <= min(d, 64)
+ *   signs       [d] int8 (+1 / -1); cols [k] int32, distinct, < d
+ *   sketch_out  fp32; element (h, global block g, c) at h * ld_head + g * k + c,
+ *               ld_head >= total_blocks * k
+ *   sum_out     optional (NULL to skip) fp32 [n_heads][total_blocks][d]: the
+ *               block sums (not divided by the token count)
+ */
+int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
+               int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
+               int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
+               int64_t ld_head, float* sum_out, void* stream);
+
+/*
+ * sws_sketch_append - decode form of sws_sketch (blog page, section 5: the
+ * same block-level sketch for each generated token).  Adds the new token of
+ * each sequence to the running sum of its open block and rewrites that
+ * block's sketch row, so the row always equals sws_sketch over the tokens the
+ * block holds so far.
+ *
+ *   x_new        [n_seqs][n_heads][d] (the new token of each sequence)
+ *   pos          [n_seqs] int32: token index of x_new in its sequence; its
+ *                block is c = pos / B; pos % B == 0 restarts the running sum
+ *   run_sum      [n_seqs][n_heads][d] fp32, in/out: sum of the open block
+ *   sketch_cache [n_seqs][n_heads][b_max][k] fp32: row c is rewritten;
+ *                the caller guarantees pos / B < b_max
+ */
+int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t n_seqs,
+                      int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
+                      const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
+                      void* stream);
+
+/*
+ * sws_walk_update - the walk state of one layer (blog page, section 4:
+ * R^0 = (A^0)^s, R^l = R^(l-1) (A^l)^s), with A = M, the causal sketched
+ * block scores M[i][j] = qs_i . ks_j / sqrt(k) for j <= i and 0 for j > i
+ * (section 3.2).  s hops per layer; each output row is divided by its largest
+ * magnitude (an all-zero row stays zero).  Per sequence and query head:
+ *   R_out = rownorm(R_prev * M^s)        (R_prev NULL: the identity)
+ *
+ *   q_sk  [hq][total_blocks][k] fp32, k_sk [hkv][total_blocks][k] fp32
+ *         (sws_sketch output with ld_head = total_blocks * k)
+ *   R_prev, R_out  fp32, packed: sequence s starts at element
+ *         hq * sum_{s' < s} b_{s'}^2 and holds [hq][b_s][b_s].  R_prev is read
+ *         as lower-triangular (entries above the diagonal are ignored).
+ *         R_out is written in full (zeros above the diagonal).  R_prev may be
+ *         the same buffer as R_out (in-place update).
+ *   max_blocks  host: max_s b_s; s >= 1; 1 <= k <= 64
+ */
+int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv, int32_t k,
+                    const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
+                    int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
+                    void* stream);
+
+/*
+ * sws_walk_update_row - decode form of sws_walk_update: only the row of the
+ * open block c = cur_block[seq] (blog page, section 5).  Equals row c of
+ * sws_walk_update over the first c + 1 blocks.
+ *
+ *   q_sk_cache [n_seqs][hq][b_max][k], k_sk_cache [n_seqs][hkv][b_max][k] fp32
+ *   cur_block  [n_seqs] int32, 0 <= cur_block < b_max
+ *   r_prev     NULL (the unit row e_c) or [n_seqs][hq][b_max]; may equal r_out
+ *   r_out      [n_seqs][hq][b_max]; entries above cur_block are written 0
+ */
+int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                        int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
+                        int32_t b_max, int32_t s, const float* r_prev, float* r_out,
+                        void* stream);
+
+/*
+ * sws_select_topk - top-tau key blocks per query block (blog page, section
+ * 4).  For sequence s, tau_s = floor(rho_percent * b_s / 100).  Row i keeps the
+ * tau_s earlier blocks m < i with the largest R[i][m] (ties: lower m first;
+ * -0 equals +0), all of them when i <= tau_s, plus the diagonal block i.
+ * dense != 0 keeps every block m <= i.  Lists are ascending local block
+ * indices.  R must hold no NaN.
+ *
+ *   R      packed as in sws_walk_update
+ *   idx    [hq][total_blocks][width] int32; cnt [hq][total_blocks] int32
+ *   width  >= min(max_blocks, floor(rho_percent * max_blocks / 100) + 1),
+ *          >= max_blocks when dense
+ *   max_blocks <= 4096
+ */
+int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
+                     int32_t total_blocks, int32_t max_blocks, int32_t rho_percent,
+                     int32_t dense, int32_t width, int32_t* idx, int32_t* cnt, void* stream);
+
+/*
+ * sws_select_topk_row - decode form of sws_select_topk for the open block
+ * c = cur_block[seq] (b = c + 1 blocks, tau = floor(rho_percent * b / 100)),
+ * followed by the union over the query heads of each KV group: the ascending
+ * list of blocks that any head of the group keeps, with a bit mask of the
+ * heads (bit g = head hkv_group * (hq/hkv) + g) that keep it.
+ *
+ *   r          [n_seqs][hq][b_max] fp32 (sws_walk_update_row output)
+ *   idx, cnt   optional (both NULL or both set): per-head lists
+ *              [n_seqs][hq][width] and counts [n_seqs][hq]
+ *   union_idx  [n_seqs][hkv][union_width] int32, union_mask same shape uint32,
+ *   union_cnt  [n_seqs][hkv] int32
+ *   width      >= min(b_max, floor(rho_percent * b_max / 100) + 1)
+ *   union_width >= min(b_max, (hq/hkv) * floor(rho_percent * b_max / 100) + 1)
+ *   hq / hkv <= 16, b_max <= 8192
+ */
+int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
+                         const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
+                         int32_t dense, int32_t width, int32_t* idx, int32_t* cnt,
+                         int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
+                         int32_t union_width, void* stream);
+
+/*
+ * sws_sparse_attn_prefill - block-sparse attention over the selected blocks
+ * on the original Q, K, V (blog page, sections 4 and 5).  Token t of block i,
+ * query head h: softmax over the keys u <= t lying in the blocks of
+ * idx[h][g][0 .. cnt[h][g]) (g = global block), scaled by `scale`,
+ * renormalised over those keys; out = weights . V.
+ *
+ *   q [T][hq][d], k and v [T][hkv][d]; out [T][hq][d] (same dtype)
+ *   dtype SWS_BF16: bf16 MFMA kernel (fp32 softmax / accumulation, output
+ *   rounded to nearest even); SWS_F32: fp32 kernel
+ *   idx, cnt as produced by sws_select_topk; idx == NULL means dense causal
+ *   (every block <= i); cnt ignored then
+ *   lse  optional [hq][T] fp32: natural-log sum of exp of the scaled scores
+ *   d in {64, 128}; B in {64, 128}
+ */
+int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
+                            const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
+                            int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
+                            int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
+                            int32_t width, float scale, void* out, float* lse, void* stream);
+
+/*
+ * sws_sparse_attn_decode - single-token attention of each sequence over the
+ * blocks its query heads kept (blog page, section 5; decode is bound by the
+ * KV-cache read, section 8.3).  Split-KV: the union list of every
+ * (sequence, KV head) is cut into chunks processed in parallel, then merged
+ * with a log-sum-exp combine; the block's KV rows are read once for all the
+ * query heads of the group that kept it.
+ *
+ *   q       [n_seqs][hq][d]; k_cache, v_cache [n_seqs][max_ctx][hkv][d]
+ *   ctx_len [n_seqs] int32: tokens in the cache including the new one
+ *           (the new token is the last; its block is the open block)
+ *   union_idx / union_cnt / union_mask as produced by sws_select_topk_row
+ *   (union_idx NULL: dense, every block of the context for every head)
+ *   out     [n_seqs][hq][d] (dtype of q); lse optional [n_seqs][hq] fp32
+ *   ws      workspace of at least sws_decode_workspace_size(...) bytes
+ *   d in {64, 128}; B in {64, 128}; hq / hkv <= 16
+ */
+int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                           const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
+                           int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
+                           const int32_t* union_cnt, const uint32_t* union_mask,
+                           int32_t union_width, float scale, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes sws_sparse_attn_decode needs for these sizes; for the dense
+ * form (union_idx NULL) pass union_width = ceil(max_ctx / B). */
+size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                 int32_t union_width);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWS_H */

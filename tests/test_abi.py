@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports every symbol include/sws.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dynamic_block_sparse_sws_amd as sws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "sws.h")) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sws_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) == 12
+    L = sws.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sws.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings():
+    L = sws.lib()
+    assert L.sws_version() == 100
+    assert L.sws_status_string(0) == b"SWS_OK"
+    assert L.sws_status_string(4) == b"SWS_ERR_WORKSPACE"
+    assert L.sws_status_string(99) == b"SWS_ERR_UNKNOWN"
+
+
+# Host-side validation: every call below must fail validation, so nothing is
+# launched and the fake pointers are never dereferenced.  On a machine with a
+# GPU these are skipped (they are covered there by the GPU tests' error cases).
+cpu_only = pytest.mark.skipif(torch.cuda.is_available(), reason="host-validation probes run without a GPU")
+P = ctypes.c_void_p(4096)
+N = None
+
+
+@cpu_only
+@pytest.mark.parametrize("args,code", [
+    # x NULL
+    ((N, 1, P, P, 1, 4, 8, 128, 64, 32, P, P, P, 128, N, N), 1),
+    # d unsupported
+    ((P, 1, P, P, 1, 4, 8, 96, 64, 32, P, P, P, 128, N, N), 3),
+    # B unsupported
+    ((P, 1, P, P, 1, 4, 8, 128, 32, 32, P, P, P, 128, N, N), 3),
+    # k > 64
+    ((P, 1, P, P, 1, 4, 8, 128, 64, 65, P, P, P, 4 * 65, N, N), 3),
+    # bad dtype
+    ((P, 7, P, P, 1, 4, 8, 128, 64, 32, P, P, P, 128, N, N), 3),
+    # ld_head too small
+    ((P, 1, P, P, 1, 4, 8, 128, 64, 32, P, P, P, 100, N, N), 2),
+    # misaligned x
+    ((ctypes.c_void_p(4098), 1, P, P, 1, 4, 8, 128, 64, 32, P, P, P, 128, N, N), 2),
+])
+def test_sketch_validation(args, code):
+    assert sws.lib().sws_sketch(*args) == code
+    assert sws.lib().sws_last_error_detail().startswith(b"sws_sketch")
+
+
+@cpu_only
+def test_other_entry_points_validation():
+    L = sws.lib()
+    # walk: hq not a multiple of hkv; s = 0; k = 0
+    assert L.sws_walk_update(P, P, 6, 4, 32, P, 1, 4, 4, 8, N, P, N) == 2
+    assert L.sws_walk_update(P, P, 8, 4, 32, P, 1, 4, 4, 0, N, P, N) == 2
+    assert L.sws_walk_update(P, P, 8, 4, 0, P, 1, 4, 4, 8, N, P, N) == 3
+    assert L.sws_walk_update(N, P, 8, 4, 32, P, 1, 4, 4, 8, N, P, N) == 1
+    assert L.sws_walk_update_row(P, P, 8, 4, 32, 2, P, 9000, 8, N, P, N) == 2
+    # select: width too small, rho out of range, too many blocks
+    assert L.sws_select_topk(P, 8, P, 1, 1024, 1024, 20, 0, 204, P, P, N) == 2
+    assert L.sws_select_topk(P, 8, P, 1, 1024, 1024, 101, 0, 1024, P, P, N) == 2
+    assert L.sws_select_topk(P, 8, P, 1, 8192, 8192, 20, 0, 8192, P, P, N) == 3
+    assert L.sws_select_topk(P, 8, P, 1, 16, 16, 100, 1, 15, P, P, N) == 2
+    # select row: union too narrow; group too large; idx without cnt
+    assert L.sws_select_topk_row(P, 32, 8, 2, P, 1029, 20, 0, 206, N, N, P, P, P, 800, N) == 2
+    assert L.sws_select_topk_row(P, 64, 2, 2, P, 1029, 20, 0, 206, N, N, P, P, P, 1029, N) == 3
+    assert L.sws_select_topk_row(P, 32, 8, 2, P, 1029, 20, 0, 206, P, N, P, P, P, 1029, N) == 1
+    # prefill attention: bad d, bad dtype, misaligned out, idx without cnt
+    assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 80, 64, P, P, 3,
+                                     ctypes.c_float(0.1), P, N, N) == 3
+    assert L.sws_sparse_attn_prefill(P, P, P, 5, P, P, 1, 8, 8, 32, 8, 128, 64, P, P, 3,
+                                     ctypes.c_float(0.1), P, N, N) == 3
+    assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 128, 64, P, P, 3,
+                                     ctypes.c_float(0.1), ctypes.c_void_p(4100), N, N) == 2
+    assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 128, 64, P, N, 3,
+                                     ctypes.c_float(0.1), P, N, N) == 1
+    # decode attention: workspace too small, group too large
+    need = L.sws_decode_workspace_size(16, 32, 8, 128, 64, 821)
+    assert need > 0
+    assert L.sws_sparse_attn_decode(P, P, P, 1, P, 16, 65792, 32, 8, 128, 64, P, P, P, 821,
+                                    ctypes.c_float(0.1), P, N, P, need - 1, N) == 4
+    assert L.sws_sparse_attn_decode(P, P, P, 1, P, 16, 65792, 32, 8, 128, 64, P, P, P, 821,
+                                    ctypes.c_float(0.1), P, N, N, need, N) == 4
+    assert L.sws_sparse_attn_decode(P, P, P, 1, P, 16, 65792, 64, 2, 128, 64, P, P, P, 821,
+                                    ctypes.c_float(0.1), P, N, P, 1 << 40, N) == 3
+    # append: b_max 0
+    assert L.sws_sketch_append(P, 1, P, 2, 8, 128, 64, 32, P, P, P, P, 0, N) == 2

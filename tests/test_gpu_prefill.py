@@ -1,0 +1,106 @@
+"""GPU parity of the prefill path (sketch -> walk -> select -> attention)
+against the oracle, stage by stage, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_sws_amd as sws
+import gen
+import oracle as O
+from gpu_util import PrefillRun, check_prefill_run, f64, TOL_ATTN_BF16
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def test_tiny_stack_fp32_all_layers():
+    """The tiny configuration: 1 head, 4 layers, n=1024, d=64, B=64, k=16,
+    20% density, fp32; every stage of every layer, every query block."""
+    cfg = gen.CONFIGS["C1"]
+    for n_dense in (0, 2):
+        _print("tiny fp32 n_dense", n_dense)
+        run = PrefillRun(cfg, cfg.seqlens, cfg.layers, cfg.rho, n_dense)
+        w = check_prefill_run(run)
+        _print("worst", w)
+
+
+@pytest.mark.parametrize("d,B,seqlens,hq,hkv,rho", [
+    (128, 64, (1000,), 8, 2, 20),
+    (128, 128, (700, 129, 1), 4, 1, 30),
+    (64, 64, (257, 64, 1500), 6, 3, 20),
+    (64, 128, (1024,), 2, 2, 10),
+])
+def test_bf16_gqa_ragged(d, B, seqlens, hq, hkv, rho):
+    cfg = gen.CONFIGS["C2"].with_(d=d, B=B, hq=hq, hkv=hkv, k=min(32, d))
+    _print("bf16", d, B, seqlens, hq, hkv, rho)
+    run = PrefillRun(cfg, seqlens, 3, rho, n_dense=1)
+    w = check_prefill_run(run)
+    _print("worst", w)
+
+
+@pytest.mark.parametrize("d,B", [(128, 128), (64, 64)])
+def test_fp32_path_ragged(d, B):
+    cfg = gen.CONFIGS["C2"].with_(d=d, B=B, hq=4, hkv=2, k=16, dtype="f32")
+    seqlens = (3 * B + 5, B - 3)
+    _print("fp32", d, B, seqlens)
+    run = PrefillRun(cfg, seqlens, 2, 25, n_dense=0)
+    w = check_prefill_run(run)
+    _print("worst", w)
+
+
+def test_dense_null_lists_equal_full_lists():
+    """idx == NULL (dense causal) gives the same output as explicit full
+    lists, and both match the oracle's dense attention."""
+    cfg = gen.CONFIGS["C2"].with_(hq=4, hkv=2, B=64)
+    run = PrefillRun(cfg, (777,), 1, 20, n_dense=1, dense_idx_null=True)
+    check_prefill_run(run)
+    run2 = PrefillRun(cfg, (777,), 1, 20, n_dense=1, dense_idx_null=False)
+    assert np.array_equal(run.layers[0]["out"], run2.layers[0]["out"])
+
+
+def test_bf16_dense_against_sdpa_fp32():
+    """Full density equals causal softmax attention computed by torch in fp32
+    on the CPU (a library routine, independent of the oracle)."""
+    cfg = gen.CONFIGS["C2"].with_(hq=4, hkv=1, B=128)
+    n = 640
+    geo = sws.Geometry([n], cfg.B)
+    q, k, v, _ = gen.layer_inputs(cfg, 0, device="cuda", seqlens=[n])
+    out = sws.sparse_attn_prefill(q, k, v, geo, None, None)
+    torch.cuda.synchronize()
+    qf = q.float().cpu().permute(1, 0, 2)
+    kf = k.float().cpu().permute(1, 0, 2).expand(cfg.hq, n, cfg.d).contiguous()
+    vf = v.float().cpu().permute(1, 0, 2).expand(cfg.hq, n, cfg.d).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, is_causal=True)
+    err = (out.float().cpu().permute(1, 0, 2) - ref).abs().max().item()
+    _print("dense vs sdpa", err)
+    assert err <= TOL_ATTN_BF16
+
+
+def test_repeat_runs_bit_identical():
+    cfg = gen.CONFIGS["C2"].with_(hq=8, hkv=2, B=64)
+    a = PrefillRun(cfg, (900,), 2, 20, 0)
+    b = PrefillRun(cfg, (900,), 2, 20, 0)
+    for la, lb in zip(a.layers, b.layers):
+        for key in ("q_sk", "k_sk", "R", "cnt", "out", "lse"):
+            assert np.array_equal(la[key], lb[key]), key
+        for h in range(cfg.hq):
+            for x, y in zip(a.lists_of(la, 0, h), b.lists_of(lb, 0, h)):
+                assert np.array_equal(x, y)
+
+
+def test_error_codes_from_the_library():
+    cfg = gen.CONFIGS["C2"].with_(hq=4, hkv=2)
+    geo = sws.Geometry([256], 64)
+    q, k, v, _ = gen.layer_inputs(cfg, 0, device="cuda", seqlens=[256])
+    with pytest.raises(sws.SwsError) as ei:
+        sws.sparse_attn_prefill(q.float()[:, :, :96].contiguous(), k.float()[:, :, :96].contiguous(),
+                                v.float()[:, :, :96].contiguous(), geo, None, None)
+    assert ei.value.code == 3
+    with pytest.raises(sws.SwsError) as ei:
+        sws.select_topk(torch.zeros(4 * 16, device="cuda"), 4, geo, 100, width=2)
+    assert ei.value.code == 2
