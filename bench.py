@@ -1,0 +1,444 @@
+#!/usr/bin/env python3
+"""Throughput of the Sketch&Walk hot path on one MI355X.
+
+Step = one sparse layer of the 128K-token prefill (32 query / 8 KV heads,
+d=128, B=128, k=32, s=8, 20% density): sketch Q, sketch K, walk update, top-tau
+selection, block-sparse attention, on inputs already resident in HBM.  The
+JSON line reports dense-equivalent TFLOP/s (4 d Hq n(n+1)/2 per layer divided
+by the layer time), ms per layer, the per-stage split, the roofline of the
+attention kernel, the 16 x 64K decode step (32 layers, first two dense), and
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "128K prefill ms/layer + dense-equiv TFLOP/s at 20% density; decode µs/step"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--rho", type=int, default=20)
+    ap.add_argument("--distinct-layers", type=int, default=4)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-layers", type=int, default=32)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense-ref", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time rho = 10, 30, 100")
+    ap.add_argument("--seqlen", type=int, default=None, help="override n (testing only)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def src_hash(name):
+    with open(os.path.join(ROOT, "dynamic_block_sparse_sws_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_src, launch_bytes_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(launch_bytes_key)
+    if not ent or ent.get("src_sha256_16") != src_hash(kernel_src):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the current stream (the one the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.acc = {}
+        self.n = {}
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def add(self, name, e0, e1):
+        self.acc.setdefault(name, []).append((e0, e1))
+
+    def ms(self, name):
+        pairs = self.acc.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in pairs) / max(1, len(pairs))
+
+
+def bench_prefill(args, torch, sws, gen, timer_cls):
+    cfg = gen.CONFIGS["C3"]
+    n = args.seqlen or cfg.seqlens[0]
+    geo = sws.Geometry([n], cfg.B)
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    signs_d = torch.from_numpy(signs).cuda()
+    cols_d = torch.from_numpy(cols).cuda()
+    L = max(1, args.distinct_layers)
+    layers = []
+    for l in range(L):
+        q, k, v, _ = gen.layer_inputs(cfg, 2 + l, device="cuda", seqlens=[n])
+        layers.append((q, k, v))
+    hq, hkv, d, B = cfg.hq, cfg.hkv, cfg.d, cfg.B
+    width = sws.select_width(args.rho, geo.max_blocks)
+    bufs = {
+        "q_sk": torch.empty((hq, geo.total_blocks, cfg.k), dtype=torch.float32, device="cuda"),
+        "k_sk": torch.empty((hkv, geo.total_blocks, cfg.k), dtype=torch.float32, device="cuda"),
+        "idx": torch.empty((hq, geo.total_blocks, width), dtype=torch.int32, device="cuda"),
+        "cnt": torch.empty((hq, geo.total_blocks), dtype=torch.int32, device="cuda"),
+        "out": torch.empty_like(layers[0][0]),
+    }
+    R = torch.empty(geo.walk_numel(hq), dtype=torch.float32, device="cuda")
+
+    def step(l, first, T=None):
+        q, k, v = layers[l % L]
+        ev = [T.ev()] if T else None
+        sws.sketch(q, geo, cfg.k, signs_d, cols_d, out=bufs["q_sk"])
+        sws.sketch(k, geo, cfg.k, signs_d, cols_d, out=bufs["k_sk"])
+        if T: ev.append(T.ev())
+        sws.walk_update(bufs["q_sk"], bufs["k_sk"], geo, cfg.s, None if first else R, R_out=R)
+        if T: ev.append(T.ev())
+        sws.select_topk(R, hq, geo, args.rho, idx=bufs["idx"], cnt=bufs["cnt"])
+        if T: ev.append(T.ev())
+        sws.sparse_attn_prefill(q, k, v, geo, bufs["idx"], bufs["cnt"], out=bufs["out"])
+        if T:
+            ev.append(T.ev())
+            for name, a, b in zip(("sketch", "walk", "select", "attention"), ev[:-1], ev[1:]):
+                T.add(name, a, b)
+            T.add("layer", ev[0], ev[-1])
+
+    for w in range(args.warmup):
+        step(w, w == 0)
+    torch.cuda.synchronize()
+    T = timer_cls(torch)
+    t0 = time.perf_counter()
+    e_start = T.ev()
+    for s in range(args.steps):
+        step(s, False, T)
+    e_end = T.ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e_start.elapsed_time(e_end)
+    ms_layer = total_ms / args.steps
+    cnt = bufs["cnt"].long()
+    pairs = int(cnt.sum().item())
+    flops_exec = 4.0 * B * B * d * pairs
+    dense_flops = 4.0 * d * hq * n * (n + 1) / 2.0
+    attn_ms = T.ms("attention")
+    causal_pairs = hq * geo.max_blocks * (geo.max_blocks + 1) // 2
+    res = {
+        "n": n, "ms_per_layer": ms_layer, "wall_s": wall,
+        "stage_us": {k_: T.ms(k_) * 1e3 for k_ in ("sketch", "walk", "select", "attention")},
+        "dense_equiv_tflops": dense_flops / (ms_layer * 1e-3) / 1e12,
+        "attn_exec_tflops": flops_exec / (attn_ms * 1e-3) / 1e12,
+        "executed_block_pairs": pairs, "executed_causal_density": pairs / causal_pairs,
+        "attn_flops_per_launch": flops_exec, "attn_ms": attn_ms,
+        "sketch_hbm_gbs": (2.0 * (hq + hkv) * d * n) / (T.ms("sketch") * 1e-3) / 1e9,
+    }
+    # our own dense attention at full density (the speed-up denominator)
+    if not args.no_dense_ref:
+        Td = timer_cls(torch)
+        q, k, v = layers[0]
+        sws.sparse_attn_prefill(q, k, v, geo, None, None, out=bufs["out"])
+        for _ in range(2):
+            a = Td.ev()
+            sws.sparse_attn_prefill(q, k, v, geo, None, None, out=bufs["out"])
+            Td.add("dense", a, Td.ev())
+        torch.cuda.synchronize()
+        dms = Td.ms("dense")
+        res["dense_attn_ms"] = dms
+        res["dense_attn_tflops"] = dense_flops / (dms * 1e-3) / 1e12
+        res["speedup_attn_vs_dense"] = dms / attn_ms
+        res["speedup_layer_vs_dense_attn"] = dms / ms_layer
+    if args.sweep:
+        sweep = {}
+        for rho in (10, 30, 100):
+            w2 = sws.select_width(rho, geo.max_blocks)
+            idx2 = torch.empty((hq, geo.total_blocks, w2), dtype=torch.int32, device="cuda")
+            cnt2 = torch.empty((hq, geo.total_blocks), dtype=torch.int32, device="cuda")
+            Ts = timer_cls(torch)
+            q, k, v = layers[0]
+            for it in range(3):
+                a = Ts.ev()
+                sws.sketch(q, geo, cfg.k, signs_d, cols_d, out=bufs["q_sk"])
+                sws.sketch(k, geo, cfg.k, signs_d, cols_d, out=bufs["k_sk"])
+                sws.walk_update(bufs["q_sk"], bufs["k_sk"], geo, cfg.s, R, R_out=R)
+                sws.select_topk(R, hq, geo, rho, idx=idx2, cnt=cnt2)
+                b_ = Ts.ev()
+                sws.sparse_attn_prefill(q, k, v, geo, idx2, cnt2, out=bufs["out"])
+                c_ = Ts.ev()
+                if it > 0:
+                    Ts.add("layer", a, c_)
+                    Ts.add("attention", b_, c_)
+            torch.cuda.synchronize()
+            p2 = int(cnt2.long().sum().item())
+            sweep[str(rho)] = {"ms_per_layer": Ts.ms("layer"), "attn_ms": Ts.ms("attention"),
+                               "attn_exec_tflops": 4.0 * B * B * d * p2 / (Ts.ms("attention") * 1e-3) / 1e12,
+                               "dense_equiv_tflops": dense_flops / (Ts.ms("layer") * 1e-3) / 1e12}
+        res["rho_sweep"] = sweep
+    ctx = {"cfg": cfg, "geo": geo, "layers": layers, "bufs": bufs, "signs": signs, "cols": cols}
+    return res, ctx
+
+
+def bench_decode(args, torch, sws, gen, timer_cls):
+    cfg = gen.CONFIGS["C4"]
+    ns, P, steps = cfg.decode_batch, cfg.decode_prefix, args.decode_steps
+    Lyr = args.decode_layers
+    hq, hkv, d, B, kd = cfg.hq, cfg.hkv, cfg.d, cfg.B, cfg.k
+    max_ctx = P + steps
+    b_max = -(-max_ctx // B)
+    signs, cols = gen.hadamard_tables(d, kd)
+    signs_d = torch.from_numpy(signs).cuda()
+    cols_d = torch.from_numpy(cols).cuda()
+    t_setup = time.perf_counter()
+    geo_p = sws.Geometry([P], B)
+    state = []
+    for l in range(Lyr):
+        qpre, qst, kc, vc = gen.decode_layer_inputs(cfg, l, device="cuda", n_seqs=ns, prefix=P,
+                                                    steps=steps)
+        qsk = torch.zeros((ns, hq, b_max, kd), dtype=torch.float32, device="cuda")
+        ksk = torch.zeros((ns, hkv, b_max, kd), dtype=torch.float32, device="cuda")
+        rq = torch.zeros((ns, hq, d), dtype=torch.float32, device="cuda")
+        rk = torch.zeros((ns, hkv, d), dtype=torch.float32, device="cuda")
+        sq = torch.empty((hq, geo_p.total_blocks, d), dtype=torch.float32, device="cuda")
+        sk = torch.empty((hkv, geo_p.total_blocks, d), dtype=torch.float32, device="cuda")
+        for s in range(ns):
+            sws.sketch(qpre[s], geo_p, kd, signs_d, cols_d, out=qsk[s], ld_head=b_max * kd,
+                       sum_out=sq)
+            sws.sketch(kc[s, :P], geo_p, kd, signs_d, cols_d, out=ksk[s], ld_head=b_max * kd,
+                       sum_out=sk)
+            rq[s] = sq[:, -1]
+            rk[s] = sk[:, -1]
+        del qpre
+        knew = kc[:, P:].permute(1, 0, 2, 3).contiguous()       # [steps, ns, hkv, d]
+        if l % 8 == 7:
+            print(f"[bench] decode setup: {l + 1}/{Lyr} layers", file=sys.stderr, flush=True)
+        state.append({"qst": qst, "knew": knew, "kc": kc, "vc": vc, "qsk": qsk, "ksk": ksk,
+                      "rq": rq, "rk": rk, "out": torch.empty((ns, hq, d), dtype=qst.dtype,
+                                                             device="cuda")})
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    pos = torch.arange(P, P + steps, dtype=torch.int32, device="cuda")[:, None].expand(steps, ns).contiguous()
+    cur = (pos // B).contiguous()
+    ctx_len = (pos + 1).contiguous()
+    uw = sws.union_width(cfg.rho, b_max, hq // hkv)
+    ubufs = (torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"), None, None)
+    dbufs = (torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"), None, None)
+    ws = torch.empty(sws.decode_workspace_size(ns, hq, hkv, d, B, b_max), dtype=torch.uint8,
+                     device="cuda")
+    r = torch.empty((ns, hq, b_max), dtype=torch.float32, device="cuda")
+
+    def one_step(t, T=None):
+        for l, st in enumerate(state):
+            dense = l < cfg.n_dense
+            a = T.ev() if T else None
+            sws.sketch_append(st["qst"][t], pos[t], B, kd, signs_d, cols_d, st["rq"], st["qsk"])
+            sws.sketch_append(st["knew"][t], pos[t], B, kd, signs_d, cols_d, st["rk"], st["ksk"])
+            sws.walk_update_row(st["qsk"], st["ksk"], cur[t], cfg.s, None if l == 0 else r, r)
+            uidx, ucnt, umask, _, _ = sws.select_topk_row(r, hq, hkv, cur[t], b_max, cfg.rho,
+                                                          dense=dense,
+                                                          out=dbufs if dense else ubufs)
+            b_ = T.ev() if T else None
+            sws.sparse_attn_decode(st["qst"][t], st["kc"], st["vc"], ctx_len[t], B, uidx, ucnt,
+                                   umask, out=st["out"], ws=ws)
+            if T:
+                c_ = T.ev()
+                T.add("dense_layer" if dense else "sparse_layer", a, c_)
+                T.add("dense_attn" if dense else "sparse_attn", b_, c_)
+                T.add("dense_select_chain" if dense else "sparse_select_chain", a, b_)
+
+    # the decode steps run in order (the sketch caches and running sums are
+    # state); one step is warm-up
+    one_step(0)
+    torch.cuda.synchronize()
+    T = timer_cls(torch)
+    e0 = T.ev()
+    for t in range(1, steps):
+        one_step(t, T)
+    e1 = T.ev()
+    torch.cuda.synchronize()
+    timed = steps - 1
+    us_step = e0.elapsed_time(e1) * 1e3 / timed
+    # union sizes at the last step (algorithmic bytes of the sparse attention)
+    ucnt = ubufs[1].long()
+    union_blocks = int(ucnt.sum().item())
+    tok_read = union_blocks * B            # the open block is partial; counted whole
+    attn_bytes = tok_read * d * 2 * 2 + ns * hq * d * 2 * 2
+    sp_attn_us = T.ms("sparse_attn") * 1e3
+    res = {
+        "batch": ns, "context": P, "steps_timed": timed, "layers": Lyr,
+        "us_per_step": us_step,
+        "us_per_sparse_layer_step": T.ms("sparse_layer") * 1e3,
+        "us_per_dense_layer_step": T.ms("dense_layer") * 1e3,
+        "sparse_attn_us": sp_attn_us,
+        "sparse_select_chain_us": T.ms("sparse_select_chain") * 1e3,
+        "dense_attn_us": T.ms("dense_attn") * 1e3,
+        "sparse_attn_bytes": attn_bytes,
+        "sparse_attn_gbs": attn_bytes / (sp_attn_us * 1e-6) / 1e9,
+        "dense_attn_gbs": (ns * (P + steps // 2) * hkv * d * 4) / (T.ms("dense_attn") * 1e-3) / 1e9,
+        "union_blocks_per_group": union_blocks / (ns * hkv),
+        "per_head_blocks": cfg.rho * (b_max - 1) // 100 + 1,
+        "setup_s": setup_s,
+    }
+    return res
+
+
+def cpu_baseline(ctx, torch, budget_s=12.0):
+    """The oracle (fp64 NumPy) on a bounded sample of one sparse 128K layer:
+    the query heads of KV head 0 sketched, walked from the identity and
+    selected in full, then the attention of as many query blocks (spread over
+    the sequence) as fit in the time budget; the time is scaled to the whole
+    layer (32 query heads, 8 KV heads, every executed block pair)."""
+    import oracle as O
+    cfg, geo = ctx["cfg"], ctx["geo"]
+    q, k, v = ctx["layers"][0]
+    n = geo.total_tokens
+    grp = cfg.hq // cfg.hkv
+    K = k[:, 0].double().cpu().numpy()
+    V = v[:, 0].double().cpu().numpy()
+    Qs = [q[:, h].double().cpu().numpy() for h in range(grp)]
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ks = O.sketch(K, cfg.B, ctx["signs"], ctx["cols"])
+    t_k = time.perf_counter() - t0
+    per_head = []
+    all_lists = []
+    for Q in Qs:
+        a = time.perf_counter()
+        qs = O.sketch(Q, cfg.B, ctx["signs"], ctx["cols"])
+        R = O.walk_update(None, O.sketched_scores(qs, ks), cfg.s)
+        lists = O.select(R, 20)
+        per_head.append(time.perf_counter() - a)
+        all_lists.append(lists)
+    b = len(all_lists[0])
+    rng = np.random.default_rng(0)
+    order = [b - 1] + rng.permutation(b - 1).tolist()
+    t_attn = 0.0
+    pairs_sample = 0
+    n_rows = 0
+    scale = 1.0 / math.sqrt(cfg.d)
+    while n_rows < len(order) and t_attn < budget_s:
+        i = order[n_rows]
+        a = time.perf_counter()
+        O.sparse_attention_rows(Qs[0], K, V, all_lists[0], cfg.B, scale, [i])
+        t_attn += time.perf_counter() - a
+        pairs_sample += len(all_lists[0][i])
+        n_rows += 1
+    total = time.perf_counter() - t0
+    attn_per_pair = t_attn / pairs_sample
+    pairs_layer = sum(len(x) for x in all_lists[0]) * cfg.hq
+    est = cfg.hkv * t_k + cfg.hq * (sum(per_head) / len(per_head)) + attn_per_pair * pairs_layer
+    dense_flops = 4.0 * cfg.d * cfg.hq * n * (n + 1) / 2.0
+    return {
+        "value": dense_flops / est / 1e12, "unit": "TFLOP/s (dense-equivalent, extrapolated)",
+        "cores": cores, "kind": "oracle",
+        "ms_per_layer_extrapolated": est * 1e3,
+        "sample": (f"fp64 NumPy oracle on one sparse layer of the 128K workload: KV head 0 and its "
+                   f"{grp} query heads sketched, walked (s={cfg.s}) from the identity and "
+                   f"top-tau selected over all {b} rows; attention of {n_rows} query blocks "
+                   f"({pairs_sample} block pairs); scaled to {cfg.hq} query heads, {cfg.hkv} KV "
+                   f"heads and {pairs_layer} block pairs"),
+        "sample_seconds": total,
+    }
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling the HBM counters."""
+    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": max(args.gpus, world)}))
+        sys.exit(2)
+    import torch
+    import dynamic_block_sparse_sws_amd as sws
+    import gen
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    sws.lib()
+    torch.cuda.init()
+    if args.copy_calib:
+        copy_calibration(torch)
+    pre, ctx = bench_prefill(args, torch, sws, gen, Timer)
+    print(f"[bench] prefill: {pre['ms_per_layer']:.3f} ms/layer, "
+          f"{pre['dense_equiv_tflops']:.1f} dense-equiv TFLOP/s, attention "
+          f"{pre['attn_exec_tflops']:.1f} TFLOP/s executed", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(ctx, torch)
+        print(f"[bench] cpu oracle sample {cpu['sample_seconds']:.1f}s", file=sys.stderr, flush=True)
+    del ctx
+    torch.cuda.empty_cache()
+    dec = None
+    if not args.no_decode:
+        dec = bench_decode(args, torch, sws, gen, Timer)
+        print(f"[bench] decode: {dec['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+    attn_bytes = traffic_for("attn_prefill.hip", "attn_prefill_bf16_128k_rho20")
+    line = {
+        "metric": METRIC,
+        "value": round(pre["dense_equiv_tflops"], 3),
+        "unit": "TFLOP/s (dense-equivalent, 128K prefill layer at 20% density)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_layer"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("long_128k_prefill: one sparse layer per step, 32 query / 8 KV "
+                                f"heads, d=128, n={pre['n']}, B=128, k=32, s=8, rho={args.rho}%; "
+                                "decode_64k_b16: 16 x 64K-token context, 32 layers (2 dense), "
+                                "B=64, k=32, rho=20%"),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(pre["attn_exec_tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pre["attn_exec_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": attn_bytes,
+                     "kernel": "attn_prefill_bf16_kernel<128,128>",
+                     "flops_per_launch": pre["attn_flops_per_launch"],
+                     "avg_launch_ms": round(pre["attn_ms"], 4)},
+        "cpu_baseline": cpu,
+        "prefill": pre,
+        "decode": dec,
+    }
+    if dec:
+        line["decode_us_per_step"] = round(dec["us_per_step"], 2)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -10,6 +10,8 @@ from .synth import (  # noqa: F401
     Config,
     hadamard_tables,
     layer_inputs,
+    seq_tensor,
+    block_latents,
     decode_layer_inputs,
     seed_for,
     ragged_lengths,

@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field, replace
+from functools import lru_cache
 
 import numpy as np
 import torch
@@ -116,6 +117,49 @@ def _unit(x: np.ndarray) -> np.ndarray:
     return x / max(np.linalg.norm(x), 1e-30)
 
 
+@lru_cache(maxsize=512)
+def _band(cfg_id: int, seq: int, group: int, b: int, d: int) -> np.ndarray:
+    """Local AR(1) band latent z [b, d] (0.9 correlation per block), shared by
+    every layer."""
+    rng = np.random.default_rng(seed_for(cfg_id, _TENSOR_ID["band"], seq, group))
+    eps = rng.normal(0.0, 0.5, size=(b, d))
+    z = np.empty((b, d))
+    z[0] = eps[0]
+    a = 0.9
+    c = math.sqrt(1.0 - a * a)
+    for i in range(1, b):
+        z[i] = a * z[i - 1] + c * eps[i]
+    z.setflags(write=False)
+    return z
+
+
+def chain_draws(cfg: Config, layer: int, seq: int, group: int, b: int, m_hat: np.ndarray):
+    """Multi-hop chains of one (sequence, KV group, layer): block triples
+    (i > j > m) and unit directions e1, e2 orthogonal to each other and to the
+    sink direction.  The first half of the chains is the same in every layer,
+    the second half is redrawn per layer."""
+    d = cfg.d
+    n_ch = -(-b // 16)
+    out = []
+    for persistent, n in ((True, n_ch // 2), (False, n_ch - n_ch // 2)):
+        if n == 0:
+            continue
+        lay = 0xFFFF if persistent else layer
+        r = np.random.default_rng(seed_for(cfg.cfg_id, _TENSOR_ID["chain"], seq, group, lay))
+        trip = np.argpartition(r.random((n, b)), 2, axis=1)[:, :3]
+        trip = -np.sort(-trip, axis=1)                         # i > j > m
+        e1 = r.normal(size=(n, d))
+        e1 -= np.outer(e1 @ m_hat, m_hat)
+        e1 /= np.linalg.norm(e1, axis=1, keepdims=True)
+        e2 = r.normal(size=(n, d))
+        e2 -= np.outer(e2 @ m_hat, m_hat)
+        e2 -= (np.sum(e2 * e1, axis=1, keepdims=True)) * e1
+        e2 /= np.linalg.norm(e2, axis=1, keepdims=True)
+        out.append((trip, e1, e2))
+    return out
+
+
+@lru_cache(maxsize=64)
 def block_latents(cfg: Config, layer: int, seq: int, group: int, seqlen: int):
     """Per-block latent offsets (fp64, [b, d]) added to every query token and
     every key token of a block, for one (sequence, KV group)."""
@@ -125,38 +169,19 @@ def block_latents(cfg: Config, layer: int, seq: int, group: int, seqlen: int):
         rng = np.random.default_rng(seed_for(cfg.cfg_id, _TENSOR_ID["mu"], seq, group))
         mu = rng.normal(0.0, 0.5, size=(b, d))
         return mu, mu.copy()
-    # local AR(1) band, shared by all layers
-    rng = np.random.default_rng(seed_for(cfg.cfg_id, _TENSOR_ID["band"], seq, group))
-    eps = rng.normal(0.0, 0.5, size=(b, d))
-    z = np.empty((b, d))
-    z[0] = eps[0]
-    a = 0.9
-    c = math.sqrt(1.0 - a * a)
-    for i in range(1, b):
-        z[i] = a * z[i - 1] + c * eps[i]
+    z = _band(cfg.cfg_id, seq, group, b, d)
     lat_q = z.copy()
     lat_k = z.copy()
     # attention sink on key block 0, along the mean query-latent direction
     m_hat = _unit(z.mean(axis=0))
     lat_k[0] += 0.5 * math.sqrt(d) * m_hat
-    # multi-hop chains i > j > m; half persist across layers, half are per layer
     if b >= 3:
-        n_ch = -(-b // 16)
         beta = 0.5 * math.sqrt(d)
-        for ch in range(n_ch):
-            persistent = ch < n_ch // 2
-            lay = 0xFFFF if persistent else layer
-            r = np.random.default_rng(seed_for(cfg.cfg_id, _TENSOR_ID["chain"], seq, group, ch, lay))
-            i, j, m = sorted(r.choice(b, size=3, replace=False).tolist(), reverse=True)
-            e1 = r.normal(size=d)
-            e1 = _unit(e1 - (e1 @ m_hat) * m_hat)
-            e2 = r.normal(size=d)
-            e2 = e2 - (e2 @ m_hat) * m_hat
-            e2 = _unit(e2 - (e2 @ e1) * e1)
-            lat_q[i] += beta * e1
-            lat_k[j] += beta * e1
-            lat_q[j] += beta * e2
-            lat_k[m] += beta * e2
+        for trip, e1, e2 in chain_draws(cfg, layer, seq, group, b, m_hat):
+            np.add.at(lat_q, trip[:, 0], beta * e1)
+            np.add.at(lat_k, trip[:, 1], beta * e1)
+            np.add.at(lat_q, trip[:, 1], beta * e2)
+            np.add.at(lat_k, trip[:, 2], beta * e2)
     return lat_q, lat_k
 
 

@@ -1,0 +1,198 @@
+"""GPU parity of the decode chain (sketch append -> walk row -> select row +
+GQA union -> split-KV attention) against the oracle, stage by stage, at steps
+that open, fill and complete blocks."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_sws_amd as sws
+import gen
+import oracle as O
+from gpu_util import f64, rowwise_rel_err, TOL_ATTN_BF16, TOL_ATTN_F32, TOL_SKETCH, TOL_WALK
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def run_decode_case(cfg, prefixes, steps, n_layers, rho, n_dense, check_steps, dense_null=False):
+    ns = len(prefixes)
+    B, d, kd, hq, hkv = cfg.B, cfg.d, cfg.k, cfg.hq, cfg.hkv
+    grp = hq // hkv
+    max_ctx = max(prefixes) + steps
+    b_max = -(-max_ctx // B)
+    signs, cols = gen.hadamard_tables(d, kd)
+    signs_d = torch.from_numpy(signs).cuda()
+    cols_d = torch.from_numpy(cols).cuda()
+    dt = cfg.torch_dtype
+    layers = []
+    for l in range(n_layers):
+        full = [{w: gen.seq_tensor(cfg, l, s, w, prefixes[s] + steps, "cuda") for w in "qkv"}
+                for s in range(ns)]
+        kc = torch.zeros((ns, max_ctx, hkv, d), dtype=dt, device="cuda")
+        vc = torch.zeros_like(kc)
+        qsk = torch.zeros((ns, hq, b_max, kd), dtype=torch.float32, device="cuda")
+        ksk = torch.zeros((ns, hkv, b_max, kd), dtype=torch.float32, device="cuda")
+        rq = torch.zeros((ns, hq, d), dtype=torch.float32, device="cuda")
+        rk = torch.zeros((ns, hkv, d), dtype=torch.float32, device="cuda")
+        for s in range(ns):
+            P = prefixes[s]
+            n_all = P + steps
+            kc[s, :n_all] = full[s]["k"]
+            vc[s, :n_all] = full[s]["v"]
+            geo = sws.Geometry([P], B)
+            sq = torch.empty((hq, geo.total_blocks, d), dtype=torch.float32, device="cuda")
+            sk = torch.empty((hkv, geo.total_blocks, d), dtype=torch.float32, device="cuda")
+            sws.sketch(full[s]["q"][:P].contiguous(), geo, kd, signs_d, cols_d, out=qsk[s],
+                       ld_head=b_max * kd, sum_out=sq)
+            sws.sketch(full[s]["k"][:P].contiguous(), geo, kd, signs_d, cols_d, out=ksk[s],
+                       ld_head=b_max * kd, sum_out=sk)
+            if P % B:
+                rq[s] = sq[:, -1]
+                rk[s] = sk[:, -1]
+        host = [{w: f64(full[s][w]) for w in "qkv"} for s in range(ns)]
+        layers.append({"full": full, "host": host, "kc": kc, "vc": vc, "qsk": qsk, "ksk": ksk,
+                       "rq": rq, "rk": rk, "r": torch.zeros((ns, hq, b_max), device="cuda")})
+    P_t = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    worst = {"sketch": 0.0, "walk": 0.0, "attn": 0.0}
+    last = None
+    tol_attn = TOL_ATTN_F32 if cfg.dtype == "f32" else TOL_ATTN_BF16
+    for t in range(steps):
+        pos = P_t + t
+        cur = pos // B
+        ctx = pos + 1
+        recs = []
+        for l, L in enumerate(layers):
+            dense = l < n_dense
+            qn = torch.stack([L["full"][s]["q"][prefixes[s] + t] for s in range(ns)]).contiguous()
+            kn = torch.stack([L["full"][s]["k"][prefixes[s] + t] for s in range(ns)]).contiguous()
+            sws.sketch_append(qn, pos, B, kd, signs_d, cols_d, L["rq"], L["qsk"])
+            sws.sketch_append(kn, pos, B, kd, signs_d, cols_d, L["rk"], L["ksk"])
+            r_prev = None if l == 0 else layers[l - 1]["r"]
+            sws.walk_update_row(L["qsk"], L["ksk"], cur, cfg.s, r_prev, L["r"])
+            uidx, ucnt, umask, idx, cnt = sws.select_topk_row(L["r"], hq, hkv, cur, b_max, rho,
+                                                              dense=dense, per_head=True)
+            lse = torch.empty((ns, hq), dtype=torch.float32, device="cuda")
+            if dense and dense_null:
+                out = sws.sparse_attn_decode(qn, L["kc"], L["vc"], ctx, B, None, None, None, lse=lse)
+            else:
+                out = sws.sparse_attn_decode(qn, L["kc"], L["vc"], ctx, B, uidx, ucnt, umask,
+                                             lse=lse)
+            if t in check_steps:
+                torch.cuda.synchronize()
+                recs.append({"qsk": f64(L["qsk"]), "ksk": f64(L["ksk"]), "r": f64(L["r"]),
+                             "uidx": uidx.cpu().numpy(), "ucnt": ucnt.cpu().numpy(),
+                             "umask": umask.cpu().numpy().astype(np.uint32),
+                             "idx": idx.cpu().numpy(), "cnt": cnt.cpu().numpy(),
+                             "out": f64(out), "lse": f64(lse)})
+        if t not in check_steps:
+            continue
+        for l, (L, rec) in enumerate(zip(layers, recs)):
+            dense = l < n_dense
+            for s in range(ns):
+                p = prefixes[s] + t
+                c = p // B
+                H = L["host"][s]
+                # sketch rows 0..c against the oracle on the first p+1 tokens
+                for h in range(hq):
+                    want = O.sketch(H["q"][:p + 1, h], B, signs, cols)
+                    e = rowwise_rel_err(rec["qsk"][s, h, :c + 1], want)
+                    worst["sketch"] = max(worst["sketch"], e)
+                    assert e <= TOL_SKETCH, (t, l, s, h, "q sketch", e)
+                for g in range(hkv):
+                    want = O.sketch(H["k"][:p + 1, g], B, signs, cols)
+                    e = rowwise_rel_err(rec["ksk"][s, g, :c + 1], want)
+                    assert e <= TOL_SKETCH, (t, l, s, g, "k sketch", e)
+                for h in range(hq):
+                    g = h // grp
+                    M = O.sketched_scores(rec["qsk"][s, h, :c + 1], rec["ksk"][s, g, :c + 1])
+                    rp = None if l == 0 else recs[l - 1]["r"][s, h, :c + 1]
+                    rw = O.walk_row(rp, M, c, cfg.s)
+                    rg = rec["r"][s, h]
+                    e = rowwise_rel_err(rg[:c + 1], rw)
+                    worst["walk"] = max(worst["walk"], e)
+                    assert e <= TOL_WALK, (t, l, s, h, "walk", e)
+                    assert np.all(rg[c + 1:] == 0)
+                    lst = (np.arange(c + 1) if dense
+                           else O.select_row(rg, c, O.n_select(rho, c + 1)))
+                    got = rec["idx"][s, h, :rec["cnt"][s, h]]
+                    assert got.tolist() == lst.tolist(), (t, l, s, h, got, lst)
+                    # attention of token p over the selected blocks
+                    keys = np.concatenate([np.arange(j * B, min((j + 1) * B, p + 1)) for j in lst])
+                    z = (H["k"][keys, g] @ H["q"][p, h]) / math.sqrt(d)
+                    zm = z.max()
+                    wgt = np.exp(z - zm)
+                    o_want = (wgt @ H["v"][keys, g]) / wgt.sum()
+                    e = float(np.abs(rec["out"][s, h] - o_want).max())
+                    worst["attn"] = max(worst["attn"], e)
+                    assert e <= tol_attn, (t, l, s, h, "attn", e)
+                    assert abs(rec["lse"][s, h] - (zm + math.log(wgt.sum()))) <= max(tol_attn, 1e-4)
+                # union list and masks of every group
+                for g in range(hkv):
+                    want = {}
+                    for h in range(g * grp, (g + 1) * grp):
+                        for m in rec["idx"][s, h, :rec["cnt"][s, h]]:
+                            want[int(m)] = want.get(int(m), 0) | (1 << (h - g * grp))
+                    n_u = rec["ucnt"][s, g]
+                    got_idx = rec["uidx"][s, g, :n_u].tolist()
+                    got_mask = rec["umask"][s, g, :n_u].tolist()
+                    assert got_idx == sorted(want), (t, l, s, g)
+                    assert got_mask == [want[m] for m in sorted(want)], (t, l, s, g)
+        last = recs
+    return worst, [L["host"] for L in layers], last
+
+
+@pytest.mark.parametrize("d,B,hq,hkv,prefixes,steps", [
+    (128, 64, 8, 2, (1000, 64, 2000), 70),
+    (64, 128, 10, 2, (700, 1000), 40),
+])
+def test_decode_bf16(d, B, hq, hkv, prefixes, steps):
+    cfg = gen.CONFIGS["C4"].with_(d=d, B=B, hq=hq, hkv=hkv, k=32)
+    checks = {0, 1, 23, 24, 25, 47, 48, 63, 64, steps - 1} & set(range(steps))
+    _print("decode bf16", d, B, hq, hkv, prefixes, steps)
+    w, _, _ = run_decode_case(cfg, prefixes, steps, 3, 30, 1, checks)
+    _print("worst", w)
+
+
+def test_decode_fp32_and_dense_null():
+    cfg = gen.CONFIGS["C4"].with_(d=64, B=64, hq=4, hkv=4, k=16, dtype="f32")
+    _print("decode fp32")
+    w, _, _ = run_decode_case(cfg, (65, 127), 10, 2, 25, 1, {0, 1, 9}, dense_null=True)
+    _print("worst", w)
+
+
+def test_decode_matches_prefix_prefill_definition():
+    """End to end: the state-carrying decode equals the oracle's stateless
+    definition (row p of the prefill on the first p+1 tokens, every layer's walk
+    carried from the previous layer in fp64) on every selection, except where
+    an fp32-versus-fp64 near-tie separates the tau-th and next candidate."""
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=4, hkv=2, k=32)
+    prefixes, steps, n_layers, rho = (190, 300), 3, 4, 30
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    _, hosts, recs = run_decode_case(cfg, prefixes, steps, n_layers, rho, 1, {steps - 1})
+    for s in range(len(prefixes)):
+        p = prefixes[s] + steps - 1
+        c = p // cfg.B
+        lay = [(H[s]["q"][:p + 1], H[s]["k"][:p + 1], H[s]["v"][:p + 1]) for H in hosts]
+        dec = O.decode_step(lay, signs, cols, cfg.B, cfg.s, rho, n_dense=1)
+        for l in range(n_layers):
+            for h in range(cfg.hq):
+                want = dec[l][h]
+                r_gpu = recs[l]["r"][s, h, :c + 1]
+                e = rowwise_rel_err(r_gpu, want["r"])
+                _print("e2e", s, l, h, "walk drift", e)
+                assert e <= 1e-4
+                got = recs[l]["idx"][s, h, :recs[l]["cnt"][s, h]]
+                if got.tolist() != want["lst"].tolist():
+                    tau = O.n_select(rho, c + 1)
+                    row = want["r"][:c]
+                    kth = np.sort(row)[::-1][tau - 1]
+                    diff = set(got.tolist()) ^ set(want["lst"].tolist())
+                    gap = max(abs(row[m] - kth) for m in diff)
+                    assert gap <= 1e-4 * np.abs(row).max(), (s, l, h, diff, gap)
+                else:
+                    assert np.abs(recs[l]["out"][s, h] - want["o"]).max() <= TOL_ATTN_BF16

@@ -115,10 +115,12 @@ def test_planted_two_hop_chain_reached_by_walk():
     K = k[:, 0].double().numpy()
     M = O.sketched_scores(O.sketch(Q, cfg.B, signs, cols), O.sketch(K, cfg.B, signs, cols))
     R = O.walk_update(None, M, 2)
-    # chain 0 of group 0 (persistent): recover its blocks from the generator's own draw
-    import numpy.random as npr
+    # first persistent chain of group 0, as the generator drew it
     b = O.n_blocks(4096, cfg.B)
-    r = npr.default_rng(gen.seed_for(cfg.cfg_id, 5, 0, 0, 0, 0xFFFF))
-    i, j, m = sorted(r.choice(b, size=3, replace=False).tolist(), reverse=True)
+    z = gen.synth._band(cfg.cfg_id, 0, 0, b, cfg.d)
+    m_hat = z.mean(axis=0) / np.linalg.norm(z.mean(axis=0))
+    trip = gen.synth.chain_draws(cfg, 0, 0, 0, b, m_hat)[0][0]
+    i, j, m = (int(x) for x in trip[0])
+    assert i > j > m
     assert R[i, j] > np.median(R[i, :i])
     assert R[i, m] > np.median(R[i, :i])
