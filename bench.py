@@ -110,6 +110,8 @@ def bench_prefill(args, torch, sws, gen, timer_cls):
         "idx": torch.empty((hq, geo.total_blocks, width), dtype=torch.int32, device="cuda"),
         "cnt": torch.empty((hq, geo.total_blocks), dtype=torch.int32, device="cuda"),
         "out": torch.empty_like(layers[0][0]),
+        "ws": torch.empty(sws.prefill_workspace_size(sws.BF16, geo.total_blocks, hkv, d, B),
+                          dtype=torch.uint8, device="cuda"),
     }
     R = torch.empty(geo.walk_numel(hq), dtype=torch.float32, device="cuda")
 
@@ -123,7 +125,7 @@ def bench_prefill(args, torch, sws, gen, timer_cls):
         if T: ev.append(T.ev())
         sws.select_topk(R, hq, geo, args.rho, idx=bufs["idx"], cnt=bufs["cnt"])
         if T: ev.append(T.ev())
-        sws.sparse_attn_prefill(q, k, v, geo, bufs["idx"], bufs["cnt"], out=bufs["out"])
+        sws.sparse_attn_prefill(q, k, v, geo, bufs["idx"], bufs["cnt"], out=bufs["out"], ws=bufs["ws"])
         if T:
             ev.append(T.ev())
             for name, a, b in zip(("sketch", "walk", "select", "attention"), ev[:-1], ev[1:]):
@@ -162,10 +164,10 @@ def bench_prefill(args, torch, sws, gen, timer_cls):
     if not args.no_dense_ref:
         Td = timer_cls(torch)
         q, k, v = layers[0]
-        sws.sparse_attn_prefill(q, k, v, geo, None, None, out=bufs["out"])
+        sws.sparse_attn_prefill(q, k, v, geo, None, None, out=bufs["out"], ws=bufs["ws"])
         for _ in range(2):
             a = Td.ev()
-            sws.sparse_attn_prefill(q, k, v, geo, None, None, out=bufs["out"])
+            sws.sparse_attn_prefill(q, k, v, geo, None, None, out=bufs["out"], ws=bufs["ws"])
             Td.add("dense", a, Td.ev())
         torch.cuda.synchronize()
         dms = Td.ms("dense")
@@ -188,7 +190,7 @@ def bench_prefill(args, torch, sws, gen, timer_cls):
                 sws.walk_update(bufs["q_sk"], bufs["k_sk"], geo, cfg.s, R, R_out=R)
                 sws.select_topk(R, hq, geo, rho, idx=idx2, cnt=cnt2)
                 b_ = Ts.ev()
-                sws.sparse_attn_prefill(q, k, v, geo, idx2, cnt2, out=bufs["out"])
+                sws.sparse_attn_prefill(q, k, v, geo, idx2, cnt2, out=bufs["out"], ws=bufs["ws"])
                 c_ = Ts.ev()
                 if it > 0:
                     Ts.add("layer", a, c_)

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "sws_version", "sws_status_string", "sws_last_error_detail", "sws_sketch",
     "sws_sketch_append", "sws_walk_update", "sws_walk_update_row", "sws_select_topk",
     "sws_select_topk_row", "sws_sparse_attn_prefill", "sws_sparse_attn_decode",
-    "sws_decode_workspace_size",
+    "sws_decode_workspace_size", "sws_prefill_workspace_size",
 )
 
 
@@ -65,7 +65,8 @@ _SIGS = {
     "sws_select_topk_row": ([_P, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P],
                             ctypes.c_int),
     "sws_sparse_attn_prefill": ([_P, _P, _P, ctypes.c_int, _P, _P, _I, _I, _I, _I, _I, _I, _I,
-                                 _P, _P, _I, _F, _P, _P, _P], ctypes.c_int),
+                                 _P, _P, _I, _F, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "sws_prefill_workspace_size": ([ctypes.c_int, _I, _I, _I, _I], _SZ),
     "sws_sparse_attn_decode": ([_P, _P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                 _P, _I, _F, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "sws_decode_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
@@ -262,21 +263,29 @@ def select_topk_row(r: Optional[torch.Tensor], hq: int, hkv: int, cur_block: tor
     return uidx, ucnt, umask, idx, cnt
 
 
+def prefill_workspace_size(dtype_code: int, total_blocks: int, hkv: int, d: int, B: int) -> int:
+    return int(lib().sws_prefill_workspace_size(dtype_code, total_blocks, hkv, d, B))
+
+
 def sparse_attn_prefill(q, k, v, geo: Geometry, idx: Optional[torch.Tensor],
                         cnt: Optional[torch.Tensor], scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                        stream=None):
+                        ws: Optional[torch.Tensor] = None, stream=None):
     T, hq, d = q.shape
     hkv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    need = prefill_workspace_size(_dtype_code(q), geo.total_blocks, hkv, d, geo.B)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     width = idx.shape[-1] if idx is not None else 0
     _check("sws_sparse_attn_prefill", lib().sws_sparse_attn_prefill(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(geo.cu_seqlens), _ptr(geo.cu_blocks),
         geo.n_seqs, geo.total_blocks, geo.max_blocks, hq, hkv, d, geo.B, _ptr(idx), _ptr(cnt),
-        width, float(scale), _ptr(out), _ptr(lse), _stream(stream)))
+        width, float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
     return out
 
 
@@ -316,5 +325,6 @@ def prefill_layer(q, k, v, geo: Geometry, kdim: int, signs, cols, s: int, rho: i
     R = walk_update(q_sk, k_sk, geo, s, None if first_layer else R, R_out=R, stream=stream)
     idx, cnt = select_topk(R, hq, geo, rho, dense=dense, idx=bufs.get("idx"),
                            cnt=bufs.get("cnt"), stream=stream)
-    o = sparse_attn_prefill(q, k, v, geo, idx, cnt, out=bufs.get("out"), stream=stream)
+    o = sparse_attn_prefill(q, k, v, geo, idx, cnt, out=bufs.get("out"), ws=bufs.get("ws"),
+                            stream=stream)
     return {"q_sk": q_sk, "k_sk": k_sk, "R": R, "idx": idx, "cnt": cnt, "out": o}

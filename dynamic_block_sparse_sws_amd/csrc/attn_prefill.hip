@@ -3,10 +3,13 @@
 // the key blocks selected for each query block).
 //
 // bf16 path: one workgroup per (query head, query block of B tokens), B/32
-// wavefronts, each owning 32 query rows.  For every selected key block the
-// workgroup stages K (row-major) and V (transposed) in LDS, then each wave
-// runs a FlashAttention-style step on the matrix cores with
-// v_mfma_f32_32x32x16_bf16:
+// wavefronts, each owning 32 query rows.  A pre-pass writes V transposed per
+// block (keys in accumulator-row order) to a workspace.  The selected key
+// blocks are walked in steps of 64 keys (32 when B = 64): the K and V^T tiles
+// of the next step are loaded into registers while the current step
+// computes, then stored into the other half of a double-buffered, XOR-swizzled
+// LDS tile pair (one barrier per step).  Each wave runs a FlashAttention-style
+// step on the matrix cores with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T          (A = K rows from LDS, B = this wave's Q in registers)
 //   online softmax       (a lane holds one query column: the row max over the
 //                         block is 64 in-register values plus one cross-lane
@@ -30,35 +33,94 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// V^T tile: D rows (feature) x 128 key slots (256 bytes, no padding); the 16-byte
-// chunks of a row are XOR-swizzled by the row so that both the transposed
-// 8-byte writes (rows 8 apart) and the 16-byte MFMA operand reads (consecutive
-// rows) spread over all banks.
-__device__ __forceinline__ int vt_offset(int d, int key) {
-  // key -> slot: within every 16 keys, groups of 4 are stored in the order
-  // 0, 2, 1, 3 (keys 0-3, 8-11, 4-7, 12-15), matching the MFMA accumulator rows
-  const int kg = (key >> 2) & 3;
-  const int slot = (key & ~15) | ((((kg & 1) << 1) | (kg >> 1)) << 2) | (key & 3);
-  const int chunk = slot >> 3;
-  const int swz = (d ^ (d >> 3)) & 15;
-  return d * 128 + ((chunk ^ swz) << 3) + (slot & 7);
+// Key order inside every 16 keys of a V^T row: groups of 4 keys stored as
+// 0-3, 8-11, 4-7, 12-15, which is the row order of the 32x32 MFMA accumulator
+// halves, so a lane's P^T operand (taken straight from its S^T accumulators)
+// lines up with 8 contiguous V^T slots.
+__device__ __forceinline__ int vt_slot_key(int slot) {
+  const int g = (slot >> 2) & 3;
+  return (slot & ~15) | ((((g & 1) << 1) | (g >> 1)) << 2) | (slot & 3);
+}
+
+// Pre-pass: V [T][hkv][D] -> V^T blocks vt[hkv][total_blocks][D][BLK] (keys in
+// slot order, zero past the end of the sequence).
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void v_transpose_kernel(
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ cu_blocks, int n_seqs, int total_blocks, int hkv,
+    uint16_t* __restrict__ vt) {
+  __shared__ uint16_t tile[D][BLK + 2];
+  const int gb = blockIdx.x;
+  const int g = blockIdx.y;
+  const int seq = seq_of_block(cu_blocks, n_seqs, gb);
+  const int i = gb - cu_blocks[seq];
+  const int tok0 = cu_seqlens[seq];
+  const int n = cu_seqlens[seq + 1] - tok0;
+  const int64_t rstride = (int64_t)hkv * D;
+  for (int u = threadIdx.x; u < BLK * (D / 8); u += 256) {
+    const int key = u / (D / 8);
+    const int ch = u % (D / 8);
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (i * BLK + key < n)
+      raw = *reinterpret_cast<const u32x4_t*>(v + (int64_t)(tok0 + i * BLK + key) * rstride + (int64_t)g * D + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[ch * 8 + 2 * e][key] = (uint16_t)(raw[e] & 0xffffu);
+      tile[ch * 8 + 2 * e + 1][key] = (uint16_t)(raw[e] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = vt + ((int64_t)g * total_blocks + gb) * D * BLK;
+  for (int u = threadIdx.x; u < D * (BLK / 8); u += 256) {
+    const int d = u / (BLK / 8);
+    const int c = u % (BLK / 8);
+    u32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[d][vt_slot_key(c * 8 + 2 * e)];
+      const uint32_t hi = tile[d][vt_slot_key(c * 8 + 2 * e + 1)];
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(dst + (int64_t)d * BLK + c * 8) = w;
+  }
+}
+
+template <int D, int BLK>
+struct PrefillTile {
+  static constexpr int NW = BLK / 32;               // waves (32 query rows each)
+  static constexpr int NT = NW * 64;
+  static constexpr int KT = (BLK == 128) ? 64 : 32; // keys per pipeline step
+  static constexpr int NSUB = BLK / KT;             // steps per selected block
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int VCH = KT / 8;                // 16-byte chunks per V^T row of a step
+  static constexpr int TILE = KT * D * 2;           // bytes of one K (or V^T) step tile
+  static constexpr int LOADS = TILE / 16 / NT;      // 16-byte loads per thread per tile
+};
+
+// XOR swizzles of the 16-byte chunks of a tile row, chosen so that the 16
+// lanes of an MFMA operand read (16 consecutive rows, same logical chunk) hit
+// 16 distinct 4-bank groups.
+template <int CH>
+__device__ __forceinline__ int row_swizzle(int row) {
+  if (CH == 16) return row & 15;          // 256-byte rows
+  if (CH == 8) return (row >> 1) & 7;     // 128-byte rows: two rows share a bank line
+  return (row >> 2) & 3;                  // 64-byte rows
 }
 
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                              const uint16_t* __restrict__ v,
+                              const uint16_t* __restrict__ vt,
                               const int32_t* __restrict__ cu_seqlens,
                               const int32_t* __restrict__ cu_blocks, int n_seqs,
                               int total_blocks, int hq, int hkv,
                               const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
                               int width, float scale_log2, uint16_t* __restrict__ out,
                               float* __restrict__ lse) {
-  constexpr int NW = BLK / 32;
-  constexpr int NT = NW * 64;
-  constexpr int KSTR = D + 8;        // K row stride in elements (272 B for D = 128)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * 128];
+  using TL = PrefillTile<D, BLK>;
+  constexpr int NW = TL::NW, NT = TL::NT, KT = TL::KT, NSUB = TL::NSUB;
+  __shared__ __attribute__((aligned(16))) char Ks[2][TL::TILE];
+  __shared__ __attribute__((aligned(16))) char Vs[2][TL::TILE];
 
   const int G = hq / hkv;
   const int id = blockIdx.x;
@@ -67,6 +129,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int gb = total_blocks - 1 - id / hq;
   const int seq = seq_of_block(cu_blocks, n_seqs, gb);
   const int i = gb - cu_blocks[seq];
+  const int blk0 = cu_blocks[seq];
   const int tok0 = cu_seqlens[seq];
   const int n = cu_seqlens[seq + 1] - tok0;
   const int T = cu_seqlens[n_seqs];
@@ -79,9 +142,11 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int qi = w * 32 + l32;          // query row within the block
-  const int qrow = i * BLK + qi;        // query row within the sequence
+  const int qi = w * 32 + l32;
+  const int qrow = i * BLK + qi;
+  (void)NW;
 
+  // ---- this wave's Q rows as MFMA B operands ----
   bf16x8_t qf[D / 16];
   {
     const uint16_t* qp = q + (int64_t)(tok0 + qrow) * qstride + (int64_t)h * D + hl * 8;
@@ -93,6 +158,52 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     }
   }
 
+  // ---- staging geometry: load u of this thread fills tile chunk u * NT + tid ----
+  int k_row[TL::LOADS];
+  uint32_t k_off[TL::LOADS], v_off[TL::LOADS];
+#pragma unroll
+  for (int u = 0; u < TL::LOADS; ++u) {
+    const int qc = u * NT + tid;
+    const int kr = qc / TL::KCH;
+    const int kp = qc % TL::KCH;
+    k_row[u] = kr;
+    k_off[u] = (uint32_t)(kr * kstride + (kp ^ row_swizzle<TL::KCH>(kr)) * 8);
+    const int vr = qc / TL::VCH;
+    const int vp = qc % TL::VCH;
+    v_off[u] = (uint32_t)(vr * BLK + (vp ^ row_swizzle<TL::VCH>(vr)) * 8);
+  }
+  const uint16_t* kbase = k + (int64_t)tok0 * kstride + (int64_t)kvh * D;
+  const uint16_t* vtbase = vt + ((int64_t)kvh * total_blocks + blk0) * D * BLK;
+
+  u32x4_t kst[TL::LOADS], vst[TL::LOADS];
+  auto load_step = [&](int j, int sub) {
+    const int key0 = j * BLK + sub * KT;
+    const uint16_t* ks = kbase + (int64_t)key0 * kstride;
+    const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
+#pragma unroll
+    for (int u = 0; u < TL::LOADS; ++u) {
+      kst[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key0 + k_row[u] < n) kst[u] = *reinterpret_cast<const u32x4_t*>(ks + k_off[u]);
+      vst[u] = *reinterpret_cast<const u32x4_t*>(vs + v_off[u]);
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < TL::LOADS; ++u) {
+      *reinterpret_cast<u32x4_t*>(&Ks[buf][(u * NT + tid) * 16]) = kst[u];
+      *reinterpret_cast<u32x4_t*>(&Vs[buf][(u * NT + tid) * 16]) = vst[u];
+    }
+  };
+
+  // ---- per-lane LDS read offsets (bytes) of the MFMA A operands ----
+  const int ksw = row_swizzle<TL::KCH>(l32);
+  const int vsw = row_swizzle<TL::VCH>(l32);
+  int k_rd[D / 16], v_rd[KT / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) k_rd[dc] = l32 * (D * 2) + (((2 * dc + hl) ^ ksw) << 4);
+#pragma unroll
+  for (int kc = 0; kc < KT / 16; ++kc) v_rd[kc] = l32 * (KT * 2) + (((2 * kc + hl) ^ vsw) << 4);
+
   floatx16_t o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -103,108 +214,95 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
 
   const int nb = idx ? cnt[(int64_t)h * total_blocks + gb] : i + 1;
   const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
-  const uint16_t* kbase = k + (int64_t)tok0 * kstride + (int64_t)kvh * D;
-  const uint16_t* vbase = v + (int64_t)tok0 * kstride + (int64_t)kvh * D;
+  const int nsteps = nb * NSUB;
 
-  for (int nn = 0; nn < nb; ++nn) {
-    const int j = lst ? lst[nn] : nn;
-    const int key0 = j * BLK;
-    __syncthreads();
-    // ---- stage K_j (row-major) ----
-#pragma unroll
-    for (int it = 0; it < (BLK * D / 8) / NT; ++it) {
-      const int u = tid + it * NT;
-      const int row = u / (D / 8);
-      const int ch = u % (D / 8);
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (key0 + row < n) raw = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(key0 + row) * kstride + ch * 8);
-      *reinterpret_cast<u32x4_t*>(&Ks[row * KSTR + ch * 8]) = raw;
+  int j = lst ? lst[0] : 0;
+  load_step(j, 0);
+  store_step(0);
+  __syncthreads();
+  for (int stp = 0; stp < nsteps; ++stp) {
+    const int sub = stp % NSUB;
+    const int buf = stp & 1;
+    const bool has_next = stp + 1 < nsteps;
+    int j_next = j;
+    if (has_next) {
+      const int nn_next = (stp + 1) / NSUB;
+      j_next = (sub + 1 < NSUB) ? j : (lst ? lst[nn_next] : nn_next);
+      load_step(j_next, (stp + 1) % NSUB);
     }
-    // ---- stage V_j transposed: 4 keys x 8 features per unit ----
-#pragma unroll
-    for (int it = 0; it < ((BLK / 4) * (D / 8)) / NT; ++it) {
-      const int u = tid + it * NT;
-      const int kg = u / (D / 8);
-      const int ch = u % (D / 8);
-      u32x4_t rr[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int key = key0 + kg * 4 + t;
-        rr[t] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key < n) rr[t] = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)key * kstride + ch * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2_t pk;
-        pk[0] = __builtin_amdgcn_perm(rr[1][wd], rr[0][wd], sel);
-        pk[1] = __builtin_amdgcn_perm(rr[3][wd], rr[2][wd], sel);
-        *reinterpret_cast<u32x2_t*>(&Vt[vt_offset(ch * 8 + e, kg * 4)]) = pk;
-      }
-    }
-    __syncthreads();
+    const char* ksb = Ks[buf];
+    const char* vsb = Vs[buf];
 
-    // ---- S^T = K Q^T ----
-    floatx16_t st[BLK / 32];
+    // ---- S^T = K Q^T for this step's KT keys ----
+    floatx16_t st[KT / 32];
 #pragma unroll
-    for (int kt = 0; kt < BLK / 32; ++kt) {
+    for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[(kt * 32 + l32) * KSTR + dc * 16 + hl * 8]);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], st[kt], 0, 0, 0);
-      }
-    }
-    // ---- scale, causal mask on the diagonal block, running max ----
-    const bool diag = (j == i);
-    float mx = -INFINITY;
+    for (int dc = 0; dc < D / 16; ++dc) {
+      bf16x8_t a[KT / 32];
 #pragma unroll
-    for (int kt = 0; kt < BLK / 32; ++kt) {
+      for (int kt = 0; kt < KT / 32; ++kt)
+        a[kt] = *reinterpret_cast<const bf16x8_t*>(ksb + k_rd[dc] + kt * 32 * D * 2);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        float sv = st[kt][r] * scale_log2;
-        if (diag && key > qi) sv = -INFINITY;
-        st[kt][r] = sv;
-        mx = fmaxf(mx, sv);
-      }
+      for (int kt = 0; kt < KT / 32; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kt], qf[dc], st[kt], 0, 0, 0);
     }
+
+    // ---- online softmax (log2 domain); mask only on the diagonal block ----
+    if (j == i) {
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = sub * KT + kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key > qi) st[kt][r] = -INFINITY;
+        }
+    }
+    float mx = st[0][0];
+#pragma unroll
+    for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    m_run = m_new;
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8_t pb[KT / 16];
+#pragma unroll
+    for (int kc = 0; kc < KT / 16; ++kc) {
+      const int kt = kc >> 1;
+      const int r0 = (kc & 1) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e], scale_log2, -m_run));
+        l_run += p;
+        pb[kc][e] = (__bf16)p;
+      }
+    }
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int kc = 0; kc < BLK / 16; ++kc) {
-      const int kt = kc >> 1;
-      const int r0 = (kc & 1) * 8;
-      float p[8];
+    for (int kc = 0; kc < KT / 16; ++kc) {
+      bf16x8_t a[D / 32];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(st[kt][r0 + e] - m_new);
-        l_run += p[e];
-      }
-      u32x4_t pw;
-      pw[0] = pack_bf16x2(p[0], p[1]);
-      pw[1] = pack_bf16x2(p[2], p[3]);
-      pw[2] = pack_bf16x2(p[4], p[5]);
-      pw[3] = pack_bf16x2(p[6], p[7]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+      for (int dt = 0; dt < D / 32; ++dt)
+        a[dt] = *reinterpret_cast<const bf16x8_t*>(vsb + v_rd[kc] + dt * 32 * KT * 2);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = dt * 32 + l32;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Vt[vt_offset(d, kc * 16 + hl * 4)]);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], pb[kc], o[dt], 0, 0, 0);
     }
+    if (has_next) store_step(buf ^ 1);
+    __syncthreads();
+    j = j_next;
   }
 
   // ---- finalise ----
@@ -217,10 +315,11 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d0 = dt * 32 + 8 * rg + 4 * hl;
-        u32x2_t pk;
-        pk[0] = pack_bf16x2(o[dt][rg * 4 + 0] * inv, o[dt][rg * 4 + 1] * inv);
-        pk[1] = pack_bf16x2(o[dt][rg * 4 + 2] * inv, o[dt][rg * 4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(op + d0) = pk;
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        bf16x4_t pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(o[dt][rg * 4 + e] * inv);
+        *reinterpret_cast<bf16x4_t*>(op + d0) = pk;
       }
     }
     if (lse && hl == 0) lse[(int64_t)h * T + tok0 + qrow] = (m_run + log2f(l_run)) * kLn2;
@@ -308,13 +407,18 @@ template <int D, int BLK>
 hipError_t run_bf16(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                     const int32_t* cu_blocks, int n_seqs, int total_blocks, int hq, int hkv,
                     const int32_t* idx, const int32_t* cnt, int width, float scale, void* out,
-                    float* lse, hipStream_t st) {
+                    float* lse, void* ws, hipStream_t st) {
+  uint16_t* vt = static_cast<uint16_t*>(ws);
+  hipLaunchKernelGGL((v_transpose_kernel<D, BLK>), dim3(total_blocks, hkv), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(v), cu_seqlens, cu_blocks, n_seqs,
+                     total_blocks, hkv, vt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)total_blocks * hq);
   hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, BLK>), grid, dim3(BLK * 2), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), cu_seqlens, cu_blocks, n_seqs,
-                     total_blocks, hq, hkv, idx, cnt, width, scale * kLog2e,
-                     static_cast<uint16_t*>(out), lse);
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt,
+                     cu_seqlens, cu_blocks, n_seqs, total_blocks, hq, hkv, idx, cnt, width,
+                     scale * kLog2e, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
@@ -322,7 +426,8 @@ template <int D, int BLK>
 hipError_t run_f32(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                    const int32_t* cu_blocks, int n_seqs, int total_blocks, int hq, int hkv,
                    const int32_t* idx, const int32_t* cnt, int width, float scale, void* out,
-                   float* lse, hipStream_t st) {
+                   float* lse, void* ws, hipStream_t st) {
+  (void)ws;
   dim3 grid(total_blocks, hq);
   hipLaunchKernelGGL((attn_prefill_f32_kernel<D, BLK>), grid, dim3(BLK), 0, st,
                      static_cast<const float*>(q), static_cast<const float*>(k),
@@ -337,21 +442,21 @@ hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, int 
                                const int32_t* cu_seqlens, const int32_t* cu_blocks, int n_seqs,
                                int total_blocks, int max_blocks, int hq, int hkv, int d, int B,
                                const int32_t* idx, const int32_t* cnt, int width, float scale,
-                               void* out, float* lse, hipStream_t st) {
+                               void* out, float* lse, void* ws, hipStream_t st) {
   (void)max_blocks;
   if (total_blocks == 0) return hipSuccess;
 #define SWS_DISPATCH(FN)                                                                      \
   if (d == 128 && B == 128) return FN<128, 128>(q, k, v, cu_seqlens, cu_blocks, n_seqs,     \
                                                 total_blocks, hq, hkv, idx, cnt, width,     \
-                                                scale, out, lse, st);                       \
+                                                scale, out, lse, ws, st);                       \
   if (d == 128 && B == 64) return FN<128, 64>(q, k, v, cu_seqlens, cu_blocks, n_seqs,       \
                                               total_blocks, hq, hkv, idx, cnt, width, scale, \
-                                              out, lse, st);                                \
+                                              out, lse, ws, st);                            \
   if (d == 64 && B == 128) return FN<64, 128>(q, k, v, cu_seqlens, cu_blocks, n_seqs,       \
                                               total_blocks, hq, hkv, idx, cnt, width, scale, \
-                                              out, lse, st);                                \
+                                              out, lse, ws, st);                            \
   return FN<64, 64>(q, k, v, cu_seqlens, cu_blocks, n_seqs, total_blocks, hq, hkv, idx, cnt, \
-                    width, scale, out, lse, st);
+                    width, scale, out, lse, ws, st);
   if (dtype == SWS_BF16) {
     SWS_DISPATCH(run_bf16)
   }

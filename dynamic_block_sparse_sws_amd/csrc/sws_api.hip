@@ -208,7 +208,8 @@ int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dty
                             const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
                             int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
                             int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
-                            int32_t width, float scale, void* out, float* lse, void* stream) {
+                            int32_t width, float scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream) {
   const char* fn = "sws_sparse_attn_prefill";
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
@@ -230,10 +231,20 @@ int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dty
   if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(SWS_ERR_SHAPE, "%s: q/k/v/out must be 16-byte aligned", fn);
+  const size_t need = sws_prefill_workspace_size(dtype, total_blocks, hkv, d, B);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu (or misaligned)", fn,
+                ws_bytes, need);
   return launched(sws::launch_attn_prefill(q, k, v, dtype, cu_seqlens, cu_blocks, n_seqs,
                                            total_blocks, max_blocks, hq, hkv, d, B, idx, cnt,
-                                           width, scale, out, lse, (hipStream_t)stream),
+                                           width, scale, out, lse, ws, (hipStream_t)stream),
                   fn);
+}
+
+size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, int32_t d,
+                                  int32_t B) {
+  if (dtype != SWS_BF16 || total_blocks < 0 || hkv < 1 || d < 1 || B < 1) return 0;
+  return (size_t)hkv * (size_t)total_blocks * (size_t)d * (size_t)B * 2u;
 }
 
 size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,

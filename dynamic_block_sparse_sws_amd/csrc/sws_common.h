@@ -92,7 +92,7 @@ hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, int 
                                const int32_t* cu_seqlens, const int32_t* cu_blocks, int n_seqs,
                                int total_blocks, int max_blocks, int hq, int hkv, int d, int B,
                                const int32_t* idx, const int32_t* cnt, int width, float scale,
-                               void* out, float* lse, hipStream_t st);
+                               void* out, float* lse, void* ws, hipStream_t st);
 hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                               int dtype, const int32_t* ctx_len, int n_seqs, int max_ctx, int hq,
                               int hkv, int d, int B, const int32_t* union_idx,

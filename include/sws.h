@@ -199,13 +199,22 @@ int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
  *   idx, cnt as produced by sws_select_topk; idx == NULL means dense causal
  *   (every block <= i); cnt ignored then
  *   lse  optional [hq][T] fp32: natural-log sum of exp of the scaled scores
+ *   ws   workspace of at least sws_prefill_workspace_size(...) bytes (the
+ *        bf16 path stages V transposed per block there; may be NULL when the
+ *        size is 0)
  *   d in {64, 128}; B in {64, 128}
  */
 int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
                             const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
                             int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
                             int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
-                            int32_t width, float scale, void* out, float* lse, void* stream);
+                            int32_t width, float scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Workspace bytes sws_sparse_attn_prefill needs (hkv * total_blocks * d * B * 2
+ * for SWS_BF16, 0 for SWS_F32). */
+size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, int32_t d,
+                                  int32_t B);
 
 /*
  * sws_sparse_attn_decode - single-token attention of each sequence over the

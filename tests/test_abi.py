@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     L = sws.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -86,13 +86,19 @@ def test_other_entry_points_validation():
     assert L.sws_select_topk_row(P, 32, 8, 2, P, 1029, 20, 0, 206, P, N, P, P, P, 1029, N) == 1
     # prefill attention: bad d, bad dtype, misaligned out, idx without cnt
     assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 80, 64, P, P, 3,
-                                     ctypes.c_float(0.1), P, N, N) == 3
+                                     ctypes.c_float(0.1), P, N, P, 1 << 30, N) == 3
     assert L.sws_sparse_attn_prefill(P, P, P, 5, P, P, 1, 8, 8, 32, 8, 128, 64, P, P, 3,
-                                     ctypes.c_float(0.1), P, N, N) == 3
+                                     ctypes.c_float(0.1), P, N, P, 1 << 30, N) == 3
     assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 128, 64, P, P, 3,
-                                     ctypes.c_float(0.1), ctypes.c_void_p(4100), N, N) == 2
+                                     ctypes.c_float(0.1), ctypes.c_void_p(4100), N, P, 1 << 30, N) == 2
     assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 128, 64, P, N, 3,
-                                     ctypes.c_float(0.1), P, N, N) == 1
+                                     ctypes.c_float(0.1), P, N, P, 1 << 30, N) == 1
+    need = L.sws_prefill_workspace_size(1, 8, 8, 128, 64)
+    assert need == 8 * 8 * 128 * 64 * 2 and L.sws_prefill_workspace_size(0, 8, 8, 128, 64) == 0
+    assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 128, 64, P, P, 3,
+                                     ctypes.c_float(0.1), P, N, P, need - 16, N) == 4
+    assert L.sws_sparse_attn_prefill(P, P, P, 1, P, P, 1, 8, 8, 32, 8, 128, 64, P, P, 3,
+                                     ctypes.c_float(0.1), P, N, N, need, N) == 4
     # decode attention: workspace too small, group too large
     need = L.sws_decode_workspace_size(16, 32, 8, 128, 64, 821)
     assert need > 0
