@@ -107,6 +107,102 @@ __device__ __forceinline__ int row_swizzle(int row) {
   return (row >> 2) & 3;                  // 64-byte rows
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Softmax reference lag: the running maximum used for the exponentials is
+// only raised when a new score exceeds it by more than this many powers of
+// two, so most steps skip the rescale of the output accumulators.  The
+// weights stay below 2^8, and numerator, denominator and log-sum-exp all use
+// the same reference, so the result is unchanged.
+constexpr float kMaxLag = 8.0f;
+
+// One pipeline step: KT keys of the current block against this wave's 32
+// query rows.  ksb / vsb are the step's K and V^T tiles in LDS.
+template <int D, int BLK>
+__device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char* vsb, int key_base,
+                                          const bf16x8_t (&qf)[D / 16],
+                                          const int (&k_rd)[D / 16],
+                                          const int (&v_rd)[PrefillTile<D, BLK>::KT / 16],
+                                          floatx16_t (&o)[D / 32], float& m_run, float& l_run,
+                                          float scale_log2, int qi, int hl) {
+  constexpr int KT = PrefillTile<D, BLK>::KT;
+  // ---- S^T = K Q^T ----
+  floatx16_t st[KT / 32];
+#pragma unroll
+  for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; dc += 2) {
+    bf16x8_t a[2][KT / 32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt)
+        a[u][kt] = *reinterpret_cast<const bf16x8_t*>(ksb + k_rd[dc + u] + kt * 32 * D * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][kt], qf[dc + u], st[kt], 0, 0, 0);
+  }
+  // ---- causal mask (diagonal block only) and the step's row maximum ----
+  if (diag) {
+#pragma unroll
+    for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key_base + kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (key > qi) st[kt][r] = -INFINITY;
+      }
+  }
+  float mx = st[0][0];
+#pragma unroll
+  for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_cand = mx * scale_log2;
+  if (__any(m_cand > m_run + kMaxLag)) {
+    const float m_new = fmaxf(m_run, m_cand);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    m_run = m_new;
+  }
+  // ---- P = exp2(S * scale - m), bf16; row sum from the same bf16 values ----
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8_t pb[KT / 16];
+#pragma unroll
+  for (int kc = 0; kc < KT / 16; ++kc) {
+    const int kt = kc >> 1;
+    const int r0 = (kc & 1) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2_t pr;
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e], scale_log2, -m_run));
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e + 1], scale_log2, -m_run));
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      pb[kc][e] = pr[0];
+      pb[kc][e + 1] = pr[1];
+    }
+  }
+  // ---- O^T += V^T P^T ----
+#pragma unroll
+  for (int kc = 0; kc < KT / 16; ++kc) {
+    bf16x8_t a[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      a[dt] = *reinterpret_cast<const bf16x8_t*>(vsb + v_rd[kc] + dt * 32 * KT * 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], pb[kc], o[dt], 0, 0, 0);
+  }
+}
+
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -118,7 +214,8 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
                               int width, float scale_log2, uint16_t* __restrict__ out,
                               float* __restrict__ lse) {
   using TL = PrefillTile<D, BLK>;
-  constexpr int NW = TL::NW, NT = TL::NT, KT = TL::KT, NSUB = TL::NSUB;
+  constexpr int NT = TL::NT, KT = TL::KT;
+  static_assert(TL::NSUB == 2, "two pipeline steps per block");
   __shared__ __attribute__((aligned(16))) char Ks[2][TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs[2][TL::TILE];
 
@@ -144,7 +241,6 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int hl = lane >> 5;
   const int qi = w * 32 + l32;
   const int qrow = i * BLK + qi;
-  (void)NW;
 
   // ---- this wave's Q rows as MFMA B operands ----
   bf16x8_t qf[D / 16];
@@ -159,15 +255,15 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   }
 
   // ---- staging geometry: load u of this thread fills tile chunk u * NT + tid ----
-  int k_row[TL::LOADS];
-  uint32_t k_off[TL::LOADS], v_off[TL::LOADS];
+  int k_row[TL::LOADS], k_col[TL::LOADS];
+  uint32_t v_off[TL::LOADS];
 #pragma unroll
   for (int u = 0; u < TL::LOADS; ++u) {
     const int qc = u * NT + tid;
     const int kr = qc / TL::KCH;
     const int kp = qc % TL::KCH;
     k_row[u] = kr;
-    k_off[u] = (uint32_t)(kr * kstride + (kp ^ row_swizzle<TL::KCH>(kr)) * 8);
+    k_col[u] = (kp ^ row_swizzle<TL::KCH>(kr)) * 8;
     const int vr = qc / TL::VCH;
     const int vp = qc % TL::VCH;
     v_off[u] = (uint32_t)(vr * BLK + (vp ^ row_swizzle<TL::VCH>(vr)) * 8);
@@ -175,15 +271,20 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const uint16_t* kbase = k + (int64_t)tok0 * kstride + (int64_t)kvh * D;
   const uint16_t* vtbase = vt + ((int64_t)kvh * total_blocks + blk0) * D * BLK;
 
+  // Register staging: the tiles of step s + 1 are loaded while step s
+  // computes, then stored into the other LDS buffer.
   u32x4_t kst[TL::LOADS], vst[TL::LOADS];
   auto load_step = [&](int j, int sub) {
+    // Rows past the end of the sequence (only in the last, partial block,
+    // which only its own query block selects, as its diagonal) re-read the
+    // last row: the causal mask removes those keys and their V^T is zero.
     const int key0 = j * BLK + sub * KT;
-    const uint16_t* ks = kbase + (int64_t)key0 * kstride;
     const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
+    const int last = n - 1 - key0;
 #pragma unroll
     for (int u = 0; u < TL::LOADS; ++u) {
-      kst[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (key0 + k_row[u] < n) kst[u] = *reinterpret_cast<const u32x4_t*>(ks + k_off[u]);
+      const int row = min(k_row[u], last);
+      kst[u] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(key0 + row) * kstride + k_col[u]);
       vst[u] = *reinterpret_cast<const u32x4_t*>(vs + v_off[u]);
     }
   };
@@ -214,93 +315,22 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
 
   const int nb = idx ? cnt[(int64_t)h * total_blocks + gb] : i + 1;
   const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
-  const int nsteps = nb * NSUB;
 
+  // Step 2nn uses LDS buffer 0 (first half of block nn), step 2nn + 1 buffer 1.
   int j = lst ? lst[0] : 0;
   load_step(j, 0);
   store_step(0);
   __syncthreads();
-  for (int stp = 0; stp < nsteps; ++stp) {
-    const int sub = stp % NSUB;
-    const int buf = stp & 1;
-    const bool has_next = stp + 1 < nsteps;
-    int j_next = j;
-    if (has_next) {
-      const int nn_next = (stp + 1) / NSUB;
-      j_next = (sub + 1 < NSUB) ? j : (lst ? lst[nn_next] : nn_next);
-      load_step(j_next, (stp + 1) % NSUB);
-    }
-    const char* ksb = Ks[buf];
-    const char* vsb = Vs[buf];
-
-    // ---- S^T = K Q^T for this step's KT keys ----
-    floatx16_t st[KT / 32];
-#pragma unroll
-    for (int kt = 0; kt < KT / 32; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      bf16x8_t a[KT / 32];
-#pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
-        a[kt] = *reinterpret_cast<const bf16x8_t*>(ksb + k_rd[dc] + kt * 32 * D * 2);
-#pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kt], qf[dc], st[kt], 0, 0, 0);
-    }
-
-    // ---- online softmax (log2 domain); mask only on the diagonal block ----
-    if (j == i) {
-#pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = sub * KT + kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > qi) st[kt][r] = -INFINITY;
-        }
-    }
-    float mx = st[0][0];
-#pragma unroll
-    for (int kt = 0; kt < KT / 32; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    if (__any(m_new > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_run = m_new;
-    }
-    bf16x8_t pb[KT / 16];
-#pragma unroll
-    for (int kc = 0; kc < KT / 16; ++kc) {
-      const int kt = kc >> 1;
-      const int r0 = (kc & 1) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e], scale_log2, -m_run));
-        l_run += p;
-        pb[kc][e] = (__bf16)p;
-      }
-    }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int kc = 0; kc < KT / 16; ++kc) {
-      bf16x8_t a[D / 32];
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        a[dt] = *reinterpret_cast<const bf16x8_t*>(vsb + v_rd[kc] + dt * 32 * KT * 2);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], pb[kc], o[dt], 0, 0, 0);
-    }
-    if (has_next) store_step(buf ^ 1);
+  for (int nn = 0; nn < nb; ++nn) {
+    const bool has_next = nn + 1 < nb;
+    const int j_next = has_next ? (lst ? lst[nn + 1] : nn + 1) : j;
+    load_step(j, 1);
+    attn_step<D, BLK>(j == i, Ks[0], Vs[0], 0, qf, k_rd, v_rd, o, m_run, l_run, scale_log2, qi, hl);
+    store_step(1);
+    __syncthreads();
+    if (has_next) load_step(j_next, 0);
+    attn_step<D, BLK>(j == i, Ks[1], Vs[1], KT, qf, k_rd, v_rd, o, m_run, l_run, scale_log2, qi, hl);
+    if (has_next) store_step(0);
     __syncthreads();
     j = j_next;
   }

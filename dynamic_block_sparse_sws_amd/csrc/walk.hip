@@ -35,19 +35,40 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Same sum with DPP lane permutes (no LDS round trip): swap neighbours, swap
+// pairs within a quad, then mirror the two quads of an 8-lane half row.
+template <int LPR>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  if (LPR >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if (LPR >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  return v;
+}
+
 constexpr int kWalkThreads = 256;
 constexpr int kTileJ = 64;
 
 template <int KP>
-__global__ __launch_bounds__(kWalkThreads) void walk_kernel(
+struct WalkTile {
+  static constexpr int LPR = KP / 8;                  // lanes per row
+  static constexpr int ROWS = kWalkThreads / LPR;     // rows per workgroup
+  static constexpr int XPT = ROWS * kTileJ / kWalkThreads;   // X tile values per thread
+  static constexpr int SPT = kTileJ * KP / kWalkThreads;     // sketch values per thread
+};
+
+template <int KP>
+__global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void walk_kernel(
     const float* __restrict__ q_sk, const float* __restrict__ k_sk, int hq, int hkv, int k,
     const int32_t* __restrict__ cu_blocks, int n_seqs, int total_blocks, int s,
     const float* R_prev, float* R_out, float inv_sqrt_k) {
-  constexpr int LPR = KP / 8;                  // lanes per row
-  constexpr int ROWS = kWalkThreads / LPR;     // rows per workgroup
-  __shared__ __attribute__((aligned(16))) float sq[kTileJ][KP + 4];
-  __shared__ __attribute__((aligned(16))) float sk[kTileJ][KP + 4];
-  __shared__ float sx[ROWS][kTileJ + 1];
+  using WT = WalkTile<KP>;
+  constexpr int LPR = WT::LPR, ROWS = WT::ROWS, XPT = WT::XPT, SPT = WT::SPT;
+  __shared__ __attribute__((aligned(16))) float sq[2][kTileJ][KP + 4];
+  __shared__ __attribute__((aligned(16))) float sk[2][kTileJ][KP + 4];
+  __shared__ float sx[2][ROWS][kTileJ + 1];
   __shared__ float smax[ROWS];
 
   const int seq = blockIdx.z;
@@ -66,64 +87,129 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(
   const int tid = threadIdx.x;
   const int r = tid / LPR;
   const int part = tid % LPR;
-  const int i = i0 + r;
   const int jmax = min(b, i0 + ROWS) - 1;
   const int top_tile = (jmax / kTileJ) * kTileJ;
 
-  float sc = 1.0f;   // rescale of this row's input for the current hop
-  float mx = 0.0f;
-  for (int hop = 0; hop < s; ++hop) {
-    const float* src = (hop == 0) ? Rp : Rh;
-    const bool ident = (hop == 0) && (Rp == nullptr);
-    float S[8];
+  // prefetch registers for one tile (X values and sketch rows).  Thread tid
+  // covers column tid % 64 of rows tid / 64 + (256 / 64) * e of the X tile,
+  // and elements tid + 256 * e of the (64 x KP) sketch tiles.
+  constexpr int RSTEP = kWalkThreads / kTileJ;
+  const int xc = tid % kTileJ;
+  const int xr0 = tid / kTileJ;
+  float xr[XPT], qr[SPT], kr[SPT];
+  auto fetch = [&](int jt, const float* src, bool ident) {
+    const int j = jt + xc;
+    if (ident) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) S[c] = 0.f;
-    mx = 0.0f;
-    for (int jt = top_tile; jt >= 0; jt -= kTileJ) {
-      __syncthreads();
-      // stage sketch rows jt .. jt + 63 (zero beyond the sequence / beyond k)
-      for (int e = tid; e < kTileJ * KP; e += kWalkThreads) {
-        const int jj = e / KP, c = e % KP;
-        const int j = jt + jj;
-        const bool ok = (j < b) && (c < k);
-        sq[jj][c] = ok ? qs[(int64_t)j * k + c] : 0.f;
-        sk[jj][c] = ok ? ks[(int64_t)j * k + c] : 0.f;
-      }
-      // stage the X tile: rows i0 .. i0 + ROWS - 1, columns jt .. jt + 63
-      for (int e = tid; e < ROWS * kTileJ; e += kWalkThreads) {
-        const int rr = e / kTileJ, jj = e % kTileJ;
-        const int ii = i0 + rr, j = jt + jj;
-        float v = 0.f;
-        if (ii < b && j <= ii) {
-          if (ident) v = (j == ii) ? 1.f : 0.f;
-          else v = src[(int64_t)ii * b + j];
-        }
-        sx[rr][jj] = v;
-      }
-      __syncthreads();
-      for (int jj = kTileJ - 1; jj >= 0; --jj) {
-        const float x = sx[r][jj] * sc;
-        const float4 qa = *reinterpret_cast<const float4*>(&sq[jj][part * 8]);
-        const float4 qb = *reinterpret_cast<const float4*>(&sq[jj][part * 8 + 4]);
-        const float4 ka = *reinterpret_cast<const float4*>(&sk[jj][part * 8]);
-        const float4 kb = *reinterpret_cast<const float4*>(&sk[jj][part * 8 + 4]);
-        S[0] += x * qa.x; S[1] += x * qa.y; S[2] += x * qa.z; S[3] += x * qa.w;
-        S[4] += x * qb.x; S[5] += x * qb.y; S[6] += x * qb.z; S[7] += x * qb.w;
-        float y = ka.x * S[0] + ka.y * S[1] + ka.z * S[2] + ka.w * S[3] +
-                  kb.x * S[4] + kb.y * S[5] + kb.z * S[6] + kb.w * S[7];
-        y = group_sum<LPR>(y) * inv_sqrt_k;
-        if (part == 0) sx[r][jj] = y;
-        mx = fmaxf(mx, fabsf(y));
-      }
-      __syncthreads();
-      for (int e = tid; e < ROWS * kTileJ; e += kWalkThreads) {
-        const int rr = e / kTileJ, jj = e % kTileJ;
-        const int ii = i0 + rr, j = jt + jj;
-        if (ii < b && j <= ii) Rh[(int64_t)ii * b + j] = sx[rr][jj];
+      for (int e = 0; e < XPT; ++e) xr[e] = (i0 + xr0 + RSTEP * e == j) ? 1.f : 0.f;
+    } else if (jt + kTileJ - 1 <= i0 && i0 + ROWS <= b) {
+      // tile entirely below the diagonal and inside the matrix: no guards
+      const float* p = src + (int64_t)(i0 + xr0) * b + j;
+      const int64_t step = (int64_t)RSTEP * b;
+#pragma unroll
+      for (int e = 0; e < XPT; ++e) xr[e] = p[step * e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < XPT; ++e) {
+        const int ii = i0 + xr0 + RSTEP * e;
+        xr[e] = (ii < b && j <= ii) ? src[(int64_t)ii * b + j] : 0.f;
       }
     }
-    sc = (mx > 0.f) ? 1.0f / mx : 1.0f;
+    if (k == KP && jt + kTileJ <= b) {
+      const float* pq = qs + (int64_t)jt * KP + tid;
+      const float* pk = ks + (int64_t)jt * KP + tid;
+#pragma unroll
+      for (int e = 0; e < SPT; ++e) {
+        qr[e] = pq[kWalkThreads * e];
+        kr[e] = pk[kWalkThreads * e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < SPT; ++e) {
+        const int idx = tid + e * kWalkThreads;
+        const int jj = idx / KP, c = idx % KP;
+        const bool ok = (jt + jj < b) && (c < k);
+        qr[e] = ok ? qs[(int64_t)(jt + jj) * k + c] : 0.f;
+        kr[e] = ok ? ks[(int64_t)(jt + jj) * k + c] : 0.f;
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < XPT; ++e) sx[buf][xr0 + RSTEP * e][xc] = xr[e];
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      const int idx = tid + e * kWalkThreads;
+      sq[buf][idx / KP][idx % KP] = qr[e];
+      sk[buf][idx / KP][idx % KP] = kr[e];
+    }
+  };
+
+  // One flat software pipeline over (hop, tile) steps, tiles from the last
+  // column down: step st computes tile st while tile st + 1 is fetched.
+  const int ntiles = top_tile / kTileJ + 1;
+  const int nsteps = s * ntiles;
+  float sc = 1.0f;   // rescale of this row's input for the current hop
+  float mx = 0.0f;   // largest |y| of this row in the current hop
+  float mx_prev = 0.0f;
+  float S[8];
+  int buf = 0;
+  // With a single column tile the next hop re-reads the tile this step writes,
+  // so its fetch has to wait for the write-back.
+  const bool late = (ntiles == 1);
+  auto fetch_step = [&](int st1) {
+    const int hop1 = st1 / ntiles;
+    const int jt1 = top_tile - (st1 % ntiles) * kTileJ;
+    fetch(jt1, hop1 == 0 ? Rp : Rh, hop1 == 0 && Rp == nullptr);
+  };
+  for (int st = -1; st < nsteps; ++st) {
+    // fetch step st + 1 into registers
+    if (st + 1 < nsteps && (!late || st < 0)) fetch_step(st + 1);
+    if (st >= 0) {
+      const int t = st % ntiles;
+      const int jt = top_tile - t * kTileJ;
+      if (t == 0) {
+        // a new hop: reset the scan, rescale by the previous hop's maximum
+        if (st > 0) {
+          mx_prev = mx;
+          sc = (mx > 0.f) ? 1.0f / mx : 1.0f;
+        }
+        mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) S[c] = 0.f;
+      }
+#pragma unroll 4
+      for (int jj = kTileJ - 1; jj >= 0; --jj) {
+        const float x = sx[buf][r][jj] * sc;
+        const float4 qa = *reinterpret_cast<const float4*>(&sq[buf][jj][part * 8]);
+        const float4 qb = *reinterpret_cast<const float4*>(&sq[buf][jj][part * 8 + 4]);
+        const float4 ka = *reinterpret_cast<const float4*>(&sk[buf][jj][part * 8]);
+        const float4 kb = *reinterpret_cast<const float4*>(&sk[buf][jj][part * 8 + 4]);
+        S[0] += x * qa.x; S[1] += x * qa.y; S[2] += x * qa.z; S[3] += x * qa.w;
+        S[4] += x * qb.x; S[5] += x * qb.y; S[6] += x * qb.z; S[7] += x * qb.w;
+        const float yp = (ka.x * S[0] + ka.y * S[1]) + (ka.z * S[2] + ka.w * S[3]) +
+                         ((kb.x * S[4] + kb.y * S[5]) + (kb.z * S[6] + kb.w * S[7]));
+        const float y = group_sum_dpp<LPR>(yp) * inv_sqrt_k;
+        mx = fmaxf(mx, fabsf(y));
+        if (part == 0) sx[buf][r][jj] = y;
+      }
+      __syncthreads();
+      // write the finished tile back (rows are owned by this workgroup)
+      for (int e = tid; e < ROWS * kTileJ; e += kWalkThreads) {
+        const int rr = e / kTileJ, jj = e % kTileJ;
+        const int ii = i0 + rr, j = jt + jj;
+        if (ii < b && j <= ii) Rh[(int64_t)ii * b + j] = sx[buf][rr][jj];
+      }
+      buf ^= 1;
+      if (late && st + 1 < nsteps) {
+        __syncthreads();
+        fetch_step(st + 1);
+      }
+    }
+    if (st + 1 < nsteps) stash(buf);
+    __syncthreads();
   }
+  (void)mx_prev;
   if (part == 0) smax[r] = mx;
   __syncthreads();
   // final pass: divide by the row maximum, zero the upper triangle
