@@ -19,6 +19,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSplitTokens = 512;
 constexpr int kDecThreads = 256;
 
+// Sum over the TPL consecutive lanes that share a token row (TPL in {8, 16}),
+// with DPP lane permutes: swap neighbours, swap pairs, mirror within 8, mirror
+// within 16.
+template <int TPL>
+__device__ __forceinline__ float token_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  if (TPL == 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
 template <typename T, int D, int BLK, int GMAX>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -28,7 +41,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
   constexpr int BPS = kSplitTokens / BLK;      // blocks per split
   constexpr int TPL = D / 8;                   // lanes per token row
-  constexpr int SLOTS = kDecThreads / TPL;     // tokens processed in parallel
+  constexpr int SLOTS = kDecThreads / TPL;     // token rows per pass
+  constexpr int UNR = 8;                       // token rows in flight per lane
   __shared__ float sc[GMAX][kSplitTokens];
   __shared__ float sm[GMAX], sl[GMAX];
   __shared__ float red[kDecThreads / 64][GMAX][D];
@@ -60,29 +74,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int32_t* ul = uidx ? uidx + ((int64_t)seq * hkv + g) * uwidth : nullptr;
   const uint32_t* um = umask ? umask + ((int64_t)seq * hkv + g) * uwidth : nullptr;
   const uint32_t all = (1u << G) - 1u;
-
-  // ---- phase 1: scores of every token of the chunk for every head ----
   const int ntok = (e1 - e0) * BLK;
-  for (int tt = slot; tt < ntok; tt += SLOTS) {
+
+  // Chunk token tt -> cache row; rows past the chunk map to ctx (masked).
+  auto token_row = [&](int tt) -> int {
+    if (tt >= ntok) return ctx;
     const int e = e0 + tt / BLK;
     const int blk = ul ? ul[e] : e;
-    const uint32_t mk = um ? um[e] : all;
-    const int tok = blk * BLK + (tt % BLK);
-    float kv[8];
-    if (tok < ctx) load8_f32(kb + (int64_t)tok * rstride, kv);
-    else
+    return blk * BLK + (tt % BLK);
+  };
+
+  // ---- phase 1: scores of every token of the chunk for every head ----
+  // UNR rows are loaded before any is used; rows at or past ctx read row
+  // ctx - 1 (in bounds) and are masked.
+  for (int base = 0; base < ntok; base += UNR * SLOTS) {
+    float kv[UNR][8];
+    int tok[UNR];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) kv[x] = 0.f;
+    for (int u = 0; u < UNR; ++u) {
+      tok[u] = token_row(base + u * SLOTS + slot);
+      load8_f32(kb + (int64_t)min(tok[u], ctx - 1) * rstride, kv[u]);
+    }
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh < G) {
-        float part = 0.f;
+    for (int u = 0; u < UNR; ++u) {
+      const int tt = base + u * SLOTS + slot;
+      const uint32_t mk = (tt < ntok) ? (um ? um[e0 + tt / BLK] : all) : 0u;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) part += qv[hh][x] * kv[x];
+      for (int hh = 0; hh < GMAX; ++hh) {
+        if (hh < G) {
+          float part = 0.f;
 #pragma unroll
-        for (int off = 1; off < TPL; off <<= 1) part += __shfl_xor(part, off);
-        if (ch == 0)
-          sc[hh][tt] = (tok < ctx && ((mk >> hh) & 1u)) ? part * scale_log2 : -INFINITY;
+          for (int x = 0; x < 8; ++x) part += qv[hh][x] * kv[u][x];
+          part = token_sum<TPL>(part);
+          if (ch == 0 && tt < ntok)
+            sc[hh][tt] = (tok[u] < ctx && ((mk >> hh) & 1u)) ? part * scale_log2 : -INFINITY;
+        }
       }
     }
   }
@@ -105,25 +131,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     if (lane == 0) { sm[hh] = mx; sl[hh] = sum; }
   }
   __syncthreads();
-  // ---- phase 3: weighted V sums ----
+  // ---- phase 3: weighted V sums (masked rows carry weight 0) ----
   float acc[GMAX][8];
 #pragma unroll
   for (int hh = 0; hh < GMAX; ++hh)
 #pragma unroll
     for (int x = 0; x < 8; ++x) acc[hh][x] = 0.f;
-  for (int tt = slot; tt < ntok; tt += SLOTS) {
-    const int e = e0 + tt / BLK;
-    const int blk = ul ? ul[e] : e;
-    const int tok = blk * BLK + (tt % BLK);
-    if (tok >= ctx) continue;
-    float vv[8];
-    load8_f32(vb + (int64_t)tok * rstride, vv);
+  for (int base = 0; base < ntok; base += UNR * SLOTS) {
+    float vv[UNR][8];
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh < G) {
-        const float p = sc[hh][tt];
+    for (int u = 0; u < UNR; ++u) {
+      const int t = token_row(base + u * SLOTS + slot);
+      load8_f32(vb + (int64_t)min(t, ctx - 1) * rstride, vv[u]);
+    }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[hh][x] += p * vv[x];
+    for (int u = 0; u < UNR; ++u) {
+      const int tt = base + u * SLOTS + slot;
+      if (tt < ntok) {
+#pragma unroll
+        for (int hh = 0; hh < GMAX; ++hh) {
+          if (hh < G) {
+            const float p = sc[hh][tt];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[hh][x] += p * vv[u][x];
+          }
+        }
       }
     }
   }
@@ -162,12 +194,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
+// Merge of the split states of one (sequence, query head): the weights
+// exp2(m_s - max m) go to LDS once, then each thread sums one feature over the
+// splits with independent loads.
+constexpr int kMaxSplits = 1024;
+
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(D) void decode_combine_kernel(
     const int32_t* __restrict__ ctx_len, int hq, int hkv, const int32_t* __restrict__ uidx,
     const int32_t* __restrict__ ucnt, int max_splits, const float* __restrict__ ws_ml,
     const float* __restrict__ ws_acc, T* __restrict__ out, float* __restrict__ lse) {
   constexpr int BPS = kSplitTokens / BLK;
+  constexpr int NW = D / 64;
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[NW];
+  __shared__ float s_M, s_L;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int G = hq / hkv;
@@ -176,22 +217,52 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   const int nblk = uidx ? ucnt[seq * hkv + g] : (ctx + BLK - 1) / BLK;
   const int ns = (nblk + BPS - 1) / BPS;
   const int64_t row0 = ((int64_t)seq * hq + h) * max_splits;
-  float M = -INFINITY;
-  for (int sidx = 0; sidx < ns; ++sidx) M = fmaxf(M, ws_ml[(row0 + sidx) * 2]);
-  float L = 0.f, a = 0.f;
-  const int dd = threadIdx.x;
-  for (int sidx = 0; sidx < ns; ++sidx) {
-    const float m = ws_ml[(row0 + sidx) * 2];
-    if (m == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(m - M);
-    L += f * ws_ml[(row0 + sidx) * 2 + 1];
-    a += f * ws_acc[(row0 + sidx) * D + dd];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  float m = -INFINITY;
+  for (int si = t; si < ns; si += D) {
+    const float v = ws_ml[(row0 + si) * 2];
+    wgt[si] = v;
+    m = fmaxf(m, v);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (t == 0) {
+    float M = red[0];
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
+    s_M = M;
+  }
+  __syncthreads();
+  const float M = s_M;
+  float lsum = 0.f;
+  for (int si = t; si < ns; si += D) {
+    const float mv = wgt[si];
+    const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+    wgt[si] = f;
+    lsum += f * ws_ml[(row0 + si) * 2 + 1];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+  __syncthreads();
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  if (t == 0) {
+    float L = 0.f;
+    for (int w = 0; w < NW; ++w) L += red[w];
+    s_L = L;
+  }
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll 8
+  for (int si = 0; si < ns; ++si) a += wgt[si] * ws_acc[(row0 + si) * D + t];
+  const float L = s_L;
   const float o = a / L;
-  T* op = out + ((int64_t)seq * hq + h) * D + dd;
+  T* op = out + ((int64_t)seq * hq + h) * D + t;
   if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t*>(op) = (uint16_t)f32_to_bf16_bits(o);
   else *op = o;
-  if (lse && dd == 0) lse[(int64_t)seq * hq + h] = (M + log2f(L)) * kLn2;
+  if (lse && t == 0) lse[(int64_t)seq * hq + h] = (M + log2f(L)) * kLn2;
 }
 
 template <typename T, int D, int BLK, int GMAX>

@@ -108,10 +108,13 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ R
 
 // Decode: the open block c of each sequence; one workgroup per (sequence, KV
 // group), one wave per query head of the group; union through an LDS mask.
-constexpr int kRowBmax = 8192;
+constexpr int kRowBmax = 4096;
 
-template <int E>
-__global__ __launch_bounds__(1024) void select_row_kernel(
+// E: key registers per lane (rows up to 64 * E blocks); NT: 64 * (largest
+// group size the instance serves), so small groups get the larger register
+// budget and keep every key in registers.
+template <int E, int NT>
+__global__ __launch_bounds__(NT) void select_row_kernel(
     const float* __restrict__ r, int hq, int hkv, const int32_t* __restrict__ cur_block,
     int b_max, int rho, int dense, int width, int32_t* __restrict__ idx,
     int32_t* __restrict__ cnt, int32_t* __restrict__ union_idx,
@@ -225,18 +228,21 @@ hipError_t launch_select_row(const float* r, int hq, int hkv, int n_seqs,
   const int G = hq / hkv;
   dim3 grid(hkv, n_seqs);
   dim3 block(64 * G);
-  if (b_max <= 1024)
-    hipLaunchKernelGGL((select_row_kernel<16>), grid, block, 0, st, r, hq, hkv, cur_block, b_max,
-                       rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,
-                       union_width);
-  else if (b_max <= 4096)
-    hipLaunchKernelGGL((select_row_kernel<64>), grid, block, 0, st, r, hq, hkv, cur_block, b_max,
-                       rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,
-                       union_width);
-  else
-    hipLaunchKernelGGL((select_row_kernel<128>), grid, block, 0, st, r, hq, hkv, cur_block,
-                       b_max, rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,
-                       union_width);
+#define SWS_SEL_ROW(E, NT)                                                                     \
+  hipLaunchKernelGGL((select_row_kernel<E, NT>), grid, block, 0, st, r, hq, hkv, cur_block,   \
+                     b_max, rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,     \
+                     union_width)
+#define SWS_SEL_ROW_NT(E)           \
+  do {                              \
+    if (G <= 4) SWS_SEL_ROW(E, 256);  \
+    else if (G <= 8) SWS_SEL_ROW(E, 512); \
+    else SWS_SEL_ROW(E, 1024);      \
+  } while (0)
+  if (b_max <= 1024) SWS_SEL_ROW_NT(16);
+  else if (b_max <= 2048) SWS_SEL_ROW_NT(32);
+  else SWS_SEL_ROW_NT(64);
+#undef SWS_SEL_ROW_NT
+#undef SWS_SEL_ROW
   return hipGetLastError();
 }
 

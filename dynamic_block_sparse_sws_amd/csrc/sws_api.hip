@@ -143,8 +143,8 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
   if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
-  if (n_seqs < 0 || b_max < 1 || b_max > 8192)
-    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,8192])", fn, n_seqs, b_max);
+  if (n_seqs < 0 || b_max < 1 || b_max > 4096)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,4096])", fn, n_seqs, b_max);
   if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
   return launched(sws::launch_walk_row(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs, cur_block,
                                        b_max, s, r_prev, r_out, (hipStream_t)stream),
@@ -188,8 +188,8 @@ int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
   if (hq / hkv > 16) return fail(SWS_ERR_UNSUPPORTED, "%s: hq/hkv=%d > 16", fn, hq / hkv);
-  if (n_seqs < 0 || b_max < 1 || b_max > 8192)
-    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,8192])", fn, n_seqs, b_max);
+  if (n_seqs < 0 || b_max < 1 || b_max > 4096)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,4096])", fn, n_seqs, b_max);
   if (rho_percent < 0 || rho_percent > 100)
     return fail(SWS_ERR_SHAPE, "%s: rho_percent=%d outside [0,100]", fn, rho_percent);
   const int tmax = tau_of(rho_percent, b_max);
@@ -278,6 +278,9 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d max_ctx=%d", fn, n_seqs, max_ctx);
   const int uw = union_idx ? union_width : (max_ctx + B - 1) / B;
   if (union_idx && union_width < 1) return fail(SWS_ERR_SHAPE, "%s: union_width=%d", fn, union_width);
+  if ((int64_t)uw * B > 524288)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: %d blocks of %d tokens exceed 1024 chunks of 512", fn,
+                uw, B);
   if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(SWS_ERR_SHAPE, "%s: q/k_cache/v_cache must be 16-byte aligned", fn);

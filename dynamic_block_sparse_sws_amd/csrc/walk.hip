@@ -229,21 +229,48 @@ void walk_kernel(
 // ---------------------------------------------------------------------------
 // decode: one row per (sequence, query head)
 // ---------------------------------------------------------------------------
-constexpr int kRowThreads = 1024;
-constexpr int kRowLmax = 5;     // sketch rows per segment held in registers
-constexpr int kRowBmax = 8192;
+// 512 threads.  Thread t works on component quarter p = t / 128 of the
+// sketches (KP / 4 components) and on segment g = t % 128 of the rows j, the
+// segments taken in descending j order so that the suffix sum over j becomes
+// a prefix scan over the threads of a quarter.  The segment's q and k sketch
+// rows stay in registers for all s hops (longer rows stream them from
+// memory); each hop is: segment totals, a DPP wave scan plus an LDS scan of
+// the quarter's two wave totals, the segment's partial dot products, a sum
+// over the four quarters in LDS, and the row maximum.
+constexpr int kRowThreads = 512;
+constexpr int kRowSeg = 128;        // segments (threads per component quarter)
+constexpr int kRowBmax = 4096;      // xs / ypart capacity (largest row)
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
+// 16-lane rows, then broadcasts of lanes 15 and 31 into the following rows).
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  int x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
 
 template <int KP>
 __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
     const float* __restrict__ q_cache, const float* __restrict__ k_cache, int hq, int hkv,
     int k, const int32_t* __restrict__ cur_block, int b_max, int s, const float* r_prev,
     float* r_out, float inv_sqrt_k) {
-  constexpr int LPR = KP / 8;
-  constexpr int NSEG = kRowThreads / LPR;
-  constexpr int SPW = 64 / LPR;              // segments per wave
+  constexpr int CQ = KP / 4;                  // components per quarter
+  constexpr int LMAX = 80 / CQ;               // segment rows held in registers
   constexpr int NWAVE = kRowThreads / 64;
+  constexpr int WPQ = kRowSeg / 64;           // waves per quarter
   __shared__ float xs[kRowBmax];
-  __shared__ float wtot[NWAVE][KP];
+  __shared__ float ypart[4][kRowBmax];
+  __shared__ float wtot[NWAVE][CQ];
   __shared__ float wmax[NWAVE];
 
   const int h = blockIdx.x;
@@ -254,122 +281,117 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int seg = tid / LPR;
-  const int seg_in_wave = lane / LPR;
-  const int part = tid % LPR;
-  const int L = (b + NSEG - 1) / NSEG;
+  const int p = tid / kRowSeg;
+  const int g = tid % kRowSeg;
+  const int L = (b + kRowSeg - 1) / kRowSeg;
+  const bool in_regs = L <= LMAX;
+  const int seg = kRowSeg - 1 - g;            // descending j order
   const int j0 = min(b, seg * L);
   const int j1 = min(b, j0 + L);
-  const bool in_regs = (L <= kRowLmax);
 
   const float* qrow = q_cache + ((int64_t)seq * hq + h) * b_max * k;
   const float* krow = k_cache + ((int64_t)seq * hkv + h / grp) * b_max * k;
   const float* rin = r_prev ? r_prev + ((int64_t)seq * hq + h) * b_max : nullptr;
   float* rout = r_out + ((int64_t)seq * hq + h) * b_max;
 
-  float qv[kRowLmax][8], kv[kRowLmax][8];
+  float qv[LMAX][CQ], kv[LMAX][CQ];
 #pragma unroll
-  for (int l = 0; l < kRowLmax; ++l) {
+  for (int l = 0; l < LMAX; ++l)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < CQ; ++e) {
       const int j = j0 + l;
-      const int cc = part * 8 + e;
-      const bool ok = in_regs && (j < j1) && (cc < k);
+      const int cc = p * CQ + e;
+      const bool ok = in_regs && j < j1 && cc < k;
       qv[l][e] = ok ? qrow[(int64_t)j * k + cc] : 0.f;
       kv[l][e] = ok ? krow[(int64_t)j * k + cc] : 0.f;
     }
-  }
-  for (int j = tid; j < b; j += kRowThreads)
-    xs[j] = rin ? rin[j] : (j == c ? 1.0f : 0.0f);
+  for (int j = tid; j < b; j += kRowThreads) xs[j] = rin ? rin[j] : (j == c ? 1.0f : 0.0f);
   __syncthreads();
+
+  auto qget = [&](int l, int e) -> float {
+    if (in_regs) return qv[l][e];
+    const int cc = p * CQ + e;
+    return cc < k ? qrow[(int64_t)(j0 + l) * k + cc] : 0.f;
+  };
+  auto kget = [&](int l, int e) -> float {
+    if (in_regs) return kv[l][e];
+    const int cc = p * CQ + e;
+    return cc < k ? krow[(int64_t)(j0 + l) * k + cc] : 0.f;
+  };
 
   float sc = 1.0f;
   float gmax = 0.0f;
   for (int hop = 0; hop < s; ++hop) {
-    // pass 1: segment totals T = sum_j x_j qs_j (this lane's 8 components)
-    float T[8];
+    float T[CQ];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) T[e] = 0.f;
+    for (int e = 0; e < CQ; ++e) T[e] = 0.f;
     if (in_regs) {
 #pragma unroll
-      for (int l = 0; l < kRowLmax; ++l) {
+      for (int l = 0; l < LMAX; ++l) {
         if (j0 + l < j1) {
           const float x = xs[j0 + l] * sc;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) T[e] += x * qv[l][e];
+          for (int e = 0; e < CQ; ++e) T[e] += x * qv[l][e];
         }
       }
     } else {
-      for (int j = j0; j < j1; ++j) {
-        const float x = xs[j] * sc;
+      for (int l = 0; l < j1 - j0; ++l) {
+        const float x = xs[j0 + l] * sc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int cc = part * 8 + e;
-          T[e] += x * (cc < k ? qrow[(int64_t)j * k + cc] : 0.f);
-        }
+        for (int e = 0; e < CQ; ++e) T[e] += x * qget(l, e);
       }
     }
-    // inclusive suffix scan over the segments of this wave
-    float incl[8];
+    // exclusive prefix over the scan order = suffix over the rows above
+    float S[CQ];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = T[e];
-#pragma unroll
-      for (int off = 1; off < SPW; off <<= 1) {
-        const float o = __shfl_down(v, off * LPR);
-        if (seg_in_wave + off < SPW) v += o;
-      }
-      incl[e] = v;
-    }
-    if (seg_in_wave == 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wtot[wave][part * 8 + e] = incl[e];
+    for (int e = 0; e < CQ; ++e) {
+      const float inc = wave_prefix_sum(T[e]);
+      S[e] = inc - T[e];
+      if (lane == 63) wtot[wave][e] = inc;
     }
     __syncthreads();
-    // carry from later waves + exclusive suffix within the wave
-    float S[8];
+    {
+      const int w0 = p * WPQ;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float cw = 0.f;
-      for (int w2 = NWAVE - 1; w2 > wave; --w2) cw += wtot[w2][part * 8 + e];
-      const float nxt = __shfl_down(incl[e], LPR);
-      S[e] = cw + ((seg_in_wave + 1 < SPW) ? nxt : 0.f);
+      for (int e = 0; e < CQ; ++e) {
+        float carry = 0.f;
+        for (int w2 = w0; w2 < wave; ++w2) carry += wtot[w2][e];
+        S[e] += carry;
+      }
     }
-    // pass 2: y_j = ks_j . S_j / sqrt(k), scanning j downwards
-    float lmax = 0.f;
     if (in_regs) {
 #pragma unroll
-      for (int l = kRowLmax - 1; l >= 0; --l) {
+      for (int l = LMAX - 1; l >= 0; --l) {
         if (j0 + l < j1) {
           const float x = xs[j0 + l] * sc;
           float y = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < CQ; ++e) {
             S[e] += x * qv[l][e];
             y += kv[l][e] * S[e];
           }
-          y = group_sum<LPR>(y) * inv_sqrt_k;
-          if (part == 0) xs[j0 + l] = y;
-          lmax = fmaxf(lmax, fabsf(y));
+          ypart[p][j0 + l] = y;
         }
       }
     } else {
-      for (int j = j1 - 1; j >= j0; --j) {
-        const float x = xs[j] * sc;
+      for (int l = j1 - j0 - 1; l >= 0; --l) {
+        const float x = xs[j0 + l] * sc;
         float y = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int cc = part * 8 + e;
-          const bool ok = cc < k;
-          S[e] += x * (ok ? qrow[(int64_t)j * k + cc] : 0.f);
-          y += (ok ? krow[(int64_t)j * k + cc] : 0.f) * S[e];
+        for (int e = 0; e < CQ; ++e) {
+          S[e] += x * qget(l, e);
+          y += kget(l, e) * S[e];
         }
-        y = group_sum<LPR>(y) * inv_sqrt_k;
-        if (part == 0) xs[j] = y;
-        lmax = fmaxf(lmax, fabsf(y));
+        ypart[p][j0 + l] = y;
       }
     }
-    // row maximum
+    __syncthreads();
+    float lmax = 0.f;
+    for (int j = tid; j < b; j += kRowThreads) {
+      const float y = ((ypart[0][j] + ypart[1][j]) + (ypart[2][j] + ypart[3][j])) * inv_sqrt_k;
+      xs[j] = y;
+      lmax = fmaxf(lmax, fabsf(y));
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
     if (lane == 0) wmax[wave] = lmax;
@@ -378,7 +400,6 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
 #pragma unroll
     for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
     sc = (gmax > 0.f) ? 1.0f / gmax : 1.0f;
-    __syncthreads();
   }
   for (int j = tid; j < b_max; j += kRowThreads) {
     float v = 0.f;

@@ -74,7 +74,7 @@ def test_other_entry_points_validation():
     assert L.sws_walk_update(P, P, 8, 4, 32, P, 1, 4, 4, 0, N, P, N) == 2
     assert L.sws_walk_update(P, P, 8, 4, 0, P, 1, 4, 4, 8, N, P, N) == 3
     assert L.sws_walk_update(N, P, 8, 4, 32, P, 1, 4, 4, 8, N, P, N) == 1
-    assert L.sws_walk_update_row(P, P, 8, 4, 32, 2, P, 9000, 8, N, P, N) == 2
+    assert L.sws_walk_update_row(P, P, 8, 4, 32, 2, P, 5000, 8, N, P, N) == 2
     # select: width too small, rho out of range, too many blocks
     assert L.sws_select_topk(P, 8, P, 1, 1024, 1024, 20, 0, 204, P, P, N) == 2
     assert L.sws_select_topk(P, 8, P, 1, 1024, 1024, 101, 0, 1024, P, P, N) == 2
