@@ -146,6 +146,8 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
   if (n_seqs < 0 || b_max < 1 || b_max > 4096)
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,4096])", fn, n_seqs, b_max);
   if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
+  if (!aligned16(q_sk_cache) || !aligned16(k_sk_cache))
+    return fail(SWS_ERR_SHAPE, "%s: q_sk_cache / k_sk_cache must be 16-byte aligned", fn);
   return launched(sws::launch_walk_row(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs, cur_block,
                                        b_max, s, r_prev, r_out, (hipStream_t)stream),
                   fn);
@@ -278,8 +280,8 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d max_ctx=%d", fn, n_seqs, max_ctx);
   const int uw = union_idx ? union_width : (max_ctx + B - 1) / B;
   if (union_idx && union_width < 1) return fail(SWS_ERR_SHAPE, "%s: union_width=%d", fn, union_width);
-  if ((int64_t)uw * B > 524288)
-    return fail(SWS_ERR_UNSUPPORTED, "%s: %d blocks of %d tokens exceed 1024 chunks of 512", fn,
+  if ((int64_t)uw * B > 1048576)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: %d blocks of %d tokens exceed 1024 chunks of 1024", fn,
                 uw, B);
   if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))

@@ -295,16 +295,32 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   float* rout = r_out + ((int64_t)seq * hq + h) * b_max;
 
   float qv[LMAX][CQ], kv[LMAX][CQ];
+  if (in_regs && k == KP) {
+    // full quarters: 16-byte loads of every segment row (rows past the
+    // segment re-read row b - 1 and are never used), no branches
 #pragma unroll
-  for (int l = 0; l < LMAX; ++l)
+    for (int l = 0; l < LMAX; ++l) {
+      const int64_t off = (int64_t)min(j0 + l, b - 1) * KP + p * CQ;
 #pragma unroll
-    for (int e = 0; e < CQ; ++e) {
-      const int j = j0 + l;
-      const int cc = p * CQ + e;
-      const bool ok = in_regs && j < j1 && cc < k;
-      qv[l][e] = ok ? qrow[(int64_t)j * k + cc] : 0.f;
-      kv[l][e] = ok ? krow[(int64_t)j * k + cc] : 0.f;
+      for (int e = 0; e < CQ; e += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(qrow + off + e);
+        const float4 bb = *reinterpret_cast<const float4*>(krow + off + e);
+        qv[l][e] = a.x; qv[l][e + 1] = a.y; qv[l][e + 2] = a.z; qv[l][e + 3] = a.w;
+        kv[l][e] = bb.x; kv[l][e + 1] = bb.y; kv[l][e + 2] = bb.z; kv[l][e + 3] = bb.w;
+      }
     }
+  } else {
+#pragma unroll
+    for (int l = 0; l < LMAX; ++l)
+#pragma unroll
+      for (int e = 0; e < CQ; ++e) {
+        const int j = j0 + l;
+        const int cc = p * CQ + e;
+        const bool ok = in_regs && j < j1 && cc < k;
+        qv[l][e] = ok ? qrow[(int64_t)j * k + cc] : 0.f;
+        kv[l][e] = ok ? krow[(int64_t)j * k + cc] : 0.f;
+      }
+  }
   for (int j = tid; j < b; j += kRowThreads) xs[j] = rin ? rin[j] : (j == c ? 1.0f : 0.0f);
   __syncthreads();
 

@@ -136,7 +136,8 @@ int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hk
  * open block c = cur_block[seq] (blog page, section 5).  Equals row c of
  * sws_walk_update over the first c + 1 blocks.
  *
- *   q_sk_cache [n_seqs][hq][b_max][k], k_sk_cache [n_seqs][hkv][b_max][k] fp32
+ *   q_sk_cache [n_seqs][hq][b_max][k], k_sk_cache [n_seqs][hkv][b_max][k] fp32,
+ *              both 16-byte aligned
  *   cur_block  [n_seqs] int32, 0 <= cur_block < b_max; b_max <= 4096
  *   r_prev     NULL (the unit row e_c) or [n_seqs][hq][b_max]; may equal r_out
  *   r_out      [n_seqs][hq][b_max]; entries above cur_block are written 0
@@ -232,8 +233,8 @@ size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, 
  *   out     [n_seqs][hq][d] (dtype of q); lse optional [n_seqs][hq] fp32
  *   ws      workspace of at least sws_decode_workspace_size(...) bytes
  *   d in {64, 128}; B in {64, 128}; hq / hkv <= 16; the list is cut into
- *   chunks of 512 tokens and at most 1024 chunks are supported
- *   (union_width * B <= 524288), else SWS_ERR_UNSUPPORTED
+ *   chunks of 1024 tokens and at most 1024 chunks are supported
+ *   (union_width * B <= 1048576), else SWS_ERR_UNSUPPORTED
  */
 int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
                            const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
