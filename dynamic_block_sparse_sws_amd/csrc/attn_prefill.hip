@@ -5,14 +5,14 @@
 // bf16 path: one workgroup per (query head, query block of B tokens), B/32
 // wavefronts, each owning 32 query rows.  A pre-pass writes V transposed per
 // block (keys in accumulator-row order) to a workspace.  The selected key
-// blocks are walked in steps of 64 keys (32 when B = 64): the K and V^T tiles
+// blocks are walked in steps of 32 keys: the K and V^T tiles
 // of the next step are loaded into registers while the current step
 // computes, then stored into the other half of a double-buffered, XOR-swizzled
 // LDS tile pair (one barrier per step).  Each wave runs a FlashAttention-style
 // step on the matrix cores with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T          (A = K rows from LDS, B = this wave's Q in registers)
 //   online softmax       (a lane holds one query column: the row max over the
-//                         block is 64 in-register values plus one cross-lane
+//                         step is 16 in-register values plus one cross-lane
 //                         exchange with the other half-wave)
 //   O^T += V^T P^T       (A = V^T from LDS, B = P^T straight from the S^T
 //                         accumulators rounded to bf16; V^T's key order in LDS
@@ -21,7 +21,10 @@
 // The causal mask is applied only on the diagonal block (the last entry of
 // every list); a partial last block is zero-padded.  Workgroups are ordered
 // longest list first, and the query heads of one KV head are mapped to the same
-// XCD (workgroup id modulo 8) so their shared K/V blocks meet in one L2.
+// XCD (workgroup id modulo 8) so their shared K/V blocks meet in one L2.  For
+// B = 128 the register budget is capped so three waves share each SIMD (the
+// short 32-key steps keep the score and staging registers small); the extra
+// wave hides more of the softmax and load latency behind other waves' MFMAs.
 //
 // fp32 path: a plain kernel, one thread per query row, key-by-key online
 // softmax with K/V tiles staged in LDS; it exists for tight-tolerance checks.
@@ -89,7 +92,7 @@ template <int D, int BLK>
 struct PrefillTile {
   static constexpr int NW = BLK / 32;               // waves (32 query rows each)
   static constexpr int NT = NW * 64;
-  static constexpr int KT = (BLK == 128) ? 64 : 32; // keys per pipeline step
+  static constexpr int KT = 32;                     // keys per pipeline step
   static constexpr int NSUB = BLK / KT;             // steps per selected block
   static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
   static constexpr int VCH = KT / 8;                // 16-byte chunks per V^T row of a step
@@ -204,7 +207,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 128 ? 3 : 2)))
 void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                               const uint16_t* __restrict__ vt,
                               const int32_t* __restrict__ cu_seqlens,
@@ -215,7 +218,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
                               float* __restrict__ lse) {
   using TL = PrefillTile<D, BLK>;
   constexpr int NT = TL::NT, KT = TL::KT;
-  static_assert(TL::NSUB == 2, "two pipeline steps per block");
+  static_assert(TL::NSUB % 2 == 0, "an even number of pipeline steps per block");
   __shared__ __attribute__((aligned(16))) char Ks[2][TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs[2][TL::TILE];
 
@@ -316,7 +319,9 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int nb = idx ? cnt[(int64_t)h * total_blocks + gb] : i + 1;
   const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
 
-  // Step 2nn uses LDS buffer 0 (first half of block nn), step 2nn + 1 buffer 1.
+  // Step sub of a block uses LDS buffer sub % 2; while it computes, the next
+  // step (the block's next sub-step, or the first of the next block) is
+  // loaded into registers, then stored into the other buffer.
   int j = lst ? lst[0] : 0;
   load_step(j, 0);
   store_step(0);
@@ -324,14 +329,17 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   for (int nn = 0; nn < nb; ++nn) {
     const bool has_next = nn + 1 < nb;
     const int j_next = has_next ? (lst ? lst[nn + 1] : nn + 1) : j;
-    load_step(j, 1);
-    attn_step<D, BLK>(j == i, Ks[0], Vs[0], 0, qf, k_rd, v_rd, o, m_run, l_run, scale_log2, qi, hl);
-    store_step(1);
-    __syncthreads();
-    if (has_next) load_step(j_next, 0);
-    attn_step<D, BLK>(j == i, Ks[1], Vs[1], KT, qf, k_rd, v_rd, o, m_run, l_run, scale_log2, qi, hl);
-    if (has_next) store_step(0);
-    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < TL::NSUB; ++sub) {
+      const int buf = sub & 1;
+      const bool last_sub = sub + 1 == TL::NSUB;
+      if (!last_sub) load_step(j, sub + 1);
+      else if (has_next) load_step(j_next, 0);
+      attn_step<D, BLK>(j == i, Ks[buf], Vs[buf], sub * KT, qf, k_rd, v_rd, o, m_run, l_run,
+                        scale_log2, qi, hl);
+      if (!last_sub || has_next) store_step(buf ^ 1);
+      __syncthreads();
+    }
     j = j_next;
   }
 
