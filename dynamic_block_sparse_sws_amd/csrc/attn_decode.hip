@@ -2,21 +2,23 @@
 // Attend", section 5: the same block selection for every decode step; section
 // 8.3: decode is bound by reading the KV cache).
 //
-// Split-KV over the union list of each (sequence, KV head): every workgroup
-// takes a chunk of 1024 key tokens (1024/B union blocks) and computes, for all
-// query heads of the group that kept each block, the partial softmax state
-// (max, sum, weighted V sum).  K rows are read once, as 16-byte vectors, and
-// dotted with every kept head's query; V rows are read once and accumulated for
-// every kept head.  A second kernel merges the partial states of the chunks
-// with the usual log-sum-exp rescaling.
+// Split-KV over the union lists of all (sequence, KV head) pairs at once: a
+// plan kernel numbers the blocks to read across the pairs and cuts them into
+// equal ranges, one per workgroup; each workgroup computes, for all query
+// heads of the group that kept each block, the partial softmax state (max,
+// sum, weighted V sum) of every pair its range touches.  K rows are read once,
+// as 16-byte vectors, and dotted with every kept head's query; V rows are read
+// once and accumulated for every kept head.  A combine kernel merges the
+// partial states of each pair with the usual log-sum-exp rescaling.
 #include "sws_common.h"
+
+#include <algorithm>
 
 namespace sws {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kSplitTokens = 1024;
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
 
@@ -99,22 +101,163 @@ __device__ __forceinline__ float exp2_or_zero(float x) {
   return x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x);
 }
 
-// One split: the workgroup's chunk of the union list is cut into batches of
-// TPB tokens (a batch never straddles a block); wave w takes batches w, w + 4,
-// ...  Within a batch a lane holds UNR token rows (TPL lanes per row, 8
-// features per lane), all K and V loads of the batch are issued before any is
-// used, and each row group of the wave keeps its own online-softmax state
-// (max, sum, weighted V sum) for up to four query heads at a time.  The row
-// groups are merged with cross-lane exchanges, the waves through LDS, and the
-// split's state is written for the combine kernel.
+// ---------------------------------------------------------------------------
+// Work plan.  The blocks to read, over all (sequence, KV head) pairs taken in
+// order, are numbered 0 .. W-1 and cut into NWG equal ranges, one per
+// workgroup, so every workgroup streams the same number of blocks whatever
+// the union sizes are, and there is no tail of half-empty chunks.  A range
+// that crosses pair boundaries leaves one partial softmax state ("record")
+// per pair it touches; the records of a pair are contiguous.
+// ---------------------------------------------------------------------------
+constexpr int kDecMaxWG = 2048;       // split workgroups at most (sizes the workspace)
+constexpr int kDecMaxPairs = 8192;    // sequences x KV heads at most
+constexpr int kPlanThreads = 1024;
+
+// floor(x / y) for 0 <= x < 2^53, 0 < y < 2^31, through one fp64 division
+// (exact here: a quotient below an integer k is at least 1/y < 2^-31 away
+// from it, far more than the rounding error of k * 2^-53).
+__device__ __forceinline__ int64_t floor_div(int64_t x, int64_t y) {
+  return (int64_t)floor((double)x / (double)y);
+}
+
+// first block of workgroup w's range, and the workgroup whose range holds block A
+__device__ __forceinline__ int64_t range_lo(int w, int64_t W, int nwg) {
+  return floor_div((int64_t)w * W, nwg);
+}
+__device__ __forceinline__ int wg_of_block(int64_t A, int64_t W, int nwg) {
+  return (int)floor_div((A + 1) * nwg - 1, W);
+}
+
+struct DecPlan {
+  int32_t* nwg;      // [1] workgroups with work: min(launched, W), so no range is empty
+  int32_t* pre;      // [P + 1] first block of each pair (pre[P] = W)
+  int32_t* rec;      // [P + 1] first record of each pair
+  int32_t* wfirst;   // [NWG] first pair of each workgroup's range
+};
+
+__device__ __forceinline__ DecPlan plan_of(void* ws, int P) {
+  int32_t* b = static_cast<int32_t*>(ws);
+  return {b, b + 1, b + 1 + (P + 1), b + 1 + 2 * (P + 1)};
+}
+
+// Exclusive prefix sum over the workgroup of one int per thread (wave scans
+// with lane shuffles, then the wave totals); also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const int t = wtot[w];
+    base += w < wave ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
+template <int BLK>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
+    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ ucnt, int n_seqs, int hkv,
+    int nwg, void* ws) {
+  constexpr int PER = kDecMaxPairs / kPlanThreads;
+  __shared__ int32_t spre[kDecMaxPairs + 1];
+  __shared__ int wtot[kPlanThreads / 64];
+  const int P = n_seqs * hkv;
+  const DecPlan pl = plan_of(ws, P);
+  const int t = threadIdx.x;
+  // thread t owns pairs t * PER .. t * PER + PER - 1
+  // (unconditional loads of clamped indices, so they are all in flight at once)
+  int cnt[PER];
+  if (ucnt) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) cnt[u] = ucnt[min(t * PER + u, P - 1)];
+  } else {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) cnt[u] = (ctx_len[min(t * PER + u, P - 1) / hkv] + BLK - 1) / BLK;
+  }
+  int run = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    cnt[u] = t * PER + u < P ? cnt[u] : 0;
+    run += cnt[u];
+  }
+  int total;
+  int acc = block_exclusive_scan(run, wtot, total);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = t * PER + u;
+    if (p < P) spre[p] = acc;
+    acc += cnt[u];
+  }
+  if (t == 0) spre[P] = total;
+  __syncthreads();
+  const int64_t W = total;
+  // with fewer blocks than workgroups, only the first W get a (one-block) range
+  nwg = (int)std::min<int64_t>(nwg, std::max<int64_t>(W, 1));
+  if (t == 0) *pl.nwg = nwg;
+  // records per pair: the workgroups holding its first and last block
+  run = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = t * PER + u;
+    int r = 0;
+    if (p < P && cnt[u] > 0)
+      r = wg_of_block(spre[p] + cnt[u] - 1, W, nwg) - wg_of_block(spre[p], W, nwg) + 1;
+    cnt[u] = r;
+    run += r;
+  }
+  acc = block_exclusive_scan(run, wtot, total);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = t * PER + u;
+    if (p < P) {
+      pl.pre[p] = spre[p];
+      pl.rec[p] = acc;
+    }
+    acc += cnt[u];
+  }
+  if (t == 0) {
+    pl.pre[P] = spre[P];
+    pl.rec[P] = total;
+  }
+  // first pair of each workgroup: the last pair starting at or before its
+  // range (pairs without blocks are skipped by the split kernel)
+  for (int w = t; w < nwg; w += kPlanThreads) {
+    const int64_t lo = range_lo(w, W, nwg);
+    int l = 0, h = P - 1;
+    while (l < h) {
+      const int m = (l + h + 1) >> 1;
+      if (spre[m] <= lo) l = m;
+      else h = m - 1;
+    }
+    pl.wfirst[w] = l;
+  }
+}
+
+// Partial state of blocks [a, b) of pair p's list for every query head of the
+// group, written as record `r`.  The range is cut into batches of TPB tokens
+// (a batch never straddles a block); wave w takes batches w, w + 4, ...  A
+// lane holds UNR token rows of a batch (TPL lanes per row, 8 features per
+// lane); all K and V loads of the batch are issued before any is used, and
+// each row group of the wave keeps its own online-softmax state (max, sum,
+// weighted V sum) for up to four query heads at a time.  Row groups merge
+// through lane exchanges, waves through LDS.
 template <typename T, int D, int BLK, int GMAX, int UNR>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+__device__ __forceinline__ void decode_range(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, int max_ctx, int hq, int hkv,
-    const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucnt,
-    const uint32_t* __restrict__ umask, int uwidth, int max_splits, float scale_log2,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
-  constexpr int BPS = kSplitTokens / BLK;      // blocks per split
+    const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth, int p,
+    int a, int b, int r, float scale_log2, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc) {
   constexpr int TPL = D / 8;                   // lanes per token row
   constexpr int RPW = 64 / TPL;                // token rows per wave-wide load
   constexpr int TPB = RPW * UNR;               // tokens per wave batch
@@ -124,15 +267,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ float wm[NWV][HC], wl[NWV][HC];
   __shared__ float wacc[NWV][HC][D];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int seq = blockIdx.z;
+  const int seq = p / hkv;
+  const int g = p % hkv;
   const int G = hq / hkv;
   const int ctx = ctx_len[seq];
-  const int nblk = uidx ? ucnt[seq * hkv + g] : (ctx + BLK - 1) / BLK;
-  const int e0 = split * BPS;
-  if (e0 >= nblk) return;
-  const int ntok = (min(nblk, e0 + BPS) - e0) * BLK;
+  const int ntok = (b - a) * BLK;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ch = lane % TPL;           // feature chunk (8 features)
@@ -140,8 +279,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int64_t rstride = (int64_t)hkv * D;
   const T* kb = kc + ((int64_t)seq * max_ctx) * rstride + (int64_t)g * D + ch * 8;
   const T* vb = vc + ((int64_t)seq * max_ctx) * rstride + (int64_t)g * D + ch * 8;
-  const int32_t* ul = uidx ? uidx + ((int64_t)seq * hkv + g) * uwidth : nullptr;
-  const uint32_t* um = umask ? umask + ((int64_t)seq * hkv + g) * uwidth : nullptr;
+  const int32_t* ul = uidx ? uidx + (int64_t)p * uwidth : nullptr;
+  const uint32_t* um = umask ? umask + (int64_t)p * uwidth : nullptr;
 
   for (int h0 = 0; h0 < G; h0 += HC) {
     QVec<T> qv[HC];
@@ -156,16 +295,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       l[hh] = 0.f;
     }
     for (int tb = wave * TPB; tb < ntok; tb += NWV * TPB) {
-      const int e = e0 + tb / BLK;
+      const int e = a + tb / BLK;
       const int blk = ul ? ul[e] : e;
       const uint32_t mk = um ? um[e] : 0xffffffffu;
       const int r0 = blk * BLK + tb % BLK + slot;      // this lane's first cache row
       Row8<T> kr[UNR], vr[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int64_t r = min(r0 + u * RPW, ctx - 1);  // rows past ctx are masked below
-        kr[u].load(kb + r * rstride);
-        vr[u].load(vb + r * rstride);
+        const int64_t row = min(r0 + u * RPW, ctx - 1);  // rows past ctx are masked below
+        kr[u].load(kb + row * rstride);
+        vr[u].load(vb + row * rstride);
       }
       float sc[UNR][HC];
 #pragma unroll
@@ -195,10 +334,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         vr[u].get(vf);
 #pragma unroll
         for (int hh = 0; hh < HC; ++hh) {
-          const float p = exp2_or_zero(sc[u][hh] == -INFINITY ? -INFINITY : sc[u][hh] - m[hh]);
-          l[hh] += p;
+          const float pw = exp2_or_zero(sc[u][hh] == -INFINITY ? -INFINITY : sc[u][hh] - m[hh]);
+          l[hh] += pw;
 #pragma unroll
-          for (int x = 0; x < 8; ++x) acc[hh][x] += p * vf[x];
+          for (int x = 0; x < 8; ++x) acc[hh][x] += pw * vf[x];
         }
       }
     }
@@ -233,7 +372,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       }
     }
     __syncthreads();
-    // merge the waves and write the split state of heads h0 .. h0 + HC - 1
+    // merge the waves and write record r for heads h0 .. h0 + HC - 1
     for (int e = tid; e < HC * D; e += kDecThreads) {
       const int hh = e / D, dd = e % D;
       if (h0 + hh >= G) continue;
@@ -247,7 +386,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         L += f * wl[w][hh];
         A += f * wacc[w][hh][dd];
       }
-      const int64_t row = ((int64_t)seq * hq + g * G + h0 + hh) * max_splits + split;
+      const int64_t row = (int64_t)r * G + h0 + hh;
       ws_acc[row * D + dd] = A;
       if (dd == 0) {
         ws_ml[row * 2 + 0] = M;
@@ -258,34 +397,60 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
-// Merge of the split states of one (sequence, query head): the weights
-// exp2(m_s - max m) go to LDS once, then each thread sums one feature over the
-// splits with independent loads.
-constexpr int kMaxSplits = 1024;
+// Split kernel: workgroup w reads blocks [w W / NWG, (w + 1) W / NWG) of the
+// concatenated pair lists, one record per pair the range touches.
+template <typename T, int D, int BLK, int GMAX, int UNR>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
+    const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth,
+    float scale_log2, void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+  const int P = n_seqs * hkv;
+  const DecPlan pl = plan_of(ws, P);
+  const int nwg = *pl.nwg;
+  const int w = blockIdx.x;
+  if (w >= nwg) return;
+  const int64_t W = pl.pre[P];
+  const int64_t lo = range_lo(w, W, nwg);
+  const int64_t hi = range_lo(w + 1, W, nwg);
+  if (lo >= hi) return;
+  for (int p = pl.wfirst[w]; p < P; ++p) {
+    const int A = pl.pre[p];
+    if (A >= hi) break;
+    const int Bn = pl.pre[p + 1];
+    const int a = (int)(max(lo, (int64_t)A) - A);
+    const int b = (int)(min(hi, (int64_t)Bn) - A);
+    if (a >= b) continue;
+    const int r = pl.rec[p] + (w - wg_of_block(A, W, nwg));
+    decode_range<T, D, BLK, GMAX, UNR>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask, uwidth,
+                                       p, a, b, r, scale_log2, ws_ml, ws_acc);
+  }
+}
 
-template <typename T, int D, int BLK>
+// Merge of the records of one (sequence, query head): the weights
+// exp2(m_r - max m) go to LDS once, then each thread sums one feature over the
+// records with independent loads.
+template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(
-    const int32_t* __restrict__ ctx_len, int hq, int hkv, const int32_t* __restrict__ uidx,
-    const int32_t* __restrict__ ucnt, int max_splits, const float* __restrict__ ws_ml,
+    int n_seqs, int hq, int hkv, const void* ws, const float* __restrict__ ws_ml,
     const float* __restrict__ ws_acc, T* __restrict__ out, float* __restrict__ lse) {
-  constexpr int BPS = kSplitTokens / BLK;
   constexpr int NW = D / 64;
-  __shared__ float wgt[kMaxSplits];
+  __shared__ float wgt[kDecMaxWG + 1];
   __shared__ float red[NW];
   __shared__ float s_M, s_L;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int G = hq / hkv;
-  const int g = h / G;
-  const int ctx = ctx_len[seq];
-  const int nblk = uidx ? ucnt[seq * hkv + g] : (ctx + BLK - 1) / BLK;
-  const int ns = (nblk + BPS - 1) / BPS;
-  const int64_t row0 = ((int64_t)seq * hq + h) * max_splits;
+  const int hh = h % G;
+  const int p = seq * hkv + h / G;
+  const DecPlan pl = plan_of(const_cast<void*>(ws), n_seqs * hkv);
+  const int r0 = pl.rec[p];
+  const int ns = pl.rec[p + 1] - r0;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   float m = -INFINITY;
   for (int si = t; si < ns; si += D) {
-    const float v = ws_ml[(row0 + si) * 2];
+    const float v = ws_ml[((int64_t)(r0 + si) * G + hh) * 2];
     wgt[si] = v;
     m = fmaxf(m, v);
   }
@@ -305,7 +470,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
     const float mv = wgt[si];
     const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
     wgt[si] = f;
-    lsum += f * ws_ml[(row0 + si) * 2 + 1];
+    lsum += f * ws_ml[((int64_t)(r0 + si) * G + hh) * 2 + 1];
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
@@ -318,15 +483,37 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
     s_L = L;
   }
   __syncthreads();
-  float a = 0.f;
+  float acc = 0.f;
 #pragma unroll 8
-  for (int si = 0; si < ns; ++si) a += wgt[si] * ws_acc[(row0 + si) * D + t];
+  for (int si = 0; si < ns; ++si) acc += wgt[si] * ws_acc[((int64_t)(r0 + si) * G + hh) * D + t];
   const float L = s_L;
-  const float o = a / L;
+  const float o = L > 0.f ? acc / L : 0.f;
   T* op = out + ((int64_t)seq * hq + h) * D + t;
   if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t*>(op) = (uint16_t)f32_to_bf16_bits(o);
   else *op = o;
   if (lse && t == 0) lse[(int64_t)seq * hq + h] = (M + log2f(L)) * kLn2;
+}
+
+// Workspace: plan (int32: nwg, pre, rec [P + 1] each, wfirst [kDecMaxWG]), then the
+// records' (max, sum) and weighted V sums, (P + kDecMaxWG) records of G heads.
+size_t plan_bytes(int P) {
+  return (((size_t)1 + 2 * (P + 1) + kDecMaxWG) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+// Split workgroups per launch: three resident per CU (the kernel's occupancy),
+// two rounds.
+int split_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = std::min(kDecMaxWG, cus * 3 * 2);
+  }
+  return cached[dev];
 }
 
 template <typename T, int D, int BLK, int GMAX>
@@ -335,20 +522,24 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* uidx, const int32_t* ucnt, const uint32_t* umask,
                       int uwidth, float scale, void* out, float* lse, void* ws,
                       hipStream_t st) {
-  constexpr int BPS = kSplitTokens / BLK;
-  const int max_splits = (uwidth + BPS - 1) / BPS;
-  float* ws_ml = static_cast<float*>(ws);
-  float* ws_acc = ws_ml + (size_t)n_seqs * hq * max_splits * 2;
-  dim3 grid(max_splits, hkv, n_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, kDecUnroll>), grid, dim3(kDecThreads), 0, st,
-                     static_cast<const T*>(q), static_cast<const T*>(k_cache),
-                     static_cast<const T*>(v_cache), ctx_len, max_ctx, hq, hkv, uidx, ucnt,
-                     umask, uwidth, max_splits, scale * kLog2e, ws_ml, ws_acc);
+  const int P = n_seqs * hkv;
+  const int G = hq / hkv;
+  const int nwg = split_workgroups();
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan_bytes(P));
+  float* ws_acc = ws_ml + (size_t)(P + kDecMaxWG) * G * 2;
+  hipLaunchKernelGGL((decode_plan_kernel<BLK>), dim3(1), dim3(kPlanThreads), 0, st, ctx_len,
+                     uidx ? ucnt : nullptr, n_seqs, hkv, nwg, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, BLK>), dim3(hq, n_seqs), dim3(D), 0, st,
-                     ctx_len, hq, hkv, uidx, ucnt, max_splits, ws_ml, ws_acc,
-                     static_cast<T*>(out), lse);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, kDecUnroll>), dim3(nwg),
+                     dim3(kDecThreads), 0, st, static_cast<const T*>(q),
+                     static_cast<const T*>(k_cache), static_cast<const T*>(v_cache), ctx_len,
+                     max_ctx, n_seqs, hq, hkv, uidx, umask, uwidth, scale * kLog2e, ws, ws_ml,
+                     ws_acc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(hq, n_seqs), dim3(D), 0, st, n_seqs,
+                     hq, hkv, ws, ws_ml, ws_acc, static_cast<T*>(out), lse);
   return hipGetLastError();
 }
 
@@ -374,10 +565,11 @@ hipError_t pick_g(const void* q, const void* k_cache, const void* v_cache,
 }  // namespace
 
 size_t decode_workspace_bytes(int n_seqs, int hq, int hkv, int d, int B, int union_width) {
-  (void)hkv;
-  const int bps = kSplitTokens / B;
-  const size_t max_splits = (size_t)((union_width + bps - 1) / bps);
-  return (size_t)n_seqs * hq * max_splits * (size_t)(d + 2) * sizeof(float);
+  (void)B;
+  (void)union_width;
+  const int P = n_seqs * hkv;
+  const size_t G = (size_t)(hq / hkv);
+  return plan_bytes(P) + (size_t)(P + kDecMaxWG) * G * (size_t)(d + 2) * sizeof(float);
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_cache,

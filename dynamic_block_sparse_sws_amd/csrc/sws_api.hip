@@ -251,7 +251,8 @@ size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, 
 
 size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
                                  int32_t union_width) {
-  if (n_seqs < 0 || hq < 1 || (d != 64 && d != 128) || (B != 64 && B != 128) || union_width < 0)
+  if (n_seqs < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || (d != 64 && d != 128) ||
+      (B != 64 && B != 128) || union_width < 0)
     return 0;
   return sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, union_width);
 }
@@ -280,9 +281,11 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d max_ctx=%d", fn, n_seqs, max_ctx);
   const int uw = union_idx ? union_width : (max_ctx + B - 1) / B;
   if (union_idx && union_width < 1) return fail(SWS_ERR_SHAPE, "%s: union_width=%d", fn, union_width);
-  if ((int64_t)uw * B > 1048576)
-    return fail(SWS_ERR_UNSUPPORTED, "%s: %d blocks of %d tokens exceed 1024 chunks of 1024", fn,
-                uw, B);
+  if ((int64_t)n_seqs * hkv > 8192)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: n_seqs * hkv = %lld > 8192", fn,
+                (long long)n_seqs * hkv);
+  if ((int64_t)n_seqs * hkv * uw > 0x7fffffffLL)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs * hkv * union_width exceeds 2^31", fn);
   if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(SWS_ERR_SHAPE, "%s: q/k_cache/v_cache must be 16-byte aligned", fn);

@@ -232,9 +232,10 @@ size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, 
  *   (union_idx NULL: dense, every block of the context for every head)
  *   out     [n_seqs][hq][d] (dtype of q); lse optional [n_seqs][hq] fp32
  *   ws      workspace of at least sws_decode_workspace_size(...) bytes
- *   d in {64, 128}; B in {64, 128}; hq / hkv <= 16; the list is cut into
- *   chunks of 1024 tokens and at most 1024 chunks are supported
- *   (union_width * B <= 1048576), else SWS_ERR_UNSUPPORTED
+ *   d in {64, 128}; B in {64, 128}; hq / hkv <= 16; n_seqs * hkv <= 8192
+ *   (else SWS_ERR_UNSUPPORTED).  The blocks to read over all pairs are split
+ *   evenly across the workgroups, so the cost follows the total number of
+ *   blocks, not the largest list.
  */
 int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
                            const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
@@ -243,8 +244,8 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            int32_t union_width, float scale, void* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream);
 
-/* Workspace bytes sws_sparse_attn_decode needs for these sizes; for the dense
- * form (union_idx NULL) pass union_width = ceil(max_ctx / B). */
+/* Workspace bytes sws_sparse_attn_decode needs for these sizes (a work plan
+ * and per-range partial softmax states; union_width does not change it). */
 size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
                                  int32_t union_width);
 
