@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time rho = 10, 30, 100")
+    ap.add_argument("--diag", action="store_true",
+                    help="parameter sweep (s, k, B, rho) and selection-quality diagnostics")
     ap.add_argument("--seqlen", type=int, default=None, help="override n (testing only)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
@@ -312,6 +314,158 @@ def bench_decode(args, torch, sws, gen, timer_cls):
     return res
 
 
+def diagnostics(args, torch, sws, gen, ctx):
+    """Sweeps over the walk degree s, the sketch dimension k, the block size B
+    and the density rho on one 128K layer (walk started from the identity), with
+    the time split per stage, plus selection-quality diagnostics on the planted
+    data:
+    * agreement (Jaccard) of each configuration's selected sets with the
+      selection of the exact block scores (k = d: the sketch is then exact, so
+      the reference walks tril(qbar kbar^T)/sqrt(d) itself, computed here with
+      plain torch fp64 on sampled heads);
+    * attention mass captured by the selected blocks, exp(lse_sparse -
+      lse_dense) per query row, from the kernels' log-sum-exp outputs;
+    * recall of the planted multi-hop chains i -> j -> m: how often the far
+      block m (and the near block j) is among block i's selection, for the
+      multi-hop walk (s = 8) against a one-hop walk (s = 1)."""
+    from gen import synth
+    cfg, geo = ctx["cfg"], ctx["geo"]
+    q, k, v = ctx["layers"][0]
+    layer_id = 2                          # ctx layers are generator layers 2, 3, ...
+    hq, hkv, d, B = cfg.hq, cfg.hkv, cfg.d, cfg.B
+    grp = hq // hkv
+    n = geo.total_tokens
+    dev = q.device
+
+    def tables(kk):
+        sg, cl = gen.hadamard_tables(d, kk)
+        return torch.from_numpy(sg).to(dev), torch.from_numpy(cl).to(dev)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def run(geo_, kk, s, rho, attn=True, lse=None):
+        sd, cd = tables(kk)
+        R = torch.empty(geo_.walk_numel(hq), dtype=torch.float32, device=dev)
+        ts = [ev()]
+        q_sk = sws.sketch(q, geo_, kk, sd, cd)
+        k_sk = sws.sketch(k, geo_, kk, sd, cd)
+        ts.append(ev())
+        sws.walk_update(q_sk, k_sk, geo_, s, None, R_out=R)
+        ts.append(ev())
+        idx, cnt = sws.select_topk(R, hq, geo_, rho)
+        ts.append(ev())
+        if attn:
+            ws = torch.empty(sws.prefill_workspace_size(sws.BF16, geo_.total_blocks, hkv, d,
+                                                        geo_.B), dtype=torch.uint8, device=dev)
+            sws.sparse_attn_prefill(q, k, v, geo_, idx, cnt, lse=lse, ws=ws)
+            ts.append(ev())
+        torch.cuda.synchronize()
+        names = ("sketch", "walk", "select", "attention")
+        t = {nm: ts[i].elapsed_time(ts[i + 1]) * 1e3 for i, nm in enumerate(names[:len(ts) - 1])}
+        return idx, cnt, t
+
+    # exact-score reference selection on sampled heads (torch fp64)
+    b = geo.max_blocks
+    tau = (20 * b) // 100
+    ref_heads = [0, 13, 26]
+
+    def block_means(x):
+        pad = b * B - n
+        xx = torch.nn.functional.pad(x.double(), (0, 0, 0, pad)).view(b, B, d).sum(1)
+        cnt_ = torch.full((b, 1), float(B), dtype=torch.float64, device=dev)
+        cnt_[-1, 0] = n - (b - 1) * B
+        return xx / cnt_
+
+    def exact_sets(h, s=8, rho=20):
+        g = h // grp
+        M = torch.tril(block_means(q[:, h]) @ block_means(k[:, g]).T) / math.sqrt(d)
+        X = torch.eye(b, dtype=torch.float64, device=dev)
+        for _ in range(s):
+            X = X @ M
+            X = X / X.abs().amax(dim=1, keepdim=True).clamp_min(1e-300)
+        t_ = (rho * b) // 100
+        sets = []
+        Xc = X.cpu().numpy()
+        for i in range(b):
+            if i <= t_:
+                sets.append(set(range(i + 1)))
+                continue
+            row = Xc[i, :i]
+            order = np.lexsort((np.arange(i), -row))[:t_]
+            sets.append(set(order.tolist()) | {i})
+        return sets
+
+    ref = {h: exact_sets(h) for h in ref_heads}
+
+    def jaccard(idx, cnt, heads=ref_heads):
+        idx_h = idx.cpu().numpy()
+        cnt_h = cnt.cpu().numpy()
+        js = []
+        for h in heads:
+            for i in range(tau + 1, b):
+                got = set(idx_h[h, i, :cnt_h[h, i]].tolist())
+                want = ref[h][i]
+                js.append(len(got & want) / len(got | want))
+        return float(np.mean(js))
+
+    sweep = []
+    for (kk, s, rho) in [(32, 1, 20), (32, 2, 20), (32, 4, 20), (32, 8, 20), (32, 16, 20),
+                         (16, 8, 20), (64, 8, 20), (32, 8, 10), (32, 8, 30)]:
+        idx, cnt, t = run(geo, kk, s, rho)
+        rec = {"B": B, "k": kk, "s": s, "rho": rho, "stage_us": t,
+               "executed_block_pairs": int(cnt.long().sum()),
+               "dense_equiv_tflops": 4.0 * d * hq * n * (n + 1) / 2.0 / (sum(t.values()) * 1e-6) / 1e12}
+        if rho == 20:
+            rec["jaccard_vs_exact_scores"] = jaccard(idx, cnt)
+        sweep.append(rec)
+        print(f"[diag] sweep B={B} k={kk} s={s} rho={rho}: {sum(t.values()) / 1e3:.2f} ms",
+              file=sys.stderr, flush=True)
+    geo64 = sws.Geometry([n], 64)
+    idx, cnt, t = run(geo64, 32, 8, 20)
+    sweep.append({"B": 64, "k": 32, "s": 8, "rho": 20, "stage_us": t,
+                  "executed_block_pairs": int(cnt.long().sum()),
+                  "dense_equiv_tflops": 4.0 * d * hq * n * (n + 1) / 2.0 / (sum(t.values()) * 1e-6) / 1e12})
+    del idx, cnt
+
+    # attention mass captured by the selection
+    lse_d = torch.empty((hq, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(sws.prefill_workspace_size(sws.BF16, geo.total_blocks, hkv, d, B),
+                     dtype=torch.uint8, device=dev)
+    sws.sparse_attn_prefill(q, k, v, geo, None, None, lse=lse_d, ws=ws)
+    captured = {}
+    for rho in (10, 20, 30):
+        lse_s = torch.empty_like(lse_d)
+        run(geo, 32, 8, rho, lse=lse_s)
+        frac = torch.exp((lse_s - lse_d).double())
+        captured[str(rho)] = {"mean": float(frac.mean()), "p5": float(frac.quantile(0.05)),
+                              "min": float(frac.min())}
+
+    # planted chain recall: multi-hop walk against a one-hop walk
+    recall = {}
+    for s in (1, 8):
+        idx, cnt, _ = run(geo, 32, s, 20, attn=False)
+        idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+        hit_j = hit_m = tot = 0
+        for g in range(hkv):
+            z = synth._band(cfg.cfg_id, 0, g, b, d)
+            m_hat = synth._unit(z.mean(axis=0))
+            for trip, _, _ in synth.chain_draws(cfg, layer_id, 0, g, b, m_hat):
+                for (i, j, m) in trip.tolist():
+                    for h in range(g * grp, (g + 1) * grp):
+                        sel = set(idx_h[h, i, :cnt_h[h, i]].tolist())
+                        hit_j += j in sel
+                        hit_m += m in sel
+                        tot += 1
+        recall[f"s={s}"] = {"near_block_j": hit_j / tot, "far_block_m": hit_m / tot,
+                            "chains_x_heads": tot}
+    return {"layer": "128K prefill layer (generator layer 2), walk from the identity",
+            "sweep": sweep, "captured_attention_mass": captured, "planted_chain_recall": recall,
+            "exact_reference_heads": ref_heads}
+
+
 def cpu_baseline(ctx, torch, budget_s=12.0):
     """The oracle (fp64 NumPy) on a bounded sample of one sparse 128K layer:
     the query heads of KV head 0 sketched, walked from the identity and
@@ -402,6 +556,9 @@ def main():
     print(f"[bench] prefill: {pre['ms_per_layer']:.3f} ms/layer, "
           f"{pre['dense_equiv_tflops']:.1f} dense-equiv TFLOP/s, attention "
           f"{pre['attn_exec_tflops']:.1f} TFLOP/s executed", file=sys.stderr, flush=True)
+    diag = None
+    if args.diag:
+        diag = diagnostics(args, torch, sws, gen, ctx)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(ctx, torch)
@@ -437,6 +594,8 @@ def main():
         "prefill": pre,
         "decode": dec,
     }
+    if diag:
+        line["diagnostics"] = diag
     if dec:
         line["decode_us_per_step"] = round(dec["us_per_step"], 2)
     print(json.dumps(line))

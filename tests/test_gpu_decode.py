@@ -196,3 +196,11 @@ def test_decode_matches_prefix_prefill_definition():
                     assert gap <= 1e-4 * np.abs(row).max(), (s, l, h, diff, gap)
                 else:
                     assert np.abs(recs[l]["out"][s, h] - want["o"]).max() <= TOL_ATTN_BF16
+
+
+def test_decode_other_walk_degree_and_sketch_dim():
+    """Decode chain with s = 2 hops and k = 64 sketch components."""
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=4, hkv=2, k=64, s=2)
+    _print("decode s=2 k=64")
+    w, _, _ = run_decode_case(cfg, (300, 129), 6, 2, 25, 0, {0, 2, 5})
+    _print("worst", w)

@@ -104,3 +104,16 @@ def test_error_codes_from_the_library():
     with pytest.raises(sws.SwsError) as ei:
         sws.select_topk(torch.zeros(4 * 16, device="cuda"), 4, geo, 100, width=2)
     assert ei.value.code == 2
+
+
+@pytest.mark.parametrize("s,kdim,B", [(1, 32, 64), (2, 32, 128), (4, 16, 64), (16, 32, 128),
+                                      (8, 64, 64)])
+def test_walk_degree_and_sketch_dim(s, kdim, B):
+    """The parameter range the sweeps use (walk degree s, sketch dimension k,
+    block size B): every stage of a two-layer ragged bf16 stack against the
+    oracle, so the walk carried across layers is checked at each s."""
+    cfg = gen.CONFIGS["C2"].with_(d=128, B=B, hq=4, hkv=2, k=kdim, s=s)
+    _print("walk sweep", s, kdim, B)
+    run = PrefillRun(cfg, (5 * B + 17, 3 * B), 2, 20, n_dense=0)
+    w = check_prefill_run(run)
+    _print("worst", w)
