@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "SwsError", "lib", "F32", "BF16", "Geometry", "geometry", "walk_state_numel",
+    "SwsError", "lib", "F32", "BF16", "SELECT_DENSE", "SELECT_ROW_TAU", "SELECT_GROUP", "Geometry", "geometry", "walk_state_numel",
     "sketch", "sketch_append", "walk_update", "walk_update_row", "select_topk",
     "select_topk_row", "sparse_attn_prefill", "sparse_attn_decode", "decode_workspace_size",
     "prefill_layer", "EXPORTED_SYMBOLS", "version",
@@ -25,6 +25,11 @@ __all__ = [
 F32 = 0
 BF16 = 1
 
+# selection flags (include/sws.h)
+SELECT_DENSE = 1
+SELECT_ROW_TAU = 2
+SELECT_GROUP = 4
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsws.so")
 
@@ -32,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "sws_version", "sws_status_string", "sws_last_error_detail", "sws_sketch",
     "sws_sketch_append", "sws_walk_update", "sws_walk_update_row", "sws_select_topk",
     "sws_select_topk_row", "sws_sparse_attn_prefill", "sws_sparse_attn_decode",
-    "sws_decode_workspace_size", "sws_prefill_workspace_size",
+    "sws_decode_workspace_size", "sws_prefill_workspace_size", "sws_select_topk_flags",
 )
 
 
@@ -62,6 +67,8 @@ _SIGS = {
     "sws_walk_update": ([_P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P], ctypes.c_int),
     "sws_walk_update_row": ([_P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P], ctypes.c_int),
     "sws_select_topk": ([_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], ctypes.c_int),
+    "sws_select_topk_flags": ([_P, _I, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
+                              ctypes.c_int),
     "sws_select_topk_row": ([_P, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P],
                             ctypes.c_int),
     "sws_sparse_attn_prefill": ([_P, _P, _P, ctypes.c_int, _P, _P, _I, _I, _I, _I, _I, _I, _I,
@@ -218,16 +225,27 @@ def select_width(rho: int, max_blocks: int, dense: bool = False) -> int:
 
 
 def select_topk(R: Optional[torch.Tensor], hq: int, geo: Geometry, rho: int, dense: bool = False,
-                width: Optional[int] = None, idx=None, cnt=None, stream=None):
+                width: Optional[int] = None, idx=None, cnt=None, stream=None,
+                row_tau: bool = False, group_hkv: Optional[int] = None):
+    """Top-tau lists per (query head, block).  row_tau / group_hkv select the
+    variants SELECT_ROW_TAU and SELECT_GROUP (one shared list per KV group of
+    hq / group_hkv heads)."""
     width = width or select_width(rho, geo.max_blocks, dense)
     dev = geo.cu_blocks.device
     if idx is None:
         idx = torch.empty((hq, geo.total_blocks, width), dtype=torch.int32, device=dev)
     if cnt is None:
         cnt = torch.empty((hq, geo.total_blocks), dtype=torch.int32, device=dev)
-    _check("sws_select_topk", lib().sws_select_topk(
-        _ptr(R), hq, _ptr(geo.cu_blocks), geo.n_seqs, geo.total_blocks, geo.max_blocks, rho,
-        int(dense), width, _ptr(idx), _ptr(cnt), _stream(stream)))
+    if not row_tau and group_hkv is None:
+        _check("sws_select_topk", lib().sws_select_topk(
+            _ptr(R), hq, _ptr(geo.cu_blocks), geo.n_seqs, geo.total_blocks, geo.max_blocks, rho,
+            int(dense), width, _ptr(idx), _ptr(cnt), _stream(stream)))
+        return idx, cnt
+    flags = ((SELECT_DENSE if dense else 0) | (SELECT_ROW_TAU if row_tau else 0)
+             | (SELECT_GROUP if group_hkv is not None else 0))
+    _check("sws_select_topk_flags", lib().sws_select_topk_flags(
+        _ptr(R), hq, group_hkv or hq, _ptr(geo.cu_blocks), geo.n_seqs, geo.total_blocks,
+        geo.max_blocks, rho, flags, width, _ptr(idx), _ptr(cnt), _stream(stream)))
     return idx, cnt
 
 
@@ -239,9 +257,10 @@ def union_width(rho: int, b_max: int, group: int, dense: bool = False) -> int:
 
 def select_topk_row(r: Optional[torch.Tensor], hq: int, hkv: int, cur_block: torch.Tensor,
                     b_max: int, rho: int, dense: bool = False, per_head: bool = False,
-                    out=None, stream=None):
+                    out=None, stream=None, group: bool = False):
     """Returns (union_idx, union_cnt, union_mask, idx, cnt); idx/cnt are None
-    unless per_head.  `out` may supply the five buffers."""
+    unless per_head.  `out` may supply the five buffers.  group selects the
+    SELECT_GROUP variant (one shared list per KV group)."""
     n_seqs = cur_block.shape[0]
     dev = cur_block.device
     uw = union_width(rho, b_max, hq // hkv, dense)
@@ -258,7 +277,8 @@ def select_topk_row(r: Optional[torch.Tensor], hq: int, hkv: int, cur_block: tor
         if idx is not None:
             w = idx.shape[2]
     _check("sws_select_topk_row", lib().sws_select_topk_row(
-        _ptr(r), hq, hkv, n_seqs, _ptr(cur_block), b_max, rho, int(dense), w, _ptr(idx),
+        _ptr(r), hq, hkv, n_seqs, _ptr(cur_block), b_max, rho,
+        (SELECT_DENSE if dense else 0) | (SELECT_GROUP if group else 0), w, _ptr(idx),
         _ptr(cnt), _ptr(uidx), _ptr(ucnt), _ptr(umask), uw, _stream(stream)))
     return uidx, ucnt, umask, idx, cnt
 

@@ -52,34 +52,49 @@ __device__ __forceinline__ void threshold(const uint32_t (&key)[E], int n, int t
   need_eq = tau - gt;
 }
 
+// flags: SWS_SELECT_DENSE keeps every block <= i; SWS_SELECT_ROW_TAU gives
+// row i the budget floor(rho (i + 1) / 100) instead of floor(rho b / 100);
+// SWS_SELECT_GROUP scores a row by the fp32 sum, in ascending head order, of
+// the rows of the GS query heads of a KV group, and writes the shared list to
+// each of them.  blockIdx.y is the query head, or the KV group with
+// SWS_SELECT_GROUP.
 template <int E>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ R, int hq,
                                                      const int32_t* __restrict__ cu_blocks,
                                                      int n_seqs, int total_blocks, int rho,
-                                                     int dense, int width,
+                                                     int flags, int GS, int width,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ cnt) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int h = blockIdx.y;
+  const int h0 = blockIdx.y * GS;
   const int seq = blockIdx.z;
   const int b0 = cu_blocks[seq];
   const int b = cu_blocks[seq + 1] - b0;
   if (i >= b) return;
   const int gb = b0 + i;
-  int32_t* out = idx + ((int64_t)h * total_blocks + gb) * width;
-  const int tau = (int)(((int64_t)rho * b) / 100);
-  if (dense || i <= tau) {
-    for (int m = lane; m <= i; m += 64) out[m] = m;
-    if (lane == 0) cnt[(int64_t)h * total_blocks + gb] = i + 1;
+  const int tau = (flags & SWS_SELECT_ROW_TAU) ? (int)(((int64_t)rho * (i + 1)) / 100)
+                                               : (int)(((int64_t)rho * b) / 100);
+  if ((flags & SWS_SELECT_DENSE) || i <= tau) {
+    for (int hh = 0; hh < GS; ++hh) {
+      int32_t* out = idx + ((int64_t)(h0 + hh) * total_blocks + gb) * width;
+      for (int m = lane; m <= i; m += 64) out[m] = m;
+      if (lane == 0) cnt[(int64_t)(h0 + hh) * total_blocks + gb] = i + 1;
+    }
     return;
   }
-  const float* row = R + walk_seq_offset(cu_blocks, seq, hq) + ((int64_t)h * b + i) * b;
+  const float* row = R + walk_seq_offset(cu_blocks, seq, hq) + ((int64_t)h0 * b + i) * b;
+  const int64_t hstride = (int64_t)b * b;
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int m = e * 64 + lane;
-    key[e] = (m < i) ? order_key(row[m]) : 0u;
+    float v = 0.f;
+    if (m < i) {
+      v = row[m];
+      for (int hh = 1; hh < GS; ++hh) v += row[hh * hstride + m];
+    }
+    key[e] = (m < i) ? order_key(v) : 0u;
   }
   uint32_t T;
   int need;
@@ -96,13 +111,17 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ R
       const bool sel = valid && (key[e] > T || (eq && eq_seen + popc64(eqm & lt) < need));
       eq_seen += popc64(eqm);
       const uint64_t sm = __ballot(sel);
-      if (sel) out[base + popc64(sm & lt)] = m;
+      if (sel)
+        for (int hh = 0; hh < GS; ++hh)
+          idx[((int64_t)(h0 + hh) * total_blocks + gb) * width + base + popc64(sm & lt)] = m;
       base += popc64(sm);
     }
   }
   if (lane == 0) {
-    out[tau] = i;
-    cnt[(int64_t)h * total_blocks + gb] = tau + 1;
+    for (int hh = 0; hh < GS; ++hh) {
+      idx[((int64_t)(h0 + hh) * total_blocks + gb) * width + tau] = i;
+      cnt[(int64_t)(h0 + hh) * total_blocks + gb] = tau + 1;
+    }
   }
 }
 
@@ -116,7 +135,7 @@ constexpr int kRowBmax = 4096;
 template <int E, int NT>
 __global__ __launch_bounds__(NT) void select_row_kernel(
     const float* __restrict__ r, int hq, int hkv, const int32_t* __restrict__ cur_block,
-    int b_max, int rho, int dense, int width, int32_t* __restrict__ idx,
+    int b_max, int rho, int flags, int width, int32_t* __restrict__ idx,
     int32_t* __restrict__ cnt, int32_t* __restrict__ union_idx,
     int32_t* __restrict__ union_cnt, uint32_t* __restrict__ union_mask, int union_width) {
   __shared__ uint32_t umask[kRowBmax];
@@ -128,7 +147,9 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
   const int nthreads = blockDim.x;
   const int c = cur_block[seq];
   const int b = c + 1;
-  const int tau = (int)(((int64_t)rho * b) / 100);
+  const int tau = (int)(((int64_t)rho * b) / 100);   // = the per-row budget of row c
+  const bool dense = (flags & SWS_SELECT_DENSE) != 0;
+  const bool group = (flags & SWS_SELECT_GROUP) != 0;
   const uint32_t all = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
   for (int m = threadIdx.x; m < b; m += nthreads) umask[m] = (dense || m == c) ? all : 0u;
   __syncthreads();
@@ -140,12 +161,20 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
       if (out) for (int m = lane; m <= c; m += 64) out[m] = m;
       if (out && lane == 0) cnt[(int64_t)seq * hq + h] = c + 1;
     } else {
-      const float* row = r + ((int64_t)seq * hq + h) * b_max;
+      // with SWS_SELECT_GROUP every wave scores the row by the group's fp32
+      // sum (heads in ascending order), so all heads keep the same blocks
+      const float* row = r + ((int64_t)seq * hq + (group ? g * G : h)) * b_max;
+      const int nsum = group ? G : 1;
       uint32_t key[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int m = e * 64 + lane;
-        key[e] = (m < c) ? order_key(row[m]) : 0u;
+        float v = 0.f;
+        if (m < c) {
+          v = row[m];
+          for (int hh = 1; hh < nsum; ++hh) v += row[(int64_t)hh * b_max + m];
+        }
+        key[e] = (m < c) ? order_key(v) : 0u;
       }
       uint32_t T;
       int need;
@@ -203,25 +232,26 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
 
 }  // namespace
 
-hipError_t launch_select(const float* R, int hq, const int32_t* cu_blocks, int n_seqs,
-                         int total_blocks, int max_blocks, int rho, int dense, int width,
+hipError_t launch_select(const float* R, int hq, int hkv, const int32_t* cu_blocks, int n_seqs,
+                         int total_blocks, int max_blocks, int rho, int flags, int width,
                          int32_t* idx, int32_t* cnt, hipStream_t st) {
   if (total_blocks == 0 || max_blocks == 0) return hipSuccess;
-  dim3 grid((max_blocks + 3) / 4, hq, n_seqs);
+  const int GS = (flags & SWS_SELECT_GROUP) ? hq / hkv : 1;
+  dim3 grid((max_blocks + 3) / 4, hq / GS, n_seqs);
   if (max_blocks <= 256)
     hipLaunchKernelGGL((select_kernel<4>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
-                       total_blocks, rho, dense, width, idx, cnt);
+                       total_blocks, rho, flags, GS, width, idx, cnt);
   else if (max_blocks <= 1024)
     hipLaunchKernelGGL((select_kernel<16>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
-                       total_blocks, rho, dense, width, idx, cnt);
+                       total_blocks, rho, flags, GS, width, idx, cnt);
   else
     hipLaunchKernelGGL((select_kernel<64>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
-                       total_blocks, rho, dense, width, idx, cnt);
+                       total_blocks, rho, flags, GS, width, idx, cnt);
   return hipGetLastError();
 }
 
 hipError_t launch_select_row(const float* r, int hq, int hkv, int n_seqs,
-                             const int32_t* cur_block, int b_max, int rho, int dense, int width,
+                             const int32_t* cur_block, int b_max, int rho, int flags, int width,
                              int32_t* idx, int32_t* cnt, int32_t* union_idx, int32_t* union_cnt,
                              uint32_t* union_mask, int union_width, hipStream_t st) {
   if (n_seqs == 0) return hipSuccess;
@@ -230,7 +260,7 @@ hipError_t launch_select_row(const float* r, int hq, int hkv, int n_seqs,
   dim3 block(64 * G);
 #define SWS_SEL_ROW(E, NT)                                                                     \
   hipLaunchKernelGGL((select_row_kernel<E, NT>), grid, block, 0, st, r, hq, hkv, cur_block,   \
-                     b_max, rho, dense, width, idx, cnt, union_idx, union_cnt, union_mask,     \
+                     b_max, rho, flags, width, idx, cnt, union_idx, union_cnt, union_mask,     \
                      union_width)
 #define SWS_SEL_ROW_NT(E)           \
   do {                              \

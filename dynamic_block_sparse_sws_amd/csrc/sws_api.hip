@@ -153,33 +153,57 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
                   fn);
 }
 
-int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
-                    int32_t total_blocks, int32_t max_blocks, int32_t rho_percent, int32_t dense,
-                    int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
-  const char* fn = "sws_select_topk";
+static int select_topk_impl(const char* fn, const float* R, int32_t hq, int32_t hkv,
+                            const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
+                            int32_t max_blocks, int32_t rho_percent, int32_t flags,
+                            int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
+  const bool dense = (flags & SWS_SELECT_DENSE) != 0;
   if (!dense) REQUIRE_PTR(R);
   REQUIRE_PTR(cu_blocks);
   REQUIRE_PTR(idx);
   REQUIRE_PTR(cnt);
+  if (flags & ~(SWS_SELECT_DENSE | SWS_SELECT_ROW_TAU | SWS_SELECT_GROUP))
+    return fail(SWS_ERR_SHAPE, "%s: unknown flags 0x%x", fn, flags);
   if (hq < 1 || n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d n_seqs=%d total_blocks=%d max_blocks=%d", fn, hq, n_seqs, total_blocks, max_blocks);
+  if (hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
   if (max_blocks > 4096) return fail(SWS_ERR_UNSUPPORTED, "%s: max_blocks=%d > 4096", fn, max_blocks);
   if (rho_percent < 0 || rho_percent > 100)
     return fail(SWS_ERR_SHAPE, "%s: rho_percent=%d outside [0,100]", fn, rho_percent);
   const int need = dense ? max_blocks : std::min(max_blocks, tau_of(rho_percent, max_blocks) + 1);
   if (width < need || width < 1)
     return fail(SWS_ERR_SHAPE, "%s: width=%d < required %d", fn, width, need);
-  return launched(sws::launch_select(R, hq, cu_blocks, n_seqs, total_blocks, max_blocks,
-                                     rho_percent, dense, width, idx, cnt, (hipStream_t)stream),
+  return launched(sws::launch_select(R, hq, hkv, cu_blocks, n_seqs, total_blocks, max_blocks,
+                                     rho_percent, flags, width, idx, cnt, (hipStream_t)stream),
                   fn);
+}
+
+int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
+                    int32_t total_blocks, int32_t max_blocks, int32_t rho_percent, int32_t dense,
+                    int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
+  return select_topk_impl("sws_select_topk", R, hq, hq, cu_blocks, n_seqs, total_blocks,
+                          max_blocks, rho_percent, dense ? SWS_SELECT_DENSE : 0, width, idx, cnt,
+                          stream);
+}
+
+int sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t* cu_blocks,
+                          int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
+                          int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
+                          int32_t* cnt, void* stream) {
+  return select_topk_impl("sws_select_topk_flags", R, hq, hkv, cu_blocks, n_seqs, total_blocks,
+                          max_blocks, rho_percent, flags, width, idx, cnt, stream);
 }
 
 int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
                         const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
-                        int32_t dense, int32_t width, int32_t* idx, int32_t* cnt,
+                        int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
                         int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
                         int32_t union_width, void* stream) {
   const char* fn = "sws_select_topk_row";
+  const bool dense = (flags & SWS_SELECT_DENSE) != 0;
+  if (flags & ~(SWS_SELECT_DENSE | SWS_SELECT_ROW_TAU | SWS_SELECT_GROUP))
+    return fail(SWS_ERR_SHAPE, "%s: unknown flags 0x%x", fn, flags);
   if (!dense) REQUIRE_PTR(r);
   REQUIRE_PTR(cur_block);
   REQUIRE_PTR(union_idx);
@@ -201,7 +225,7 @@ int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
   if (union_width < uneed)
     return fail(SWS_ERR_SHAPE, "%s: union_width=%d < required %d", fn, union_width, uneed);
   return launched(sws::launch_select_row(r, hq, hkv, n_seqs, cur_block, b_max, rho_percent,
-                                         dense, width, idx, cnt, union_idx, union_cnt,
+                                         flags, width, idx, cnt, union_idx, union_cnt,
                                          union_mask, union_width, (hipStream_t)stream),
                   fn);
 }

@@ -81,11 +81,11 @@ hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, in
 hipError_t launch_walk_row(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
                            int n_seqs, const int32_t* cur_block, int b_max, int s,
                            const float* r_prev, float* r_out, hipStream_t st);
-hipError_t launch_select(const float* R, int hq, const int32_t* cu_blocks, int n_seqs,
-                         int total_blocks, int max_blocks, int rho, int dense, int width,
+hipError_t launch_select(const float* R, int hq, int hkv, const int32_t* cu_blocks, int n_seqs,
+                         int total_blocks, int max_blocks, int rho, int flags, int width,
                          int32_t* idx, int32_t* cnt, hipStream_t st);
 hipError_t launch_select_row(const float* r, int hq, int hkv, int n_seqs,
-                             const int32_t* cur_block, int b_max, int rho, int dense, int width,
+                             const int32_t* cur_block, int b_max, int rho, int flags, int width,
                              int32_t* idx, int32_t* cnt, int32_t* union_idx, int32_t* union_cnt,
                              uint32_t* union_mask, int union_width, hipStream_t st);
 hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, int dtype,

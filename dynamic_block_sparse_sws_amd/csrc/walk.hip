@@ -296,18 +296,36 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
 
   float qv[LMAX][CQ], kv[LMAX][CQ];
   if (in_regs && k == KP) {
-    // full quarters: 16-byte loads of every segment row (rows past the
-    // segment re-read row b - 1 and are never used), no branches
-#pragma unroll
-    for (int l = 0; l < LMAX; ++l) {
-      const int64_t off = (int64_t)min(j0 + l, b - 1) * KP + p * CQ;
-#pragma unroll
-      for (int e = 0; e < CQ; e += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + off + e);
-        const float4 bb = *reinterpret_cast<const float4*>(krow + off + e);
-        qv[l][e] = a.x; qv[l][e + 1] = a.y; qv[l][e + 2] = a.z; qv[l][e + 3] = a.w;
-        kv[l][e] = bb.x; kv[l][e + 1] = bb.y; kv[l][e + 2] = bb.z; kv[l][e + 3] = bb.w;
+    // full quarters: the sketch rows go through LDS (the ypart area, unused
+    // until the first hop) in chunks of R rows, read with contiguous 16-byte
+    // loads across the workgroup; each thread then picks its segment's rows
+    constexpr int R = 8192 / KP;               // rows per chunk: q and k fill 64 KB
+    constexpr int V4 = KP / 4;                 // float4 per row
+    float* stage = &ypart[0][0];
+    for (int r0 = 0; r0 < b; r0 += R) {
+      const int nr = min(R, b - r0);
+      for (int v = tid; v < nr * V4; v += kRowThreads) {
+        const int64_t g4 = (int64_t)r0 * V4 + v;
+        reinterpret_cast<float4*>(stage)[v] = reinterpret_cast<const float4*>(qrow)[g4];
+        reinterpret_cast<float4*>(stage + R * KP)[v] = reinterpret_cast<const float4*>(krow)[g4];
       }
+      __syncthreads();
+#pragma unroll
+      for (int l = 0; l < LMAX; ++l) {
+        const int j = j0 + l;
+        if (j >= r0 && j < r0 + nr && j < j1) {
+          const float* qs = stage + (j - r0) * KP + p * CQ;
+          const float* ks = stage + R * KP + (j - r0) * KP + p * CQ;
+#pragma unroll
+          for (int e = 0; e < CQ; e += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(qs + e);
+            const float4 bb = *reinterpret_cast<const float4*>(ks + e);
+            qv[l][e] = a.x; qv[l][e + 1] = a.y; qv[l][e + 2] = a.z; qv[l][e + 3] = a.w;
+            kv[l][e] = bb.x; kv[l][e + 1] = bb.y; kv[l][e + 2] = bb.z; kv[l][e + 3] = bb.w;
+          }
+        }
+      }
+      __syncthreads();
     }
   } else {
 #pragma unroll

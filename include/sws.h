@@ -55,6 +55,23 @@ typedef enum sws_dtype {
   SWS_BF16 = 1
 } sws_dtype;
 
+/* Selection flags (sws_select_topk_flags, sws_select_topk_row).  The page
+ * leaves the density rule and the GQA treatment open; the default (0) is one
+ * budget tau = floor(rho * b / 100) per sequence and one list per query head.
+ *   SWS_SELECT_DENSE   every block m <= i (the dense early layers)
+ *   SWS_SELECT_ROW_TAU row i keeps tau_i = floor(rho * (i + 1) / 100) earlier
+ *                      blocks, the density of its own causal prefix (in decode
+ *                      this is the default rule already)
+ *   SWS_SELECT_GROUP   one list per KV group: rows are scored by the fp32 sum,
+ *                      in ascending head order, of the walk states of the
+ *                      group's query heads, and every head of the group gets
+ *                      that list */
+enum {
+  SWS_SELECT_DENSE = 1,
+  SWS_SELECT_ROW_TAU = 2,
+  SWS_SELECT_GROUP = 4
+};
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int sws_version(void);
 
@@ -166,6 +183,18 @@ int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_
                      int32_t dense, int32_t width, int32_t* idx, int32_t* cnt, void* stream);
 
 /*
+ * sws_select_topk_flags - sws_select_topk with the selection variants of the
+ * SWS_SELECT_* flags; hkv (a divisor of hq) is used by SWS_SELECT_GROUP only.
+ * Same layouts, limits and errors as sws_select_topk; with
+ * SWS_SELECT_ROW_TAU the width bound is the same (the last row has the
+ * largest budget).
+ */
+int sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t* cu_blocks,
+                          int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
+                          int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
+                          int32_t* cnt, void* stream);
+
+/*
  * sws_select_topk_row - decode form of sws_select_topk for the open block
  * c = cur_block[seq] (b = c + 1 blocks, tau = floor(rho_percent * b / 100)),
  * followed by the union over the query heads of each KV group: the ascending
@@ -180,10 +209,14 @@ int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_
  *   width      >= min(b_max, floor(rho_percent * b_max / 100) + 1)
  *   union_width >= min(b_max, (hq/hkv) * floor(rho_percent * b_max / 100) + 1)
  *   hq / hkv <= 16, b_max <= 4096
+ *   flags      SWS_SELECT_* bits (0 or 1 keep the meaning of the former
+ *              `dense` argument; SWS_SELECT_ROW_TAU changes nothing here;
+ *              with SWS_SELECT_GROUP the union is the group's shared list,
+ *              kept by every head)
  */
 int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
                          const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
-                         int32_t dense, int32_t width, int32_t* idx, int32_t* cnt,
+                         int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
                          int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
                          int32_t union_width, void* stream);
 

@@ -52,7 +52,8 @@ import numpy as np
 __all__ = [
     "n_blocks", "block_ranges", "block_sums", "block_means", "a_true", "a_true_bruteforce",
     "sylvester", "fwht", "hadamard_projection", "sketch_from_means", "sketch", "sketched_scores",
-    "rownorm", "walk_update", "walk_row", "n_select", "select_row", "select", "sparse_attention",
+    "rownorm", "walk_update", "walk_row", "n_select", "select_row", "select", "n_select_row",
+    "select_rows_tau", "group_scores", "sparse_attention",
     "sparse_attention_rows", "prefill_layer", "prefill", "decode_step", "SeqPrefill",
 ]
 
@@ -232,6 +233,37 @@ def select(R: np.ndarray, rho: int, dense: bool = False):
         return [np.arange(i + 1, dtype=np.int64) for i in range(b)]
     tau = n_select(rho, b)
     return [select_row(R[i], i, tau) for i in range(b)]
+
+
+# ---------------------------------------------------------------------------
+# Selection variants for readings the page leaves open (kept behind flags)
+# ---------------------------------------------------------------------------
+
+def n_select_row(rho: int, i: int) -> int:
+    """Per-row budget: query block i keeps tau_i = floor(rho * (i + 1) / 100)
+    earlier blocks, the same density of its own causal prefix (the decode
+    rule, where the open block is the last of the prefix, applied to every
+    prefill row)."""
+    return (int(rho) * (int(i) + 1)) // 100
+
+
+def select_rows_tau(R: np.ndarray, rho: int, dense: bool = False):
+    """Per-row lists with the per-row budget tau_i of n_select_row."""
+    b = R.shape[0]
+    if dense:
+        return [np.arange(i + 1, dtype=np.int64) for i in range(b)]
+    return [select_row(R[i], i, n_select_row(rho, i)) for i in range(b)]
+
+
+def group_scores(Rs) -> np.ndarray:
+    """Shared walk score of a KV group (GQA): the walk states of the group's
+    query heads added up, in fp32 and in ascending head order.  The score only
+    decides an integer result (which blocks are kept), so it is formed in the
+    precision and order the kernels use, and the selections compare exactly."""
+    acc = np.asarray(Rs[0], np.float32).copy()
+    for R in Rs[1:]:
+        acc = (acc + np.asarray(R, np.float32)).astype(np.float32)
+    return acc
 
 
 # ---------------------------------------------------------------------------

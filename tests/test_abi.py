@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     L = sws.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -80,6 +80,11 @@ def test_other_entry_points_validation():
     assert L.sws_select_topk(P, 8, P, 1, 1024, 1024, 101, 0, 1024, P, P, N) == 2
     assert L.sws_select_topk(P, 8, P, 1, 8192, 8192, 20, 0, 8192, P, P, N) == 3
     assert L.sws_select_topk(P, 8, P, 1, 16, 16, 100, 1, 15, P, P, N) == 2
+    # select with flags: unknown flag bits, group size not dividing hq, R NULL
+    assert L.sws_select_topk_flags(P, 8, 4, P, 1, 16, 16, 20, 8, 16, P, P, N) == 2
+    assert L.sws_select_topk_flags(P, 8, 3, P, 1, 16, 16, 20, 4, 16, P, P, N) == 2
+    assert L.sws_select_topk_flags(N, 8, 4, P, 1, 16, 16, 20, 6, 16, P, P, N) == 1
+    assert L.sws_select_topk_row(P, 32, 8, 2, P, 1029, 20, 16, 206, N, N, P, P, P, 1029, N) == 2
     # select row: union too narrow; group too large; idx without cnt
     assert L.sws_select_topk_row(P, 32, 8, 2, P, 1029, 20, 0, 206, N, N, P, P, P, 800, N) == 2
     assert L.sws_select_topk_row(P, 64, 2, 2, P, 1029, 20, 0, 206, N, N, P, P, P, 1029, N) == 3

@@ -204,3 +204,52 @@ def test_decode_other_walk_degree_and_sketch_dim():
     _print("decode s=2 k=64")
     w, _, _ = run_decode_case(cfg, (300, 129), 6, 2, 25, 0, {0, 2, 5})
     _print("worst", w)
+
+
+def test_decode_group_shared_selection():
+    """Decode with one shared list per KV group: every head keeps the list the
+    oracle selects on the group's fp32-summed walk rows, the union is that
+    list with every head's bit set, and the attention matches."""
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=8, hkv=2, k=32)
+    ns, P, B = 2, 900, cfg.B
+    hq, hkv, kd, grp = cfg.hq, cfg.hkv, cfg.k, cfg.hq // cfg.hkv
+    b_max = -(-(P + 1) // B)
+    signs, cols = gen.hadamard_tables(cfg.d, kd)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    full = [{w: gen.seq_tensor(cfg, 0, s, w, P + 1, "cuda") for w in "qkv"} for s in range(ns)]
+    geo = sws.Geometry([P + 1], B)
+    qsk = torch.zeros((ns, hq, b_max, kd), dtype=torch.float32, device="cuda")
+    ksk = torch.zeros((ns, hkv, b_max, kd), dtype=torch.float32, device="cuda")
+    for s in range(ns):
+        sws.sketch(full[s]["q"].contiguous(), geo, kd, sd, cd, out=qsk[s], ld_head=b_max * kd)
+        sws.sketch(full[s]["k"].contiguous(), geo, kd, sd, cd, out=ksk[s], ld_head=b_max * kd)
+    cur = torch.full((ns,), P // B, dtype=torch.int32, device="cuda")
+    r = torch.zeros((ns, hq, b_max), dtype=torch.float32, device="cuda")
+    sws.walk_update_row(qsk, ksk, cur, cfg.s, None, r)
+    rho = 30
+    uidx, ucnt, umask, idx, cnt = sws.select_topk_row(r, hq, hkv, cur, b_max, rho, per_head=True,
+                                                      group=True)
+    kc = torch.stack([full[s]["k"] for s in range(ns)]).contiguous()
+    vc = torch.stack([full[s]["v"] for s in range(ns)]).contiguous()
+    qn = torch.stack([full[s]["q"][P] for s in range(ns)]).contiguous()
+    ctx = torch.full((ns,), P + 1, dtype=torch.int32, device="cuda")
+    out = sws.sparse_attn_decode(qn, kc, vc, ctx, B, uidx, ucnt, umask)
+    torch.cuda.synchronize()
+    c = P // B
+    rh = r.cpu().numpy()
+    for s in range(ns):
+        for g in range(hkv):
+            score = O.group_scores([rh[s, h, :c + 1] for h in range(g * grp, (g + 1) * grp)])
+            want = O.select_row(score, c, O.n_select(rho, c + 1)).tolist()
+            for h in range(g * grp, (g + 1) * grp):
+                assert idx[s, h, :cnt[s, h]].tolist() == want, (s, h)
+            n_u = int(ucnt[s, g])
+            assert uidx[s, g, :n_u].tolist() == want
+            assert (umask[s, g, :n_u].cpu().numpy().astype(np.uint32) == (1 << grp) - 1).all()
+            H = {w: f64(full[s][w]) for w in "qkv"}
+            keys = np.concatenate([np.arange(j * B, min((j + 1) * B, P + 1)) for j in want])
+            for h in range(g * grp, (g + 1) * grp):
+                z = (H["k"][keys, g] @ H["q"][P, h]) / math.sqrt(cfg.d)
+                wgt = np.exp(z - z.max())
+                o_want = (wgt @ H["v"][keys, g]) / wgt.sum()
+                assert np.abs(f64(out[s, h]) - o_want).max() <= TOL_ATTN_BF16, (s, h)

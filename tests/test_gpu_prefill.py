@@ -117,3 +117,55 @@ def test_walk_degree_and_sketch_dim(s, kdim, B):
     run = PrefillRun(cfg, (5 * B + 17, 3 * B), 2, 20, n_dense=0)
     w = check_prefill_run(run)
     _print("worst", w)
+
+
+@pytest.mark.parametrize("row_tau,group", [(True, False), (False, True), (True, True)])
+def test_selection_variants(row_tau, group):
+    """The selection variants behind flags (per-row budget, one shared list per
+    KV group) are bit-exact against the oracle on the GPU's own walk states,
+    and the attention over the shared lists matches the oracle."""
+    cfg = gen.CONFIGS["C2"].with_(d=128, B=64, hq=8, hkv=2, k=32)
+    seqlens = (1500, 700)
+    geo = sws.Geometry(list(seqlens), cfg.B)
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    grp = cfg.hq // cfg.hkv
+    rho = 25
+    R = None
+    for l in range(2):
+        q, k, v, _ = gen.layer_inputs(cfg, l, device="cuda", seqlens=list(seqlens))
+        q_sk = sws.sketch(q, geo, cfg.k, sd, cd)
+        k_sk = sws.sketch(k, geo, cfg.k, sd, cd)
+        R = sws.walk_update(q_sk, k_sk, geo, cfg.s, R, R_out=R)
+        idx, cnt = sws.select_topk(R, cfg.hq, geo, rho, row_tau=row_tau,
+                                   group_hkv=cfg.hkv if group else None)
+        out = sws.sparse_attn_prefill(q, k, v, geo, idx, cnt)
+        torch.cuda.synchronize()
+        Rh, idx_h, cnt_h = R.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+        _print("variant", row_tau, group, "layer", l)
+        for s in range(len(seqlens)):
+            b = geo.blocks[s]
+            b0 = int(geo.cu_blocks_host[s])
+            off = geo.walk_offset(s, cfg.hq)
+            Rs = [Rh[off + h * b * b: off + (h + 1) * b * b].reshape(b, b) for h in range(cfg.hq)]
+            for h in range(cfg.hq):
+                g = h // grp
+                score = O.group_scores(Rs[g * grp:(g + 1) * grp]) if group else Rs[h]
+                want = O.select_rows_tau(score, rho) if row_tau else O.select(score, rho)
+                for i in range(b):
+                    got = idx_h[h, b0 + i, :cnt_h[h, b0 + i]].tolist()
+                    assert got == want[i].tolist(), (row_tau, group, l, s, h, i)
+            # attention of sampled blocks over the variant's lists
+            t0 = int(geo.cu_seqlens_host[s])
+            ts = slice(t0, t0 + seqlens[s])
+            for h in (0, cfg.hq - 1):
+                g = h // grp
+                lists = [idx_h[h, b0 + i, :cnt_h[h, b0 + i]].astype(np.int64) for i in range(b)]
+                rows = [0, b // 2, b - 1]
+                res = O.sparse_attention_rows(f64(q[ts, h]), f64(k[ts, g]), f64(v[ts, g]), lists,
+                                              cfg.B, 1.0 / math.sqrt(cfg.d), rows)
+                o = f64(out[ts, h])
+                for i in rows:
+                    ow, _ = res[i]
+                    err = np.abs(o[i * cfg.B:i * cfg.B + ow.shape[0]] - ow).max()
+                    assert err <= TOL_ATTN_BF16, (row_tau, group, l, s, h, i, err)
