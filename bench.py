@@ -346,14 +346,19 @@ def diagnostics(args, torch, sws, gen, ctx):
         e.record()
         return e
 
-    def run(geo_, kk, s, rho, attn=True, lse=None):
+    def run(geo_, kk, s, rho, attn=True, lse=None, mode=0):
         sd, cd = tables(kk)
         R = torch.empty(geo_.walk_numel(hq), dtype=torch.float32, device=dev)
+        wws = (torch.empty(sws.walk_variant_workspace_size(geo_.walk_numel(hq)),
+                           dtype=torch.uint8, device=dev) if mode else None)
         ts = [ev()]
         q_sk = sws.sketch(q, geo_, kk, sd, cd)
         k_sk = sws.sketch(k, geo_, kk, sd, cd)
         ts.append(ev())
-        sws.walk_update(q_sk, k_sk, geo_, s, None, R_out=R)
+        if mode:
+            sws.walk_update_variant(q_sk, k_sk, geo_, s, mode, None, R_out=R, ws=wws)
+        else:
+            sws.walk_update(q_sk, k_sk, geo_, s, None, R_out=R)
         ts.append(ev())
         idx, cnt = sws.select_topk(R, hq, geo_, rho)
         ts.append(ev())
@@ -423,6 +428,14 @@ def diagnostics(args, torch, sws, gen, ctx):
         sweep.append(rec)
         print(f"[diag] sweep B={B} k={kk} s={s} rho={rho}: {sum(t.values()) / 1e3:.2f} ms",
               file=sys.stderr, flush=True)
+    for mode, name in ((sws.WALK_POWER, "power"), (sws.WALK_SOFTMAX, "softmax")):
+        run(geo, 32, 8, 20, attn=False, mode=mode)          # warm-up
+        idx, cnt, t = run(geo, 32, 8, 20, attn=False, mode=mode)
+        sweep.append({"B": B, "k": 32, "s": 8, "rho": 20, "walk_mode": name, "stage_us": t,
+                      "executed_block_pairs": int(cnt.long().sum()),
+                      "jaccard_vs_exact_scores": jaccard(idx, cnt)})
+        print(f"[diag] walk variant {name}: walk {t['walk'] / 1e3:.2f} ms", file=sys.stderr,
+              flush=True)
     geo64 = sws.Geometry([n], 64)
     idx, cnt, t = run(geo64, 32, 8, 20)
     sweep.append({"B": 64, "k": 32, "s": 8, "rho": 20, "stage_us": t,
@@ -445,8 +458,9 @@ def diagnostics(args, torch, sws, gen, ctx):
 
     # planted chain recall: multi-hop walk against a one-hop walk
     recall = {}
-    for s in (1, 8):
-        idx, cnt, _ = run(geo, 32, s, 20, attn=False)
+    for s, mode, key in ((1, 0, "s=1"), (8, 0, "s=8"), (8, sws.WALK_POWER, "power s=8"),
+                         (8, sws.WALK_SOFTMAX, "softmax s=8")):
+        idx, cnt, _ = run(geo, 32, s, 20, attn=False, mode=mode)
         idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
         hit_j = hit_m = tot = 0
         for g in range(hkv):
@@ -459,8 +473,8 @@ def diagnostics(args, torch, sws, gen, ctx):
                         hit_j += j in sel
                         hit_m += m in sel
                         tot += 1
-        recall[f"s={s}"] = {"near_block_j": hit_j / tot, "far_block_m": hit_m / tot,
-                            "chains_x_heads": tot}
+        recall[key] = {"near_block_j": hit_j / tot, "far_block_m": hit_m / tot,
+                       "chains_x_heads": tot}
     return {"layer": "128K prefill layer (generator layer 2), walk from the identity",
             "sweep": sweep, "captured_attention_mass": captured, "planted_chain_recall": recall,
             "exact_reference_heads": ref_heads}

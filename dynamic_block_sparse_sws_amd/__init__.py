@@ -16,8 +16,9 @@ import numpy as np
 import torch
 
 __all__ = [
-    "SwsError", "lib", "F32", "BF16", "SELECT_DENSE", "SELECT_ROW_TAU", "SELECT_GROUP", "Geometry", "geometry", "walk_state_numel",
-    "sketch", "sketch_append", "walk_update", "walk_update_row", "select_topk",
+    "SwsError", "lib", "F32", "BF16", "WALK_DEFAULT", "WALK_POWER", "WALK_SOFTMAX", "SELECT_DENSE", "SELECT_ROW_TAU", "SELECT_GROUP", "Geometry", "geometry", "walk_state_numel",
+    "sketch", "sketch_append", "walk_update", "walk_update_row", "walk_update_variant",
+    "walk_variant_workspace_size", "select_topk",
     "select_topk_row", "sparse_attn_prefill", "sparse_attn_decode", "decode_workspace_size",
     "prefill_layer", "EXPORTED_SYMBOLS", "version",
 ]
@@ -25,7 +26,10 @@ __all__ = [
 F32 = 0
 BF16 = 1
 
-# selection flags (include/sws.h)
+# walk modes and selection flags (include/sws.h)
+WALK_DEFAULT = 0
+WALK_POWER = 1
+WALK_SOFTMAX = 2
 SELECT_DENSE = 1
 SELECT_ROW_TAU = 2
 SELECT_GROUP = 4
@@ -38,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "sws_sketch_append", "sws_walk_update", "sws_walk_update_row", "sws_select_topk",
     "sws_select_topk_row", "sws_sparse_attn_prefill", "sws_sparse_attn_decode",
     "sws_decode_workspace_size", "sws_prefill_workspace_size", "sws_select_topk_flags",
+    "sws_walk_update_variant", "sws_walk_variant_workspace_size", "sws_walk_update_row_variant",
 )
 
 
@@ -66,6 +71,11 @@ _SIGS = {
                           ctypes.c_int),
     "sws_walk_update": ([_P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P], ctypes.c_int),
     "sws_walk_update_row": ([_P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P], ctypes.c_int),
+    "sws_walk_update_variant": ([_P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _I64, _P,
+                                 _SZ, _P], ctypes.c_int),
+    "sws_walk_variant_workspace_size": ([_I64], _SZ),
+    "sws_walk_update_row_variant": ([_P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P],
+                                    ctypes.c_int),
     "sws_select_topk": ([_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], ctypes.c_int),
     "sws_select_topk_flags": ([_P, _I, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
                               ctypes.c_int),
@@ -209,13 +219,43 @@ def walk_update(q_sk: torch.Tensor, k_sk: torch.Tensor, geo: Geometry, s: int,
 
 
 def walk_update_row(q_cache: torch.Tensor, k_cache: torch.Tensor, cur_block: torch.Tensor,
-                    s: int, r_prev: Optional[torch.Tensor], r_out: torch.Tensor, stream=None):
+                    s: int, r_prev: Optional[torch.Tensor], r_out: torch.Tensor, stream=None,
+                    mode: int = WALK_DEFAULT):
     n_seqs, hq, b_max, k = q_cache.shape
     hkv = k_cache.shape[1]
-    _check("sws_walk_update_row", lib().sws_walk_update_row(
-        _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs, _ptr(cur_block), b_max, s,
-        _ptr(r_prev), _ptr(r_out), _stream(stream)))
+    if mode == WALK_DEFAULT:
+        _check("sws_walk_update_row", lib().sws_walk_update_row(
+            _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs, _ptr(cur_block), b_max, s,
+            _ptr(r_prev), _ptr(r_out), _stream(stream)))
+    else:
+        _check("sws_walk_update_row_variant", lib().sws_walk_update_row_variant(
+            _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs, _ptr(cur_block), b_max, s, mode,
+            _ptr(r_prev), _ptr(r_out), _stream(stream)))
     return r_out
+
+
+def walk_variant_workspace_size(walk_numel: int) -> int:
+    return int(lib().sws_walk_variant_workspace_size(walk_numel))
+
+
+def walk_update_variant(q_sk: torch.Tensor, k_sk: torch.Tensor, geo: Geometry, s: int,
+                        mode: int, R_prev: Optional[torch.Tensor],
+                        R_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Walk update with a walk mode (WALK_POWER, WALK_SOFTMAX)."""
+    hq, _, k = q_sk.shape
+    hkv = k_sk.shape[0]
+    numel = geo.walk_numel(hq)
+    if R_out is None:
+        R_out = torch.empty(numel, dtype=torch.float32, device=q_sk.device)
+    if ws is None:
+        ws = torch.empty(max(1, walk_variant_workspace_size(numel)), dtype=torch.uint8,
+                         device=q_sk.device)
+    _check("sws_walk_update_variant", lib().sws_walk_update_variant(
+        _ptr(q_sk), _ptr(k_sk), hq, hkv, k, _ptr(geo.cu_blocks), geo.n_seqs, geo.total_blocks,
+        geo.max_blocks, s, mode, _ptr(R_prev), _ptr(R_out), numel, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return R_out
 
 
 def select_width(rho: int, max_blocks: int, dense: bool = False) -> int:

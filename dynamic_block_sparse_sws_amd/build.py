@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsws.so")
-SOURCES = ["sws_api.hip", "sketch.hip", "walk.hip", "select.hip", "attn_prefill.hip",
-           "attn_decode.hip"]
+SOURCES = ["sws_api.hip", "sketch.hip", "walk.hip", "walk_variant.hip", "select.hip",
+           "attn_prefill.hip", "attn_decode.hip"]
 ARCH = os.environ.get("SWS_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

@@ -153,6 +153,70 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
                   fn);
 }
 
+int sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv,
+                            int32_t k, const int32_t* cu_blocks, int32_t n_seqs,
+                            int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
+                            const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const char* fn = "sws_walk_update_variant";
+  if (mode == SWS_WALK_DEFAULT)
+    return sws_walk_update(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks,
+                           s, R_prev, R_out, stream);
+  if (mode != SWS_WALK_POWER && mode != SWS_WALK_SOFTMAX)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: mode=%d", fn, mode);
+  REQUIRE_PTR(q_sk);
+  REQUIRE_PTR(k_sk);
+  REQUIRE_PTR(cu_blocks);
+  REQUIRE_PTR(R_out);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
+  if (n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d max_blocks=%d", fn, n_seqs, total_blocks, max_blocks);
+  if (max_blocks > 4096) return fail(SWS_ERR_UNSUPPORTED, "%s: max_blocks=%d > 4096", fn, max_blocks);
+  if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
+  if (walk_numel < (int64_t)hq * max_blocks * max_blocks)
+    return fail(SWS_ERR_SHAPE, "%s: walk_numel=%lld smaller than hq * max_blocks^2", fn,
+                (long long)walk_numel);
+  const size_t need = sws::walk_variant_workspace_bytes(walk_numel);
+  if (!ws || ws_bytes < need)
+    return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+  return launched(sws::launch_walk_variant(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs,
+                                           total_blocks, max_blocks, s, mode, R_prev, R_out,
+                                           walk_numel, ws, (hipStream_t)stream),
+                  fn);
+}
+
+size_t sws_walk_variant_workspace_size(int64_t walk_numel) {
+  return walk_numel > 0 ? sws::walk_variant_workspace_bytes(walk_numel) : 0;
+}
+
+int sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                                int32_t hkv, int32_t k, int32_t n_seqs,
+                                const int32_t* cur_block, int32_t b_max, int32_t s,
+                                int32_t mode, const float* r_prev, float* r_out, void* stream) {
+  const char* fn = "sws_walk_update_row_variant";
+  if (mode == SWS_WALK_DEFAULT)
+    return sws_walk_update_row(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs, cur_block, b_max, s,
+                               r_prev, r_out, stream);
+  if (mode != SWS_WALK_POWER && mode != SWS_WALK_SOFTMAX)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: mode=%d", fn, mode);
+  REQUIRE_PTR(q_sk_cache);
+  REQUIRE_PTR(k_sk_cache);
+  REQUIRE_PTR(cur_block);
+  REQUIRE_PTR(r_out);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
+  if (n_seqs < 0 || b_max < 1 || b_max > 4096)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d b_max=%d (b_max in [1,4096])", fn, n_seqs, b_max);
+  if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
+  return launched(sws::launch_walk_row_variant(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs,
+                                               cur_block, b_max, s, mode, r_prev, r_out,
+                                               (hipStream_t)stream),
+                  fn);
+}
+
 static int select_topk_impl(const char* fn, const float* R, int32_t hq, int32_t hkv,
                             const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
                             int32_t max_blocks, int32_t rho_percent, int32_t flags,

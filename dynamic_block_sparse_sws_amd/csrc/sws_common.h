@@ -81,6 +81,14 @@ hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, in
 hipError_t launch_walk_row(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
                            int n_seqs, const int32_t* cur_block, int b_max, int s,
                            const float* r_prev, float* r_out, hipStream_t st);
+hipError_t launch_walk_variant(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
+                               const int32_t* cu_blocks, int n_seqs, int total_blocks,
+                               int max_blocks, int s, int mode, const float* R_prev,
+                               float* R_out, int64_t walk_numel, void* ws, hipStream_t st);
+size_t walk_variant_workspace_bytes(int64_t walk_numel);
+hipError_t launch_walk_row_variant(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
+                                   int n_seqs, const int32_t* cur_block, int b_max, int s,
+                                   int mode, const float* r_prev, float* r_out, hipStream_t st);
 hipError_t launch_select(const float* R, int hq, int hkv, const int32_t* cu_blocks, int n_seqs,
                          int total_blocks, int max_blocks, int rho, int flags, int width,
                          int32_t* idx, int32_t* cnt, hipStream_t st);

@@ -55,6 +55,20 @@ typedef enum sws_dtype {
   SWS_BF16 = 1
 } sws_dtype;
 
+/* Walk modes (sws_walk_update_variant, sws_walk_update_row_variant).  The
+ * page writes the walk update as R^l = R^(l-1) (A^l)^s and calls s the walk
+ * degree; the default reading (mode 0, sws_walk_update) is s hops with the
+ * signed sketched scores.  Two other readings are kept behind a mode:
+ *   SWS_WALK_POWER    the exponent elementwise: R = rownorm(R_prev T) with
+ *                     T[i][j] = M[i][j]^s (j <= i)
+ *   SWS_WALK_SOFTMAX  transition probabilities: row i of T is the softmax of
+ *                     M[i][0..i]; R = rownorm(R_prev T^s) */
+enum {
+  SWS_WALK_DEFAULT = 0,
+  SWS_WALK_POWER = 1,
+  SWS_WALK_SOFTMAX = 2
+};
+
 /* Selection flags (sws_select_topk_flags, sws_select_topk_row).  The page
  * leaves the density rule and the GQA treatment open; the default (0) is one
  * budget tau = floor(rho * b / 100) per sequence and one list per query head.
@@ -163,6 +177,40 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
                         int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
                         int32_t b_max, int32_t s, const float* r_prev, float* r_out,
                         void* stream);
+
+/*
+ * sws_walk_update_variant - sws_walk_update with a walk mode (SWS_WALK_*).
+ * The variants form the b x b transition matrix T of every (sequence, head)
+ * explicitly and multiply lower-triangular matrices in fp32 (cost s b^3 / 3
+ * multiply-adds per head for SWS_WALK_SOFTMAX, b^3 / 3 for SWS_WALK_POWER).
+ *
+ *   same arguments and layouts as sws_walk_update, plus
+ *   mode        SWS_WALK_DEFAULT (then ws may be NULL), SWS_WALK_POWER or
+ *               SWS_WALK_SOFTMAX, else SWS_ERR_UNSUPPORTED
+ *   walk_numel  hq * sum_s b_s^2 (the element count of R)
+ *   ws          workspace of sws_walk_variant_workspace_size(walk_numel) bytes
+ *               (T and two products, packed like R)
+ *   max_blocks <= 4096; R_prev may equal R_out
+ */
+int sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv,
+                            int32_t k, const int32_t* cu_blocks, int32_t n_seqs,
+                            int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
+                            const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sws_walk_update_variant for walk_numel = hq * sum b_s^2. */
+size_t sws_walk_variant_workspace_size(int64_t walk_numel);
+
+/*
+ * sws_walk_update_row_variant - decode form of sws_walk_update_variant: row
+ * c = cur_block[seq] only, computed with the entries of T formed on the fly
+ * from the sketch caches.  Arguments and layouts as sws_walk_update_row, plus
+ * mode (SWS_WALK_*; SWS_WALK_DEFAULT runs sws_walk_update_row).
+ */
+int sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                                int32_t hkv, int32_t k, int32_t n_seqs,
+                                const int32_t* cur_block, int32_t b_max, int32_t s,
+                                int32_t mode, const float* r_prev, float* r_out, void* stream);
 
 /*
  * sws_select_topk - top-tau key blocks per query block (blog page, section

@@ -53,7 +53,8 @@ __all__ = [
     "n_blocks", "block_ranges", "block_sums", "block_means", "a_true", "a_true_bruteforce",
     "sylvester", "fwht", "hadamard_projection", "sketch_from_means", "sketch", "sketched_scores",
     "rownorm", "walk_update", "walk_row", "n_select", "select_row", "select", "n_select_row",
-    "select_rows_tau", "group_scores", "sparse_attention",
+    "select_rows_tau", "group_scores", "transition", "walk_update_variant",
+    "walk_row_variant", "sparse_attention",
     "sparse_attention_rows", "prefill_layer", "prefill", "decode_step", "SeqPrefill",
 ]
 
@@ -233,6 +234,56 @@ def select(R: np.ndarray, rho: int, dense: bool = False):
         return [np.arange(i + 1, dtype=np.int64) for i in range(b)]
     tau = n_select(rho, b)
     return [select_row(R[i], i, tau) for i in range(b)]
+
+
+# ---------------------------------------------------------------------------
+# Walk variants for readings the page leaves open (kept behind a mode)
+# ---------------------------------------------------------------------------
+
+def transition(M: np.ndarray, mode: str, s: int) -> np.ndarray:
+    """The block transition matrix T of a walk variant, from the causal
+    sketched scores M (entries above the diagonal are not part of the graph):
+    * "power"   - the exponent read elementwise: T[i, j] = M[i, j] ** s;
+    * "softmax" - the scores turned into transition probabilities: row i of T
+                  is the softmax of M[i, 0..i] (0 above the diagonal)."""
+    M = np.asarray(M, np.float64)
+    b = M.shape[0]
+    lower = np.tril(np.ones((b, b), dtype=bool))
+    if mode == "power":
+        return np.where(lower, M ** s, 0.0)
+    if mode == "softmax":
+        Z = np.where(lower, M, -np.inf)
+        Z = Z - Z.max(axis=1, keepdims=True)
+        E = np.exp(Z)
+        return E / E.sum(axis=1, keepdims=True)
+    raise ValueError(mode)
+
+
+def walk_update_variant(R_prev: Optional[np.ndarray], M: np.ndarray, s: int,
+                        mode: str) -> np.ndarray:
+    """Walk state of a variant: "power" takes one step with the elementwise
+    power, R = rownorm(R_prev T); "softmax" takes s steps with the transition
+    probabilities, R = rownorm(R_prev T^s).  R_prev = None is the identity."""
+    T = transition(M, mode, s)
+    X = np.eye(T.shape[0]) if R_prev is None else np.asarray(R_prev, np.float64).copy()
+    for _ in range(1 if mode == "power" else s):
+        X = X @ T
+    return rownorm(X)
+
+
+def walk_row_variant(r_prev: Optional[np.ndarray], M: np.ndarray, i: int, s: int,
+                     mode: str) -> np.ndarray:
+    """Row i of walk_update_variant, as a row vector (decode)."""
+    T = transition(M, mode, s)
+    if r_prev is None:
+        x = np.zeros(T.shape[0])
+        x[i] = 1.0
+    else:
+        x = np.asarray(r_prev, np.float64).copy()
+    for _ in range(1 if mode == "power" else s):
+        x = x @ T
+    m = np.abs(x).max()
+    return x / m if m > 0 else x
 
 
 # ---------------------------------------------------------------------------

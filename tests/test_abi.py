@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 17
     L = sws.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -80,6 +80,14 @@ def test_other_entry_points_validation():
     assert L.sws_select_topk(P, 8, P, 1, 1024, 1024, 101, 0, 1024, P, P, N) == 2
     assert L.sws_select_topk(P, 8, P, 1, 8192, 8192, 20, 0, 8192, P, P, N) == 3
     assert L.sws_select_topk(P, 8, P, 1, 16, 16, 100, 1, 15, P, P, N) == 2
+    # walk variants: unknown mode, workspace too small, walk_numel too small
+    assert L.sws_walk_update_variant(P, P, 8, 4, 32, P, 1, 4, 4, 8, 7, N, P, 128, P, 1 << 20, N) == 3
+    need = L.sws_walk_variant_workspace_size(128)
+    assert need == 128 * 3 * 4
+    assert L.sws_walk_update_variant(P, P, 8, 4, 32, P, 1, 4, 4, 8, 2, N, P, 128, P, need - 4, N) == 4
+    assert L.sws_walk_update_variant(P, P, 8, 4, 32, P, 1, 4, 4, 8, 1, N, P, 100, P, 1 << 20, N) == 2
+    assert L.sws_walk_update_row_variant(P, P, 8, 4, 32, 2, P, 5000, 8, 1, N, P, N) == 2
+    assert L.sws_walk_update_row_variant(P, P, 8, 4, 32, 2, P, 50, 8, 9, N, P, N) == 3
     # select with flags: unknown flag bits, group size not dividing hq, R NULL
     assert L.sws_select_topk_flags(P, 8, 4, P, 1, 16, 16, 20, 8, 16, P, P, N) == 2
     assert L.sws_select_topk_flags(P, 8, 3, P, 1, 16, 16, 20, 4, 16, P, P, N) == 2

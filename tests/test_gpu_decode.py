@@ -253,3 +253,43 @@ def test_decode_group_shared_selection():
                 wgt = np.exp(z - z.max())
                 o_want = (wgt @ H["v"][keys, g]) / wgt.sum()
                 assert np.abs(f64(out[s, h]) - o_want).max() <= TOL_ATTN_BF16, (s, h)
+
+
+@pytest.mark.parametrize("mode,s", [(sws.WALK_POWER, 8), (sws.WALK_SOFTMAX, 8), (sws.WALK_POWER, 3)])
+def test_decode_walk_variants(mode, s):
+    """Decode row walk of the variants against the oracle's row form, two
+    layers carried, for sequences whose open block is partial and full."""
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=4, hkv=2, k=32)
+    B, kd, hq, hkv = cfg.B, cfg.k, cfg.hq, cfg.hkv
+    grp = hq // hkv
+    name = {sws.WALK_POWER: "power", sws.WALK_SOFTMAX: "softmax"}[mode]
+    lens = (530, 640)                      # open block partial / just completed
+    ns = len(lens)
+    b_max = -(-max(lens) // B)
+    signs, cols = gen.hadamard_tables(cfg.d, kd)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    cur = torch.tensor([(n - 1) // B for n in lens], dtype=torch.int32, device="cuda")
+    r_prev = None
+    for l in range(2):
+        qsk = torch.zeros((ns, hq, b_max, kd), dtype=torch.float32, device="cuda")
+        ksk = torch.zeros((ns, hkv, b_max, kd), dtype=torch.float32, device="cuda")
+        for si, n in enumerate(lens):
+            geo = sws.Geometry([n], B)
+            sws.sketch(gen.seq_tensor(cfg, l, si, "q", n, "cuda"), geo, kd, sd, cd, out=qsk[si],
+                       ld_head=b_max * kd)
+            sws.sketch(gen.seq_tensor(cfg, l, si, "k", n, "cuda"), geo, kd, sd, cd, out=ksk[si],
+                       ld_head=b_max * kd)
+        r = torch.zeros((ns, hq, b_max), dtype=torch.float32, device="cuda")
+        sws.walk_update_row(qsk, ksk, cur, s, r_prev, r, mode=mode)
+        torch.cuda.synchronize()
+        for si, n in enumerate(lens):
+            c = (n - 1) // B
+            for h in range(hq):
+                M = O.sketched_scores(f64(qsk[si, h, :c + 1]), f64(ksk[si, h // grp, :c + 1]))
+                rp = None if r_prev is None else f64(r_prev[si, h, :c + 1])
+                want = O.walk_row_variant(rp, M, c, s, name)
+                got = f64(r[si, h])
+                assert np.all(got[c + 1:] == 0)
+                e = rowwise_rel_err(got[:c + 1], want)
+                assert e <= 1e-4, (name, s, l, si, h, e)
+        r_prev = r

@@ -169,3 +169,48 @@ def test_selection_variants(row_tau, group):
                     ow, _ = res[i]
                     err = np.abs(o[i * cfg.B:i * cfg.B + ow.shape[0]] - ow).max()
                     assert err <= TOL_ATTN_BF16, (row_tau, group, l, s, h, i, err)
+
+
+@pytest.mark.parametrize("mode,s,layers", [(sws.WALK_POWER, 8, 2), (sws.WALK_POWER, 3, 1),
+                                           (sws.WALK_SOFTMAX, 8, 2), (sws.WALK_SOFTMAX, 1, 1)])
+def test_walk_variants(mode, s, layers):
+    """The walk variants (elementwise power, softmax transition probabilities)
+    against the oracle on the GPU's own sketches and previous walk state,
+    ragged batch with a partial and a one-token sequence, then selection on the
+    variant's state is bit-exact."""
+    cfg = gen.CONFIGS["C2"].with_(d=128, B=64, hq=4, hkv=2, k=32)
+    seqlens = (700, 129, 1)
+    geo = sws.Geometry(list(seqlens), cfg.B)
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    grp = cfg.hq // cfg.hkv
+    name = {sws.WALK_POWER: "power", sws.WALK_SOFTMAX: "softmax"}[mode]
+    R = None
+    for l in range(layers):
+        q, k, v, _ = gen.layer_inputs(cfg, l, device="cuda", seqlens=list(seqlens))
+        q_sk = sws.sketch(q, geo, cfg.k, sd, cd)
+        k_sk = sws.sketch(k, geo, cfg.k, sd, cd)
+        R_prev = None if R is None else R.clone()
+        R = sws.walk_update_variant(q_sk, k_sk, geo, s, mode, R_prev)
+        idx, cnt = sws.select_topk(R, cfg.hq, geo, 30)
+        torch.cuda.synchronize()
+        qs, ks, Rh = f64(q_sk), f64(k_sk), R.cpu().numpy()
+        Rp = None if R_prev is None else R_prev.cpu().numpy()
+        idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+        worst = 0.0
+        for si in range(len(seqlens)):
+            b = geo.blocks[si]
+            bs = slice(int(geo.cu_blocks_host[si]), int(geo.cu_blocks_host[si]) + b)
+            off = geo.walk_offset(si, cfg.hq)
+            for h in range(cfg.hq):
+                M = O.sketched_scores(qs[h, bs], ks[h // grp, bs])
+                prev = None if Rp is None else np.tril(Rp[off + h * b * b: off + (h + 1) * b * b].reshape(b, b))
+                want = O.walk_update_variant(prev, M, s, name)
+                got = Rh[off + h * b * b: off + (h + 1) * b * b].reshape(b, b).astype(np.float64)
+                e = float((np.abs(got - want).max(axis=1) / np.maximum(np.abs(want).max(axis=1), 1e-300)).max())
+                worst = max(worst, e)
+                assert e <= 1e-4, (name, s, l, si, h, e)
+                lists = O.select(got, 30)
+                for i in range(b):
+                    assert idx_h[h, bs.start + i, :cnt_h[h, bs.start + i]].tolist() == lists[i].tolist()
+        _print("walk variant", name, s, "layer", l, "worst", worst)

@@ -1,5 +1,6 @@
 """Pins for the oracle's walk state (blog page section 4)."""
 import itertools
+import math
 import json
 import os
 
@@ -124,3 +125,47 @@ def test_planted_two_hop_chain_reached_by_walk():
     assert i > j > m
     assert R[i, j] > np.median(R[i, :i])
     assert R[i, m] > np.median(R[i, :i])
+
+
+def test_variant_transitions_hand_case():
+    """Walk variants: the transition matrices of a 3-block example worked out
+    by hand."""
+    M = np.array([[2.0, 9.0, 9.0],
+                  [1.0, -1.0, 9.0],
+                  [0.5, 0.0, -2.0]])
+    Tp = O.transition(M, "power", 3)
+    assert np.allclose(Tp, [[8.0, 0, 0], [1.0, -1.0, 0], [0.125, 0.0, -8.0]], rtol=0, atol=0)
+    Ts = O.transition(M, "softmax", 8)
+    e = math.e
+    assert np.allclose(Ts[0], [1.0, 0, 0])
+    assert np.allclose(Ts[1], [e / (e + 1 / e), (1 / e) / (e + 1 / e), 0])
+    den = math.exp(0.5) + 1.0 + math.exp(-2.0)
+    assert np.allclose(Ts[2], [math.exp(0.5) / den, 1.0 / den, math.exp(-2.0) / den])
+
+
+def test_variant_walks_reduce_to_closed_forms():
+    rng = np.random.default_rng(11)
+    b = 7
+    M = np.tril(rng.standard_normal((b, b)))
+    # power with s = 1 is the one-hop walk of the default reading
+    assert np.allclose(O.walk_update_variant(None, M, 1, "power"), O.walk_update(None, M, 1))
+    # power: one product with the elementwise power, from any previous state
+    Rp = np.tril(rng.standard_normal((b, b)))
+    want = O.rownorm(Rp @ np.tril(M ** 4))
+    assert np.allclose(O.walk_update_variant(Rp, M, 4, "power"), want)
+    # softmax: rows of T are probability vectors on the causal prefix
+    T = O.transition(M, "softmax", 1)
+    assert np.allclose(T.sum(axis=1), 1.0) and np.all(np.triu(T, 1) == 0) and np.all(T >= 0)
+    # softmax, s hops from the identity: the rows of T^s, row-normalised
+    R = O.walk_update_variant(None, M, 3, "softmax")
+    assert np.allclose(R, O.rownorm(T @ T @ T))
+    # s hops as single-step products: entries are sums over causal paths
+    i, m = 5, 1
+    paths = sum(T[i, j1] * T[j1, j2] * T[j2, m] for j1 in range(b) for j2 in range(b))
+    assert np.isclose((T @ T @ T)[i, m], paths)
+    # the row form equals the matrix row
+    for mode, s in (("power", 8), ("softmax", 8)):
+        full = O.walk_update_variant(Rp, M, s, mode)
+        assert np.allclose(O.walk_row_variant(Rp[4], M, 4, s, mode), full[4])
+        full0 = O.walk_update_variant(None, M, s, mode)
+        assert np.allclose(O.walk_row_variant(None, M, 6, s, mode), full0[6])
