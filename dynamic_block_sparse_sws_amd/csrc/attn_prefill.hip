@@ -112,6 +112,15 @@ __device__ __forceinline__ int row_swizzle(int row) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// max(v, v of the lane 32 away): v_permlane32_swap exchanges the two halves
+// of the wave in registers (no LDS round trip); the larger of the swapped pair
+// is the answer in either half.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 // Softmax reference lag: the running maximum used for the exponentials is
 // only raised when a new score exceeds it by more than this many powers of
 // two, so most steps skip the rescale of the output accumulators.  The
@@ -164,7 +173,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
   for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_halves(mx);
   const float m_cand = mx * scale_log2;
   if (__any(m_cand > m_run + kMaxLag)) {
     const float m_new = fmaxf(m_run, m_cand);
