@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the paged / fp8 KV decode-attention timings")
     ap.add_argument("--sweep", action="store_true", help="also time rho = 10, 30, 100")
     ap.add_argument("--diag", action="store_true",
                     help="parameter sweep (s, k, B, rho) and selection-quality diagnostics")
@@ -311,6 +313,73 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         "per_head_blocks": cfg.rho * (b_max - 1) // 100 + 1,
         "setup_s": setup_s,
     }
+    if not args.no_serving:
+        res["serving_layouts"] = serving_layouts(torch, sws, gen, state[-1], ubufs, ctx_len[-1],
+                                                 B, steps - 1)
+    return res
+
+
+def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, reps=20):
+    """Decode attention of one sparse layer at the last decode step on the
+    same union lists, over the contiguous cache, a paged copy (pages of one
+    block in a random order) and an fp8 e4m3 paged copy (per-tensor scales),
+    sparse and dense.  Bytes are the KV rows the lists name (K and V) plus
+    q and out; GB/s is those bytes over the average call time."""
+    kc, vc = st["kc"], st["vc"]
+    ns, max_ctx, hkv, d = kc.shape
+    q = st["qst"][t]
+    hq = q.shape[1]
+    nb = -(-max_ctx // B)
+    table, num_pages = gen.page_table([max_ctx] * ns, B, spare_pages=0)
+    tab = torch.from_numpy(table).cuda()
+    dst = tab.reshape(-1).long()
+
+    def to_pages(x):
+        pad = nb * B - max_ctx
+        xp = torch.nn.functional.pad(x, (0, 0, 0, 0, 0, pad)) if pad else x
+        pages = torch.empty((num_pages, B, hkv, d), dtype=x.dtype, device=x.device)
+        pages[dst] = xp.reshape(ns * nb, B, hkv, d)
+        return pages
+
+    kp, vp = to_pages(kc), to_pages(vc)
+    ksc = float(kc.float().abs().amax()) / 448.0
+    vsc = float(vc.float().abs().amax()) / 448.0
+    kp8 = gen.to_fp8_e4m3(kp, ksc).view(torch.float8_e4m3fn)
+    vp8 = gen.to_fp8_e4m3(vp, vsc).view(torch.float8_e4m3fn)
+    uidx, ucnt, umask = ubufs[0], ubufs[1], ubufs[2]
+    ws = torch.empty(sws.decode_workspace_size(ns, hq, hkv, d, B, nb), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+    union_rows = int(ucnt.long().sum().item()) * B
+    dense_rows = int(ctx.long().sum().item()) * hkv
+    qo = ns * hq * d * 2 * 2
+    runs = {
+        "contiguous_bf16": (lambda u: sws.sparse_attn_decode(q, kc, vc, ctx, B, *u, out=out,
+                                                             ws=ws), 2),
+        "paged_bf16": (lambda u: sws.sparse_attn_decode_paged(q, kp, vp, tab, ctx, *u, out=out,
+                                                              ws=ws), 2),
+        "paged_fp8": (lambda u: sws.sparse_attn_decode_paged(q, kp8, vp8, tab, ctx, *u,
+                                                             k_scale=ksc, v_scale=vsc, out=out,
+                                                             ws=ws), 1),
+    }
+    res = {"batch": ns, "context": int(ctx[0]), "reps": reps}
+    for mode, u, rows in (("sparse", (uidx, ucnt, umask), union_rows),
+                          ("dense", (None, None, None), dense_rows)):
+        for name, (fn, eb) in runs.items():
+            fn(u)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn(u)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            nbytes = rows * d * eb * 2 + qo
+            res[f"{mode}_{name}_us"] = round(us, 2)
+            res[f"{mode}_{name}_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del kp, vp, kp8, vp8
     return res
 
 

@@ -16,15 +16,18 @@ import numpy as np
 import torch
 
 __all__ = [
-    "SwsError", "lib", "F32", "BF16", "WALK_DEFAULT", "WALK_POWER", "WALK_SOFTMAX", "SELECT_DENSE", "SELECT_ROW_TAU", "SELECT_GROUP", "Geometry", "geometry", "walk_state_numel",
+    "SwsError", "lib", "F32", "BF16", "FP8_E4M3", "WALK_DEFAULT", "WALK_POWER", "WALK_SOFTMAX",
+    "SELECT_DENSE", "SELECT_ROW_TAU", "SELECT_GROUP", "Geometry", "geometry", "walk_state_numel",
     "sketch", "sketch_append", "walk_update", "walk_update_row", "walk_update_variant",
     "walk_variant_workspace_size", "select_topk",
     "select_topk_row", "sparse_attn_prefill", "sparse_attn_decode", "decode_workspace_size",
+    "sparse_attn_decode_paged",
     "prefill_layer", "EXPORTED_SYMBOLS", "version",
 ]
 
 F32 = 0
 BF16 = 1
+FP8_E4M3 = 2   # KV pages only
 
 # walk modes and selection flags (include/sws.h)
 WALK_DEFAULT = 0
@@ -43,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "sws_select_topk_row", "sws_sparse_attn_prefill", "sws_sparse_attn_decode",
     "sws_decode_workspace_size", "sws_prefill_workspace_size", "sws_select_topk_flags",
     "sws_walk_update_variant", "sws_walk_variant_workspace_size", "sws_walk_update_row_variant",
+    "sws_sparse_attn_decode_paged",
 )
 
 
@@ -87,6 +91,9 @@ _SIGS = {
     "sws_sparse_attn_decode": ([_P, _P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                 _P, _I, _F, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "sws_decode_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "sws_sparse_attn_decode_paged": ([_P, _P, _P, ctypes.c_int, _F, _F, _P, _I, _I, _P, _I, _I,
+                                      _I, _I, _I, _P, _P, _P, _I, _F, _P, _P, _P, _SZ, _P],
+                                     ctypes.c_int),
 }
 
 
@@ -368,6 +375,42 @@ def sparse_attn_decode(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cn
     _check("sws_sparse_attn_decode", lib().sws_sparse_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(ctx_len), n_seqs, max_ctx, hq,
         hkv, d, B, _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
+        _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def sparse_attn_decode_paged(q, k_pages, v_pages, block_table, ctx_len, union_idx, union_cnt,
+                             union_mask, k_scale: float = 1.0, v_scale: float = 1.0,
+                             scale: Optional[float] = None, out=None, lse=None, ws=None,
+                             stream=None):
+    """Decode attention over a paged cache: k_pages / v_pages [num_pages][B][hkv][d] in bf16
+    or torch.float8_e4m3fn (value = code * k_scale / v_scale), block_table [n_seqs][width]
+    int32 pages of each sequence's logical blocks; q and out bf16."""
+    n_seqs, hq, d = q.shape
+    num_pages, B, hkv, _ = k_pages.shape
+    width = block_table.shape[1]
+    if k_pages.dtype == torch.bfloat16:
+        kv = BF16
+    elif k_pages.dtype == torch.float8_e4m3fn:
+        kv = FP8_E4M3
+    else:
+        raise TypeError(f"KV pages must be bf16 or float8_e4m3fn, not {k_pages.dtype}")
+    if v_pages.dtype != k_pages.dtype or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages differ in dtype or shape")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bf16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    uw = union_idx.shape[2] if union_idx is not None else width
+    if ws is None:
+        ws = torch.empty(max(1, decode_workspace_size(n_seqs, hq, hkv, d, B, uw)),
+                         dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("sws_sparse_attn_decode_paged", lib().sws_sparse_attn_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), kv, float(k_scale), float(v_scale),
+        _ptr(block_table), width, num_pages, _ptr(ctx_len), n_seqs, hq, hkv, d, B,
+        _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
 

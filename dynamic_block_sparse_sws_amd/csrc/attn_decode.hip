@@ -13,6 +13,7 @@
 #include "sws_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sws {
 namespace {
@@ -21,6 +22,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
+// fp8 rows are 8 bytes a lane: twice the rows per batch keeps the same bytes
+// in flight per wave as bf16 (the loop is latency-bound below that).
+template <typename TK> constexpr int dec_unroll() { return sizeof(TK) == 1 ? 2 * kDecUnroll : kDecUnroll; }
 
 // Sum over the TPL consecutive lanes that share a token row (TPL in {8, 16}),
 // with DPP lane permutes: swap neighbours, swap pairs, mirror within 8, mirror
@@ -59,6 +63,22 @@ template <> struct Row8<float> {
   }
 };
 
+// fp8 rows (OCP e4m3, 8 bytes per lane), decoded with v_cvt_pk_f32_fp8; the
+// per-tensor scales are applied by the caller (K's to the score, V's to the
+// partial output).
+template <> struct Row8<uint8_t> {
+  uint2 r;
+  __device__ __forceinline__ void load(const uint8_t* p) { r = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void get(float* o) const {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, true);
+    o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+    o[4] = c[0]; o[5] = c[1]; o[6] = d[0]; o[7] = d[1];
+  }
+};
+
 // A query head's 8 features of this lane, and its dot product with a K row:
 // bf16 pairs through v_dot2_f32_bf16 (exact products, fp32 sums), fp32 with
 // plain fused multiply-adds.
@@ -94,6 +114,31 @@ template <> struct QVec<float> {
 #pragma unroll
     for (int x = 0; x < 8; ++x) a += v[x] * kf[x];
     return a;
+  }
+};
+
+// bf16 query against fp8 keys: the codes widened to bf16 (exact: e4m3 is a
+// subset of bf16) and multiplied with v_dot2_f32_bf16 like bf16 keys; the K
+// scale is applied to the score.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+struct QVecF8 {
+  uint4 r;
+  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { r = make_uint4(0u, 0u, 0u, 0u); }
+  template <bool HI> __device__ __forceinline__ static bf16x2_t pair(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    return __builtin_convertvector((f32x2_t){f[0], f[1]}, bf16x2_t);
+  }
+  __device__ __forceinline__ float dot(const Row8<uint8_t>& k) const {
+    float a = __builtin_amdgcn_fdot2_f32_bf16(pair<false>(k.r.x),
+                                              __builtin_bit_cast(bf16x2_t, r.x), 0.f, false);
+    float b = __builtin_amdgcn_fdot2_f32_bf16(pair<true>(k.r.x),
+                                              __builtin_bit_cast(bf16x2_t, r.y), 0.f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(pair<false>(k.r.y), __builtin_bit_cast(bf16x2_t, r.z), a,
+                                        false);
+    b = __builtin_amdgcn_fdot2_f32_bf16(pair<true>(k.r.y), __builtin_bit_cast(bf16x2_t, r.w), b,
+                                        false);
+    return a + b;
   }
 };
 
@@ -251,13 +296,19 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
 // each row group of the wave keeps its own online-softmax state (max, sum,
 // weighted V sum) for up to four query heads at a time.  Row groups merge
 // through lane exchanges, waves through LDS.
-template <typename T, int D, int BLK, int GMAX, int UNR>
+// KV addressing: contiguous caches [n_seqs][max_ctx][hkv][d] (table == null),
+// or pages of BLK tokens [num_pages][BLK][hkv][d] with table[seq][logical
+// block] giving the page.  TK is the cache element type (bf16, fp32, or fp8
+// e4m3 codes with per-tensor scales kscale / vscale).
+template <typename T, int D, int BLK, int GMAX, int UNR, typename TK = T>
 __device__ __forceinline__ void decode_range(
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, int max_ctx, int hq, int hkv,
     const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth, int p,
     int a, int b, int r, float scale_log2, float* __restrict__ ws_ml,
-    float* __restrict__ ws_acc) {
+    float* __restrict__ ws_acc, const int32_t* __restrict__ table = nullptr, int table_width = 0,
+    int num_pages = 0, float kscale = 1.0f, float vscale = 1.0f) {
+  using QV = typename std::conditional<std::is_same<TK, uint8_t>::value, QVecF8, QVec<T>>::type;
   constexpr int TPL = D / 8;                   // lanes per token row
   constexpr int RPW = 64 / TPL;                // token rows per wave-wide load
   constexpr int TPB = RPW * UNR;               // tokens per wave batch
@@ -270,20 +321,24 @@ __device__ __forceinline__ void decode_range(
   const int seq = p / hkv;
   const int g = p % hkv;
   const int G = hq / hkv;
-  const int ctx = ctx_len[seq];
+  const int ctx = max(ctx_len[seq], 1);   // at least the new token
+  const float sl2 = scale_log2 * kscale;
+  const int last_blk = (ctx - 1) / BLK;
   const int ntok = (b - a) * BLK;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ch = lane % TPL;           // feature chunk (8 features)
   const int slot = lane / TPL;         // row group of the wave
   const int64_t rstride = (int64_t)hkv * D;
-  const T* kb = kc + ((int64_t)seq * max_ctx) * rstride + (int64_t)g * D + ch * 8;
-  const T* vb = vc + ((int64_t)seq * max_ctx) * rstride + (int64_t)g * D + ch * 8;
+  const int64_t seq_off = table ? 0 : ((int64_t)seq * max_ctx) * rstride;
+  const TK* kb = kc + seq_off + (int64_t)g * D + ch * 8;
+  const TK* vb = vc + seq_off + (int64_t)g * D + ch * 8;
+  const int32_t* trow = table ? table + (int64_t)seq * table_width : nullptr;
   const int32_t* ul = uidx ? uidx + (int64_t)p * uwidth : nullptr;
   const uint32_t* um = umask ? umask + (int64_t)p * uwidth : nullptr;
 
   for (int h0 = 0; h0 < G; h0 += HC) {
-    QVec<T> qv[HC];
+    QV qv[HC];
     float acc[HC][8], m[HC], l[HC];
 #pragma unroll
     for (int hh = 0; hh < HC; ++hh) {
@@ -296,13 +351,23 @@ __device__ __forceinline__ void decode_range(
     }
     for (int tb = wave * TPB; tb < ntok; tb += NWV * TPB) {
       const int e = a + tb / BLK;
-      const int blk = ul ? ul[e] : e;
+      // list entries are blocks of the context; a stray one is clamped so every
+      // access stays inside this sequence's rows
+      const int blk = min(max(ul ? ul[e] : e, 0), last_blk);
       const uint32_t mk = um ? um[e] : 0xffffffffu;
       const int r0 = blk * BLK + tb % BLK + slot;      // this lane's first cache row
-      Row8<T> kr[UNR], vr[UNR];
+      // Paged: the batch lies in one logical block, so one page; out-of-range
+      // table entries are clamped (the caller's error, never a stray access).
+      int64_t pbase = 0;
+      if (trow) {
+        const int pg = min(max(trow[min(blk, table_width - 1)], 0), num_pages - 1);
+        pbase = ((int64_t)pg - blk) * BLK;
+      }
+      Row8<TK> kr[UNR], vr[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int64_t row = min(r0 + u * RPW, ctx - 1);  // rows past ctx are masked below
+        // rows past ctx are masked below (the clamped row is in the same block)
+        const int64_t row = pbase + min(r0 + u * RPW, ctx - 1);
         kr[u].load(kb + row * rstride);
         vr[u].load(vb + row * rstride);
       }
@@ -313,7 +378,7 @@ __device__ __forceinline__ void decode_range(
 #pragma unroll
         for (int hh = 0; hh < HC; ++hh) {
           const float part = token_sum<TPL>(qv[hh].dot(kr[u]));
-          sc[u][hh] = (ok && ((mk >> (h0 + hh)) & 1u)) ? part * scale_log2 : -INFINITY;
+          sc[u][hh] = (ok && ((mk >> (h0 + hh)) & 1u)) ? part * sl2 : -INFINITY;
         }
       }
 #pragma unroll
@@ -387,7 +452,7 @@ __device__ __forceinline__ void decode_range(
         A += f * wacc[w][hh][dd];
       }
       const int64_t row = (int64_t)r * G + h0 + hh;
-      ws_acc[row * D + dd] = A;
+      ws_acc[row * D + dd] = A * vscale;
       if (dd == 0) {
         ws_ml[row * 2 + 0] = M;
         ws_ml[row * 2 + 1] = L;
@@ -399,12 +464,14 @@ __device__ __forceinline__ void decode_range(
 
 // Split kernel: workgroup w reads blocks [w W / NWG, (w + 1) W / NWG) of the
 // concatenated pair lists, one record per pair the range touches.
-template <typename T, int D, int BLK, int GMAX, int UNR>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+template <typename T, int D, int BLK, int GMAX, int UNR, typename TK>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(
+    const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
     const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth,
-    float scale_log2, void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+    float scale_log2, void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    const int32_t* __restrict__ table, int table_width, int num_pages, float kscale,
+    float vscale) {
   const int P = n_seqs * hkv;
   const DecPlan pl = plan_of(ws, P);
   const int nwg = *pl.nwg;
@@ -422,8 +489,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int b = (int)(min(hi, (int64_t)Bn) - A);
     if (a >= b) continue;
     const int r = pl.rec[p] + (w - wg_of_block(A, W, nwg));
-    decode_range<T, D, BLK, GMAX, UNR>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask, uwidth,
-                                       p, a, b, r, scale_log2, ws_ml, ws_acc);
+    decode_range<T, D, BLK, GMAX, UNR, TK>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask,
+                                           uwidth, p, a, b, r, scale_log2, ws_ml, ws_acc, table,
+                                           table_width, num_pages, kscale, vscale);
   }
 }
 
@@ -516,12 +584,13 @@ int split_workgroups() {
   return cached[dev];
 }
 
-template <typename T, int D, int BLK, int GMAX>
+template <typename T, int D, int BLK, int GMAX, typename TK>
 hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* ctx_len, int n_seqs, int max_ctx, int hq, int hkv,
                       const int32_t* uidx, const int32_t* ucnt, const uint32_t* umask,
                       int uwidth, float scale, void* out, float* lse, void* ws,
-                      hipStream_t st) {
+                      hipStream_t st, const int32_t* table, int table_width, int num_pages,
+                      float kscale, float vscale) {
   const int P = n_seqs * hkv;
   const int G = hq / hkv;
   const int nwg = split_workgroups();
@@ -531,11 +600,11 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
                      uidx ? ucnt : nullptr, n_seqs, hkv, nwg, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, kDecUnroll>), dim3(nwg),
+  hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, dec_unroll<TK>(), TK>), dim3(nwg),
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
-                     static_cast<const T*>(k_cache), static_cast<const T*>(v_cache), ctx_len,
+                     static_cast<const TK*>(k_cache), static_cast<const TK*>(v_cache), ctx_len,
                      max_ctx, n_seqs, hq, hkv, uidx, umask, uwidth, scale * kLog2e, ws, ws_ml,
-                     ws_acc);
+                     ws_acc, table, table_width, num_pages, kscale, vscale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(hq, n_seqs), dim3(D), 0, st, n_seqs,
@@ -543,23 +612,23 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
   return hipGetLastError();
 }
 
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, typename TK = T>
 hipError_t pick_g(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* ctx_len, int n_seqs, int max_ctx, int hq, int hkv,
                   const int32_t* uidx, const int32_t* ucnt, const uint32_t* umask, int uwidth,
-                  float scale, void* out, float* lse, void* ws, hipStream_t st) {
+                  float scale, void* out, float* lse, void* ws, hipStream_t st,
+                  const int32_t* table = nullptr, int table_width = 0, int num_pages = 0,
+                  float kscale = 1.0f, float vscale = 1.0f) {
   const int G = hq / hkv;
-  if (G <= 1)
-    return run_decode<T, D, BLK, 1>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv, uidx,
-                                    ucnt, umask, uwidth, scale, out, lse, ws, st);
-  if (G <= 4)
-    return run_decode<T, D, BLK, 4>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv, uidx,
-                                    ucnt, umask, uwidth, scale, out, lse, ws, st);
-  if (G <= 8)
-    return run_decode<T, D, BLK, 8>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv, uidx,
-                                    ucnt, umask, uwidth, scale, out, lse, ws, st);
-  return run_decode<T, D, BLK, 16>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv, uidx,
-                                   ucnt, umask, uwidth, scale, out, lse, ws, st);
+#define SWS_RUN(GM)                                                                            \
+  return run_decode<T, D, BLK, GM, TK>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv,  \
+                                       uidx, ucnt, umask, uwidth, scale, out, lse, ws, st,     \
+                                       table, table_width, num_pages, kscale, vscale)
+  if (G <= 1) SWS_RUN(1);
+  if (G <= 4) SWS_RUN(4);
+  if (G <= 8) SWS_RUN(8);
+  SWS_RUN(16);
+#undef SWS_RUN
 }
 
 }  // namespace
@@ -592,6 +661,32 @@ hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_
   if (d == 128 && B == 128) SWS_DEC(float, 128, 128);
   if (d == 64 && B == 64) SWS_DEC(float, 64, 64);
   SWS_DEC(float, 64, 128);
+#undef SWS_DEC
+}
+
+hipError_t launch_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                    int kv_dtype, float k_scale, float v_scale,
+                                    const int32_t* block_table, int table_width,
+                                    int num_pages, const int32_t* ctx_len, int n_seqs, int hq, int hkv, int d,
+                                    int B, const int32_t* union_idx, const int32_t* union_cnt,
+                                    const uint32_t* union_mask, int union_width, float scale,
+                                    void* out, float* lse, void* ws, hipStream_t st) {
+  if (n_seqs == 0) return hipSuccess;
+#define SWS_DEC(TK, D, BLK)                                                                    \
+  return pick_g<uint16_t, D, BLK, TK>(q, k_pages, v_pages, ctx_len, n_seqs, 0, hq, hkv,       \
+                                      union_idx, union_cnt, union_mask, union_width, scale,   \
+                                      out, lse, ws, st, block_table, table_width, num_pages,  \
+                                      k_scale, v_scale)
+  if (kv_dtype == SWS_FP8_E4M3) {
+    if (d == 128 && B == 64) SWS_DEC(uint8_t, 128, 64);
+    if (d == 128 && B == 128) SWS_DEC(uint8_t, 128, 128);
+    if (d == 64 && B == 64) SWS_DEC(uint8_t, 64, 64);
+    SWS_DEC(uint8_t, 64, 128);
+  }
+  if (d == 128 && B == 64) SWS_DEC(uint16_t, 128, 64);
+  if (d == 128 && B == 128) SWS_DEC(uint16_t, 128, 128);
+  if (d == 64 && B == 64) SWS_DEC(uint16_t, 64, 64);
+  SWS_DEC(uint16_t, 64, 128);
 #undef SWS_DEC
 }
 

@@ -386,4 +386,53 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
                   fn);
 }
 
+int sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                 int kv_dtype, float k_scale, float v_scale,
+                                 const int32_t* block_table, int32_t table_width,
+                                 int32_t num_pages, const int32_t* ctx_len, int32_t n_seqs,
+                                 int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                 const int32_t* union_idx, const int32_t* union_cnt,
+                                 const uint32_t* union_mask, int32_t union_width, float scale,
+                                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sws_sparse_attn_decode_paged";
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_pages);
+  REQUIRE_PTR(v_pages);
+  REQUIRE_PTR(block_table);
+  REQUIRE_PTR(ctx_len);
+  REQUIRE_PTR(out);
+  if (union_idx && (!union_cnt || !union_mask))
+    return fail(SWS_ERR_NULL, "%s: union_idx given without union_cnt / union_mask", fn);
+  if (kv_dtype != SWS_BF16 && kv_dtype != SWS_FP8_E4M3)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: kv_dtype %d", fn, kv_dtype);
+  if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
+  if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
+  if (hq / hkv > 16) return fail(SWS_ERR_UNSUPPORTED, "%s: hq/hkv=%d > 16", fn, hq / hkv);
+  if (n_seqs < 0 || table_width < 1 || num_pages < 1)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d table_width=%d num_pages=%d", fn, n_seqs,
+                table_width, num_pages);
+  const int uw = union_idx ? union_width : table_width;
+  if (union_idx && union_width < 1) return fail(SWS_ERR_SHAPE, "%s: union_width=%d", fn, union_width);
+  if ((int64_t)n_seqs * hkv > 8192)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: n_seqs * hkv = %lld > 8192", fn,
+                (long long)n_seqs * hkv);
+  if ((int64_t)n_seqs * hkv * uw > 0x7fffffffLL)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs * hkv * union_width exceeds 2^31", fn);
+  if (!std::isfinite(scale)) return fail(SWS_ERR_SHAPE, "%s: scale is not finite", fn);
+  if (kv_dtype == SWS_FP8_E4M3 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(SWS_ERR_SHAPE, "%s: k_scale / v_scale not finite", fn);
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages))
+    return fail(SWS_ERR_SHAPE, "%s: q/k_pages/v_pages must be 16-byte aligned", fn);
+  const size_t need = sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, uw);
+  if (!ws || ws_bytes < need)
+    return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+  return launched(sws::launch_attn_decode_paged(
+                      q, k_pages, v_pages, kv_dtype, k_scale, v_scale, block_table, table_width,
+                      num_pages, ctx_len, n_seqs, hq, hkv, d, B, union_idx, union_cnt,
+                      union_mask, uw, scale, out, lse, ws, (hipStream_t)stream),
+                  fn);
+}
+
 }  // extern "C"

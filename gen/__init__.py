@@ -16,4 +16,6 @@ from .synth import (  # noqa: F401
     seed_for,
     ragged_lengths,
     cu_offsets,
+    page_table,
+    to_fp8_e4m3,
 )

@@ -250,3 +250,35 @@ def decode_layer_inputs(cfg: Config, layer: int, device="cpu", n_seqs=None, pref
         kc[si] = seq_tensor(cfg, layer, si, "k", total, dev)
         vc[si] = seq_tensor(cfg, layer, si, "v", total, dev)
     return qpre, qst, kc, vc
+
+
+def page_table(ctx_lens, B: int, spare_pages: int = 3, share_prefix_blocks: int = 0,
+               seed_parts=(9,)):
+    """A paged-KV layout for sequences of `ctx_lens` tokens with pages of B
+    tokens: a seeded random page for every logical block, `spare_pages` pages
+    that no sequence uses, and, when share_prefix_blocks > 0, sequence 1
+    reusing sequence 0's first pages (a shared prompt prefix).  Returns
+    (table [n_seqs][width] int32, num_pages); unused entries hold -1."""
+    rng = np.random.default_rng(seed_for(_TENSOR_ID["tables"], *seed_parts))
+    nb = [-(-int(n) // B) for n in ctx_lens]
+    width = max(nb)
+    shared = min(share_prefix_blocks, nb[0], nb[1] if len(nb) > 1 else 0)
+    need = sum(nb) - (shared if len(nb) > 1 else 0)
+    num_pages = need + spare_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((len(nb), width), -1, dtype=np.int32)
+    nxt = 0
+    for s, n in enumerate(nb):
+        for j in range(n):
+            if s == 1 and j < shared:
+                table[1, j] = table[0, j]
+            else:
+                table[s, j] = perm[nxt]
+                nxt += 1
+    return table, num_pages
+
+
+def to_fp8_e4m3(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """Store x as OCP fp8 e4m3 codes of x / scale (torch's round-to-nearest
+    cast), returned as raw bytes (uint8)."""
+    return (x.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)

@@ -52,7 +52,9 @@ typedef enum sws_status {
 
 typedef enum sws_dtype {
   SWS_F32 = 0,
-  SWS_BF16 = 1
+  SWS_BF16 = 1,
+  SWS_FP8_E4M3 = 2  /* KV pages only (sws_sparse_attn_decode_paged): OCP e4m3,
+                       value = code * per-tensor scale                        */
 } sws_dtype;
 
 /* Walk modes (sws_walk_update_variant, sws_walk_update_row_variant).  The
@@ -329,6 +331,41 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
  * and per-range partial softmax states; union_width does not change it). */
 size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
                                  int32_t union_width);
+
+/*
+ * sws_sparse_attn_decode_paged - sws_sparse_attn_decode over a paged KV cache,
+ * with bf16 or fp8 pages.  The deep-reading page lists paged KV caches,
+ * continuous batching and mixed precision among what a serving system adds
+ * around the method's kernels (section 11.4); this is that layout for the
+ * decode step of section 5.  The result is the one sws_sparse_attn_decode
+ * gives on the gathered (and, for fp8, dequantised) contiguous cache.
+ *
+ *   q            [n_seqs][hq][d] bf16
+ *   k_pages,     [num_pages][B][hkv][d], one page per KV block of B tokens,
+ *   v_pages      dtype kv_dtype: SWS_BF16, or SWS_FP8_E4M3 whose value is
+ *                code * k_scale (K) or code * v_scale (V); scales are
+ *                ignored for SWS_BF16
+ *   block_table  [n_seqs][table_width] int32: page of logical block j of
+ *                sequence s.  Sequences come and go between calls
+ *                (continuous batching) by rewriting their table rows; pages
+ *                may be shared.  The caller guarantees table_width * B >=
+ *                ctx_len[s] and 0 <= page < num_pages; entries out of range
+ *                are clamped on the device (a wrong result, never a stray
+ *                access).
+ *   ctx_len, union_idx / union_cnt / union_mask, scale, out, lse: as for
+ *                sws_sparse_attn_decode (out is bf16)
+ *   ws           workspace of sws_decode_workspace_size(n_seqs, hq, hkv, d,
+ *                B, union_width) bytes
+ *   Same size limits as sws_sparse_attn_decode; pages 16-byte aligned.
+ */
+int sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                 int kv_dtype, float k_scale, float v_scale,
+                                 const int32_t* block_table, int32_t table_width,
+                                 int32_t num_pages, const int32_t* ctx_len, int32_t n_seqs,
+                                 int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                 const int32_t* union_idx, const int32_t* union_cnt,
+                                 const uint32_t* union_mask, int32_t union_width, float scale,
+                                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,7 @@ __all__ = [
     "select_rows_tau", "group_scores", "transition", "walk_update_variant",
     "walk_row_variant", "sparse_attention",
     "sparse_attention_rows", "prefill_layer", "prefill", "decode_step", "SeqPrefill",
+    "fp8_e4m3_value", "gather_pages",
 ]
 
 
@@ -452,3 +453,28 @@ def decode_step(layers_prefix, signs, cols, B: int, s: int, rho: int, n_dense: i
                           "lse": zmax + math.log(w.sum())})
         out.append(heads)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Section 11.4 (serving integration): paged KV caches and low-precision KV
+# ---------------------------------------------------------------------------
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Value of OCP 8-bit floating-point E4M3 codes (OCP "8-bit Floating Point
+    Specification (OFP8)"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent field 0 is subnormal (m / 8 * 2^-6); S.1111.111 is NaN and
+    there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def gather_pages(pages, table_row, n: int, B: int) -> np.ndarray:
+    """The contiguous cache rows of one sequence of n tokens held in pages of B
+    tokens: token t lives in row t % B of page table_row[t // B]."""
+    pages = np.asarray(pages)
+    return np.stack([pages[int(table_row[t // B]), t % B] for t in range(n)])

@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     L = sws.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -121,5 +121,18 @@ def test_other_entry_points_validation():
                                     ctypes.c_float(0.1), P, N, N, need, N) == 4
     assert L.sws_sparse_attn_decode(P, P, P, 1, P, 16, 65792, 64, 2, 128, 64, P, P, P, 821,
                                     ctypes.c_float(0.1), P, N, P, 1 << 40, N) == 3
+    # paged decode: bad kv dtype, table NULL, table_width 0, workspace too small
+    need = L.sws_decode_workspace_size(16, 32, 8, 128, 64, 821)
+    f = ctypes.c_float
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 0, f(1), f(1), P, 1029, 4096, P, 16, 32, 8, 128,
+                                          64, P, P, P, 821, f(0.1), P, N, P, need, N) == 3
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 2, f(1), f(1), N, 1029, 4096, P, 16, 32, 8, 128,
+                                          64, P, P, P, 821, f(0.1), P, N, P, need, N) == 1
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 2, f(1), f(1), P, 0, 4096, P, 16, 32, 8, 128,
+                                          64, P, P, P, 821, f(0.1), P, N, P, need, N) == 2
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 1, f(1), f(1), P, 1029, 4096, P, 16, 32, 8, 128,
+                                          64, P, P, P, 821, f(0.1), P, N, P, need - 1, N) == 4
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 2, f(float("inf")), f(1), P, 1029, 4096, P, 16,
+                                          32, 8, 128, 64, P, P, P, 821, f(0.1), P, N, P, need, N) == 2
     # append: b_max 0
     assert L.sws_sketch_append(P, 1, P, 2, 8, 128, 64, 32, P, P, P, P, 0, N) == 2

@@ -293,3 +293,134 @@ def test_decode_walk_variants(mode, s):
                 e = rowwise_rel_err(got[:c + 1], want)
                 assert e <= 1e-4, (name, s, l, si, h, e)
         r_prev = r
+
+
+def _paged_inputs(cfg, lens, share, layer=0):
+    """Per-sequence K/V (sequence 1 reusing sequence 0's first `share` blocks
+    when share > 0), the new token's q, a contiguous cache and a page table."""
+    ns, B = len(lens), cfg.B
+    K, V, q = [], [], []
+    for s, n in enumerate(lens):
+        k = gen.seq_tensor(cfg, layer, s, "k", n, "cuda")
+        v = gen.seq_tensor(cfg, layer, s, "v", n, "cuda")
+        if s == 1 and share:
+            k[:share * B] = K[0][:share * B]
+            v[:share * B] = V[0][:share * B]
+        K.append(k)
+        V.append(v)
+        q.append(gen.seq_tensor(cfg, layer, s, "q", n, "cuda")[n - 1])
+    table, num_pages = gen.page_table(lens, B, share_prefix_blocks=share)
+    return K, V, torch.stack(q).contiguous(), table, num_pages
+
+
+def _fill_pages(X, table, num_pages, B, dtype, tail):
+    """Scatter per-sequence rows X[s] [n, hkv, d] into pages; rows past each
+    sequence's end and unused pages hold `tail` (NaN), which the kernel must
+    never read."""
+    hkv, d = X[0].shape[1:]
+    pages = torch.full((num_pages, B, hkv, d), tail, dtype=dtype, device="cuda")
+    for s, x in enumerate(X):
+        for j in range(-(-x.shape[0] // B)):
+            rows = x[j * B:(j + 1) * B]
+            pages[int(table[s, j]), :rows.shape[0]] = rows
+    return pages
+
+
+def _check_decode_rows(out, lse, qh, Kh, Vh, lens, lists, B, d, grp, tol):
+    for s, n in enumerate(lens):
+        for h in range(out.shape[1]):
+            g = h // grp
+            keys = np.concatenate([np.arange(j * B, min((j + 1) * B, n)) for j in lists(s, h)])
+            z = (Kh[s][keys, g] @ qh[s, h]) / math.sqrt(d)
+            zm = z.max()
+            w = np.exp(z - zm)
+            o_want = (w @ Vh[s][keys, g]) / w.sum()
+            e = float(np.abs(out[s, h] - o_want).max())
+            assert e <= tol, (s, h, e)
+            assert abs(lse[s, h] - (zm + math.log(w.sum()))) <= max(tol, 1e-4), (s, h)
+
+
+@pytest.mark.parametrize("d,B,hq,hkv,lens,share", [
+    (128, 64, 8, 2, (1000, 2049, 64), 7),
+    (64, 128, 4, 4, (700, 1, 1280), 0),
+    (128, 64, 16, 1, (333, 4100), 2),
+])
+def test_decode_paged_bf16(d, B, hq, hkv, lens, share):
+    """Paged bf16 cache (random page order, a shared prefix, NaN in every
+    unused row and page): the output and lse equal the contiguous kernel's bit
+    for bit, and the oracle's attention over the pages gathered by the table."""
+    cfg = gen.CONFIGS["C4"].with_(d=d, B=B, hq=hq, hkv=hkv)
+    ns, grp = len(lens), hq // hkv
+    _print("paged bf16", d, B, hq, hkv, lens, share)
+    K, V, q, table, num_pages = _paged_inputs(cfg, lens, share)
+    kp = _fill_pages(K, table, num_pages, B, torch.bfloat16, float("nan"))
+    vp = _fill_pages(V, table, num_pages, B, torch.bfloat16, float("nan"))
+    max_ctx = max(lens)
+    kc = torch.zeros((ns, max_ctx, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for s, n in enumerate(lens):
+        kc[s, :n] = K[s]
+        vc[s, :n] = V[s]
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cur = (ctx - 1) // B
+    b_max = -(-max_ctx // B)
+    gr = torch.Generator(device="cuda")
+    gr.manual_seed(gen.seed_for(11, d, B, hq))
+    r = torch.rand((ns, hq, b_max), generator=gr, device="cuda")
+    uidx, ucnt, umask, idx, cnt = sws.select_topk_row(r, hq, hkv, cur, b_max, 25, per_head=True)
+    tab = torch.from_numpy(table).cuda()
+    for sparse in (True, False):
+        u = (uidx, ucnt, umask) if sparse else (None, None, None)
+        lse_p = torch.empty((ns, hq), dtype=torch.float32, device="cuda")
+        lse_c = torch.empty_like(lse_p)
+        out_p = sws.sparse_attn_decode_paged(q, kp, vp, tab, ctx, *u, lse=lse_p)
+        out_c = sws.sparse_attn_decode(q, kc, vc, ctx, B, *u, lse=lse_c)
+        torch.cuda.synchronize()
+        assert torch.equal(out_p, out_c) and torch.equal(lse_p, lse_c), sparse
+        Kh = [O.gather_pages(f64(kp), table[s], n, B) for s, n in enumerate(lens)]
+        Vh = [O.gather_pages(f64(vp), table[s], n, B) for s, n in enumerate(lens)]
+        ih, ch = idx.cpu().numpy(), cnt.cpu().numpy()
+        lists = ((lambda s, h: ih[s, h, :ch[s, h]]) if sparse
+                 else (lambda s, h: np.arange(-(-lens[s] // B))))
+        _check_decode_rows(f64(out_p), f64(lse_p), f64(q), Kh, Vh, lens, lists, B, d, grp,
+                           TOL_ATTN_BF16)
+
+
+@pytest.mark.parametrize("d,B,hq,hkv,lens,share", [
+    (128, 64, 8, 2, (1000, 2049, 64), 7),
+    (64, 128, 8, 1, (700, 1281), 3),
+])
+def test_decode_paged_fp8(d, B, hq, hkv, lens, share):
+    """fp8 e4m3 pages with per-tensor scales: the kernel's attention against
+    the oracle on the codes decoded from the format's definition and scaled
+    (code NaN in every unused row and page)."""
+    cfg = gen.CONFIGS["C4"].with_(d=d, B=B, hq=hq, hkv=hkv)
+    ns, grp = len(lens), hq // hkv
+    _print("paged fp8", d, B, hq, hkv, lens, share)
+    K, V, q, table, num_pages = _paged_inputs(cfg, lens, share)
+    ks, vs = 0.0625, 0.02
+    kp = _fill_pages([gen.to_fp8_e4m3(k, ks) for k in K], table, num_pages, B, torch.uint8, 0x7F)
+    vp = _fill_pages([gen.to_fp8_e4m3(v, vs) for v in V], table, num_pages, B, torch.uint8, 0x7F)
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cur = (ctx - 1) // B
+    b_max = -(-max(lens) // B)
+    gr = torch.Generator(device="cuda")
+    gr.manual_seed(gen.seed_for(12, d, B, hq))
+    r = torch.rand((ns, hq, b_max), generator=gr, device="cuda")
+    uidx, ucnt, umask, idx, cnt = sws.select_topk_row(r, hq, hkv, cur, b_max, 25, per_head=True)
+    tab = torch.from_numpy(table).cuda()
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    Kh = [O.fp8_e4m3_value(O.gather_pages(kph, table[s], n, B)) * ks for s, n in enumerate(lens)]
+    Vh = [O.fp8_e4m3_value(O.gather_pages(vph, table[s], n, B)) * vs for s, n in enumerate(lens)]
+    ih, ch = idx.cpu().numpy(), cnt.cpu().numpy()
+    for sparse in (True, False):
+        u = (uidx, ucnt, umask) if sparse else (None, None, None)
+        lse = torch.empty((ns, hq), dtype=torch.float32, device="cuda")
+        out = sws.sparse_attn_decode_paged(q, kp.view(torch.float8_e4m3fn),
+                                           vp.view(torch.float8_e4m3fn), tab, ctx, *u,
+                                           k_scale=ks, v_scale=vs, lse=lse)
+        torch.cuda.synchronize()
+        lists = ((lambda s, h: ih[s, h, :ch[s, h]]) if sparse
+                 else (lambda s, h: np.arange(-(-lens[s] // B))))
+        _check_decode_rows(f64(out), f64(lse), f64(q), Kh, Vh, lens, lists, B, d, grp,
+                           TOL_ATTN_BF16)

@@ -34,3 +34,35 @@ def test_decode_equals_prefix_prefill_row(p_len):
             np.testing.assert_allclose(dh["o"], o_blk[t], rtol=1e-11, atol=1e-12)
             assert abs(dh["lse"] - lse_blk[t]) < 1e-11
     assert b == c + 1
+
+
+def test_fp8_e4m3_value_spec_points():
+    """Codes whose values the OCP E4M3 definition fixes: one, the largest
+    finite value, the smallest normal and subnormal, signed zero, NaN."""
+    v = O.fp8_e4m3_value([0x38, 0xB8, 0x7E, 0xFE, 0x08, 0x01, 0x07, 0x00, 0x80, 0x7F, 0xFF,
+                          0x40, 0x3C, 0x30])
+    want = [1.0, -1.0, 448.0, -448.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, 0.0, -0.0,
+            np.nan, np.nan, 2.0, 1.5, 0.5]
+    np.testing.assert_array_equal(v, want)
+    assert np.signbit(v[8]) and not np.signbit(v[7])
+
+
+def test_fp8_e4m3_value_matches_torch_on_every_code():
+    """All 256 codes against torch's float8_e4m3fn, an independent decoder of
+    the same format (NaN codes compare as NaN)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = O.fp8_e4m3_value(codes)
+    np.testing.assert_array_equal(got, want)
+    # monotone over the positive finite codes
+    pos = got[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_gather_pages_by_hand():
+    """Two pages of B = 2 tokens in swapped order: token t sits in row t % 2
+    of page table[t // 2]."""
+    pages = np.arange(3 * 2 * 1).reshape(3, 2, 1)   # page p row r holds 2 p + r
+    got = O.gather_pages(pages, [2, 0, 1], 5, 2)[:, 0].tolist()
+    assert got == [4, 5, 0, 1, 2]
