@@ -144,19 +144,22 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
   for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+  static_assert(KT == 32, "one S tile per step");
+  {
+    bf16x8_t a[D / 16];
 #pragma unroll
-  for (int dc = 0; dc < D / 16; dc += 2) {
-    bf16x8_t a[2][KT / 32];
+    for (int dc = 0; dc < D / 16; ++dc)
+      a[dc] = *reinterpret_cast<const bf16x8_t*>(ksb + k_rd[dc]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int dc = 0; dc < D / 16; ++dc)
+      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dc], qf[dc], st[0], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
-        a[u][kt] = *reinterpret_cast<const bf16x8_t*>(ksb + k_rd[dc + u] + kt * 32 * D * 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][kt], qf[dc + u], st[kt], 0, 0, 0);
+    for (int dc = 0; dc < D / 16 - 2; ++dc) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
   // ---- causal mask (diagonal block only) and the step's row maximum ----
   if (diag) {
@@ -228,8 +231,13 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   using TL = PrefillTile<D, BLK>;
   constexpr int NT = TL::NT, KT = TL::KT;
   static_assert(TL::NSUB % 2 == 0, "an even number of pipeline steps per block");
-  __shared__ __attribute__((aligned(16))) char Ks[2][TL::TILE];
-  __shared__ __attribute__((aligned(16))) char Vs[2][TL::TILE];
+  // Two buffers per operand as separate LDS objects, so the compiler can tell
+  // that the reads of one buffer do not wait on the direct-to-LDS loads
+  // filling the other.
+  __shared__ __attribute__((aligned(16))) char Ks0[TL::TILE];
+  __shared__ __attribute__((aligned(16))) char Ks1[TL::TILE];
+  __shared__ __attribute__((aligned(16))) char Vs0[TL::TILE];
+  __shared__ __attribute__((aligned(16))) char Vs1[TL::TILE];
 
   const int G = hq / hkv;
   const int id = blockIdx.x;
@@ -267,14 +275,17 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   }
 
   // ---- staging geometry: load u of this thread fills tile chunk u * NT + tid ----
-  int k_row[TL::LOADS], k_col[TL::LOADS];
+  // The tiles go global -> LDS directly (global_load_lds_dwordx4): lane l of
+  // wave w writes the 16 bytes at chunk u * NT + 64 w + l, so the XOR swizzle
+  // of the LDS layout is applied to the global source column instead.
+  int k_roff[TL::LOADS], k_col[TL::LOADS];
   uint32_t v_off[TL::LOADS];
 #pragma unroll
   for (int u = 0; u < TL::LOADS; ++u) {
     const int qc = u * NT + tid;
     const int kr = qc / TL::KCH;
     const int kp = qc % TL::KCH;
-    k_row[u] = kr;
+    k_roff[u] = kr * (int)kstride;
     k_col[u] = (kp ^ row_swizzle<TL::KCH>(kr)) * 8;
     const int vr = qc / TL::VCH;
     const int vp = qc % TL::VCH;
@@ -282,30 +293,38 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   }
   const uint16_t* kbase = k + (int64_t)tok0 * kstride + (int64_t)kvh * D;
   const uint16_t* vtbase = vt + ((int64_t)kvh * total_blocks + blk0) * D * BLK;
+  const int wave_chunk = __builtin_amdgcn_readfirstlane(w) * 64 * 16;
 
-  // Register staging: the tiles of step s + 1 are loaded while step s
-  // computes, then stored into the other LDS buffer.
-  u32x4_t kst[TL::LOADS], vst[TL::LOADS];
-  auto load_step = [&](int j, int sub) {
-    // Rows past the end of the sequence (only in the last, partial block,
-    // which only its own query block selects, as its diagonal) re-read the
-    // last row: the causal mask removes those keys and their V^T is zero.
-    const int key0 = j * BLK + sub * KT;
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(1))) void glb_void_t;
+  // Issue the loads of step `sub` of block j into LDS buffer pair (kd, vd).
+  // Rows past the end of the sequence (only in the last, partial block, which
+  // only its own query block selects, as its diagonal) re-read the last row:
+  // the causal mask removes those keys and their V^T is zero.
+  auto load_step = [&](int j, int sub, char* kd, char* vd) {
+    // offsets from the block's first row: block j holds at least one token,
+    // so the clamp row n - 1 - j * BLK is >= 0 and every offset is
+    // non-negative (a sub-step of a partial block may start past the end)
+    const uint16_t* ks = kbase + (int64_t)j * BLK * kstride;
     const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
-    const int last = n - 1 - key0;
+    const int last_off = (n - 1 - j * BLK) * (int)kstride;
+    const int sub_off = sub * KT * (int)kstride;
 #pragma unroll
     for (int u = 0; u < TL::LOADS; ++u) {
-      const int row = min(k_row[u], last);
-      kst[u] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(key0 + row) * kstride + k_col[u]);
-      vst[u] = *reinterpret_cast<const u32x4_t*>(vs + v_off[u]);
+      // 32-bit byte offsets from a uniform base (scalar base + vector offset)
+      const uint32_t kb = (uint32_t)(min(sub_off + k_roff[u], last_off) + k_col[u]) * 2u;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const char*>(ks) + kb),
+                                       (lds_void_t*)(kd + u * NT * 16 + wave_chunk), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (glb_void_t*)(reinterpret_cast<const char*>(vs) + v_off[u] * 2u),
+          (lds_void_t*)(vd + u * NT * 16 + wave_chunk), 16, 0, 0);
     }
   };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < TL::LOADS; ++u) {
-      *reinterpret_cast<u32x4_t*>(&Ks[buf][(u * NT + tid) * 16]) = kst[u];
-      *reinterpret_cast<u32x4_t*>(&Vs[buf][(u * NT + tid) * 16]) = vst[u];
-    }
+  // A step's tiles are complete for the workgroup once every wave has waited
+  // for its own loads and passed the barrier.
+  auto step_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   };
 
   // ---- per-lane LDS read offsets (bytes) of the MFMA A operands ----
@@ -328,26 +347,24 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int nb = idx ? cnt[(int64_t)h * total_blocks + gb] : i + 1;
   const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
 
-  // Step sub of a block uses LDS buffer sub % 2; while it computes, the next
-  // step (the block's next sub-step, or the first of the next block) is
-  // loaded into registers, then stored into the other buffer.
+  // Step sub of a block uses LDS buffer pair sub % 2; while it computes, the
+  // next step (the block's next sub-step, or the first of the next block)
+  // streams into the other pair.
   int j = lst ? lst[0] : 0;
-  load_step(j, 0);
-  store_step(0);
-  __syncthreads();
+  load_step(j, 0, Ks0, Vs0);
+  step_barrier();
   for (int nn = 0; nn < nb; ++nn) {
     const bool has_next = nn + 1 < nb;
     const int j_next = has_next ? (lst ? lst[nn + 1] : nn + 1) : j;
 #pragma unroll
     for (int sub = 0; sub < TL::NSUB; ++sub) {
-      const int buf = sub & 1;
+      const bool odd = sub & 1;
       const bool last_sub = sub + 1 == TL::NSUB;
-      if (!last_sub) load_step(j, sub + 1);
-      else if (has_next) load_step(j_next, 0);
-      attn_step<D, BLK>(j == i, Ks[buf], Vs[buf], sub * KT, qf, k_rd, v_rd, o, m_run, l_run,
-                        scale_log2, qi, hl);
-      if (!last_sub || has_next) store_step(buf ^ 1);
-      __syncthreads();
+      if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
+      else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
+      attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd, o,
+                        m_run, l_run, scale_log2, qi, hl);
+      step_barrier();
     }
     j = j_next;
   }
