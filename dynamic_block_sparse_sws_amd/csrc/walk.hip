@@ -17,10 +17,10 @@
 // only the final division is visible), which keeps s * layers hops in fp32.
 //
 // Decode: one workgroup per (sequence, query head) walks the single row of
-// the open block; the j range is cut into segments, one per lane group, with
-// the segment's sketch rows held in registers for all s hops, and the suffix
-// carry across segments comes from a wave scan plus an LDS scan of the wave
-// totals.
+// the open block; the j range is cut into segments, one per thread of a
+// component quarter, with the segment's sketch rows held in registers for all
+// s hops, and the suffix carry across segments comes from a wave scan plus
+// the wave totals in LDS.
 #include "sws_common.h"
 
 namespace sws {
@@ -229,17 +229,24 @@ void walk_kernel(
 // ---------------------------------------------------------------------------
 // decode: one row per (sequence, query head)
 // ---------------------------------------------------------------------------
-// 512 threads.  Thread t works on component quarter p = t / 128 of the
-// sketches (KP / 4 components) and on segment g = t % 128 of the rows j, the
+// 1024 threads.  Thread t works on component quarter p = t / 256 of the
+// sketches (KP / 4 components) and on segment g = t % 256 of the rows j, the
 // segments taken in descending j order so that the suffix sum over j becomes
-// a prefix scan over the threads of a quarter.  The segment's q and k sketch
-// rows stay in registers for all s hops (longer rows stream them from
-// memory); each hop is: segment totals, a DPP wave scan plus an LDS scan of
-// the quarter's two wave totals, the segment's partial dot products, a sum
-// over the four quarters in LDS, and the row maximum.
-constexpr int kRowThreads = 512;
-constexpr int kRowSeg = 128;        // segments (threads per component quarter)
-constexpr int kRowBmax = 4096;      // xs / ypart capacity (largest row)
+// a prefix scan over the threads of a quarter.  REG: the segment's q and k
+// sketch rows (up to 40 / (KP / 4) of them) stay in registers for all s hops;
+// otherwise they are re-read from memory every hop.  The segment's x values
+// live in registers too.  A hop:
+//   A  x of the segment's rows from the previous hop's four partial products
+//      (LDS), T = sum over the segment of x q, and the largest |x|;
+//   B  a wave scan of T, the wave totals and maxima to LDS, barrier;
+//   C  S = exclusive scan (+ the totals of the quarter's earlier waves), all
+//      scaled by 1 / max (T is linear in x, so the scale of a hop is applied
+//      after the barrier), then the rows' partial products k . S to LDS,
+//      barrier.
+constexpr int kRowThreads = 1024;
+constexpr int kRowSeg = 256;        // segments (threads per component quarter)
+constexpr int kRowBmax = 4096;      // ypart capacity (largest row)
+constexpr int kRowLStream = kRowBmax / kRowSeg;   // rows per segment, streaming form
 
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
 // 16-lane rows, then broadcasts of lanes 15 and 31 into the following rows).
@@ -259,23 +266,74 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
-template <int KP>
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_shifted(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, RMASK, 0xF, false));
+}
+
+// The same scan for N independent values at once, step by step, so the DPP
+// read of one value is separated from its last write by the others.
+template <int N>
+__device__ __forceinline__ void wave_prefix_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x111, 0xF>(v[e]);   // row_shr:1
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x112, 0xF>(v[e]);   // row_shr:2
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x114, 0xF>(v[e]);   // row_shr:4
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x118, 0xF>(v[e]);   // row_shr:8
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x142, 0xA>(v[e]);   // row_bcast:15
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x143, 0xC>(v[e]);   // row_bcast:31
+}
+
+// Maximum of non-negative values over the wave, valid in lane 63 (the scan's
+// DPP pattern with max in place of add; absent lanes contribute 0).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp_shifted<0x111, 0xF>(v));
+  v = fmaxf(v, dpp_shifted<0x112, 0xF>(v));
+  v = fmaxf(v, dpp_shifted<0x114, 0xF>(v));
+  v = fmaxf(v, dpp_shifted<0x118, 0xF>(v));
+  v = fmaxf(v, dpp_shifted<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_shifted<0x143, 0xC>(v));
+  return v;
+}
+
+template <int KP, bool REG>
 __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
     const float* __restrict__ q_cache, const float* __restrict__ k_cache, int hq, int hkv,
-    int k, const int32_t* __restrict__ cur_block, int b_max, int s, const float* r_prev,
-    float* r_out, float inv_sqrt_k) {
-  constexpr int CQ = KP / 4;                  // components per quarter
-  constexpr int LMAX = 80 / CQ;               // segment rows held in registers
+    int k, const int32_t* __restrict__ cur_block, int n_seqs, int b_max, int s,
+    const float* r_prev, float* r_out, float inv_sqrt_k) {
+  constexpr int CQ = KP / 4;                                  // components per quarter
+  constexpr int LR = REG ? 40 / CQ : kRowLStream;             // rows per segment (capacity)
   constexpr int NWAVE = kRowThreads / 64;
-  constexpr int WPQ = kRowSeg / 64;           // waves per quarter
-  __shared__ float xs[kRowBmax];
+  constexpr int WPQ = kRowSeg / 64;                           // waves per quarter
   __shared__ float ypart[4][kRowBmax];
   __shared__ float wtot[NWAVE][CQ];
   __shared__ float wmax[NWAVE];
 
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
+  // Workgroup -> (sequence, head): the query heads of one (sequence, KV head)
+  // pair get ids equal modulo 8, so they run on one XCD and read the shared K
+  // sketch rows through one L2 (pairs past the last multiple of 8 map plainly).
   const int grp = hq / hkv;
+  int pair, hi;
+  {
+    const int id = blockIdx.x;
+    const int np8 = (n_seqs * hkv) / 8 * 8;
+    if (id < np8 * grp) {
+      pair = id / (8 * grp) * 8 + id % 8;
+      hi = id / 8 % grp;
+    } else {
+      const int t = id - np8 * grp;
+      pair = np8 + t / grp;
+      hi = t % grp;
+    }
+  }
+  const int seq = pair / hkv;
+  const int h = pair % hkv * grp + hi;
   const int c = cur_block[seq];
   const int b = c + 1;
   const int tid = threadIdx.x;
@@ -283,9 +341,8 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   const int wave = tid >> 6;
   const int p = tid / kRowSeg;
   const int g = tid % kRowSeg;
-  const int L = (b + kRowSeg - 1) / kRowSeg;
-  const bool in_regs = L <= LMAX;
-  const int seg = kRowSeg - 1 - g;            // descending j order
+  const int L = (b + kRowSeg - 1) / kRowSeg;                  // <= LR (checked on the host)
+  const int seg = kRowSeg - 1 - g;                            // descending j order
   const int j0 = min(b, seg * L);
   const int j1 = min(b, j0 + L);
 
@@ -294,122 +351,130 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   const float* rin = r_prev ? r_prev + ((int64_t)seq * hq + h) * b_max : nullptr;
   float* rout = r_out + ((int64_t)seq * hq + h) * b_max;
 
-  float qv[LMAX][CQ], kv[LMAX][CQ];
-  if (in_regs && k == KP) {
-    // full quarters: the sketch rows go through LDS (the ypart area, unused
-    // until the first hop) in chunks of R rows, read with contiguous 16-byte
-    // loads across the workgroup; each thread then picks its segment's rows
-    constexpr int R = 8192 / KP;               // rows per chunk: q and k fill 64 KB
-    constexpr int V4 = KP / 4;                 // float4 per row
-    float* stage = &ypart[0][0];
-    for (int r0 = 0; r0 < b; r0 += R) {
-      const int nr = min(R, b - r0);
+  // sketch rows of the segment (REG), zero past the segment's end.  They go
+  // through LDS (the ypart area, unused until the first hop) in chunks of
+  // whole segments, read from memory with contiguous 16-byte loads; the
+  // 16-byte slots of a staged row are XOR-swizzled by the row index so the
+  // threads of consecutive segments (rows L apart) read distinct banks.
+  float qv[REG ? LR : 1][CQ], kv[REG ? LR : 1][CQ];
+  if (REG) {
+    constexpr int V4 = KP / 4;                  // float4 per row
+    constexpr int R = 8192 / KP;                // staged rows: q and k fill 64 KB
+    float4* stq = reinterpret_cast<float4*>(&ypart[0][0]);
+    float4* stk = stq + R * V4;
+#pragma unroll
+    for (int l = 0; l < LR; ++l)
+#pragma unroll
+      for (int e = 0; e < CQ; ++e) qv[l][e] = kv[l][e] = 0.f;
+    const int ns = R / L;                       // whole segments per chunk
+    for (int s0 = 0; s0 * L < b; s0 += ns) {
+      const int r0 = s0 * L;
+      const int nr = min(ns * L, b - r0);
       for (int v = tid; v < nr * V4; v += kRowThreads) {
-        const int64_t g4 = (int64_t)r0 * V4 + v;
-        reinterpret_cast<float4*>(stage)[v] = reinterpret_cast<const float4*>(qrow)[g4];
-        reinterpret_cast<float4*>(stage + R * KP)[v] = reinterpret_cast<const float4*>(krow)[g4];
+        const int r = v / V4, cc = v % V4;
+        const int64_t src = (int64_t)(r0 + r) * V4 + cc;
+        stq[r * V4 + (cc ^ (r & (V4 - 1)))] = reinterpret_cast<const float4*>(qrow)[src];
+        stk[r * V4 + (cc ^ (r & (V4 - 1)))] = reinterpret_cast<const float4*>(krow)[src];
       }
       __syncthreads();
+      if (seg >= s0 && seg < s0 + ns) {
 #pragma unroll
-      for (int l = 0; l < LMAX; ++l) {
-        const int j = j0 + l;
-        if (j >= r0 && j < r0 + nr && j < j1) {
-          const float* qs = stage + (j - r0) * KP + p * CQ;
-          const float* ks = stage + R * KP + (j - r0) * KP + p * CQ;
+        for (int l = 0; l < LR; ++l) {
+          if (l < j1 - j0) {
+            const int r = j0 + l - r0;
 #pragma unroll
-          for (int e = 0; e < CQ; e += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(qs + e);
-            const float4 bb = *reinterpret_cast<const float4*>(ks + e);
-            qv[l][e] = a.x; qv[l][e + 1] = a.y; qv[l][e + 2] = a.z; qv[l][e + 3] = a.w;
-            kv[l][e] = bb.x; kv[l][e + 1] = bb.y; kv[l][e + 2] = bb.z; kv[l][e + 3] = bb.w;
+            for (int e = 0; e < CQ; e += 4) {
+              const int slot = r * V4 + (((p * CQ + e) / 4) ^ (r & (V4 - 1)));
+              const float4 a = stq[slot];
+              const float4 bb = stk[slot];
+              qv[l][e] = a.x; qv[l][e + 1] = a.y; qv[l][e + 2] = a.z; qv[l][e + 3] = a.w;
+              kv[l][e] = bb.x; kv[l][e + 1] = bb.y; kv[l][e + 2] = bb.z; kv[l][e + 3] = bb.w;
+            }
           }
         }
       }
       __syncthreads();
     }
-  } else {
-#pragma unroll
-    for (int l = 0; l < LMAX; ++l)
-#pragma unroll
-      for (int e = 0; e < CQ; ++e) {
-        const int j = j0 + l;
-        const int cc = p * CQ + e;
-        const bool ok = in_regs && j < j1 && cc < k;
-        qv[l][e] = ok ? qrow[(int64_t)j * k + cc] : 0.f;
-        kv[l][e] = ok ? krow[(int64_t)j * k + cc] : 0.f;
-      }
   }
-  for (int j = tid; j < b; j += kRowThreads) xs[j] = rin ? rin[j] : (j == c ? 1.0f : 0.0f);
-  __syncthreads();
-
   auto qget = [&](int l, int e) -> float {
-    if (in_regs) return qv[l][e];
+    if (REG) return qv[REG ? l : 0][e];
     const int cc = p * CQ + e;
     return cc < k ? qrow[(int64_t)(j0 + l) * k + cc] : 0.f;
   };
   auto kget = [&](int l, int e) -> float {
-    if (in_regs) return kv[l][e];
+    if (REG) return kv[REG ? l : 0][e];
     const int cc = p * CQ + e;
     return cc < k ? krow[(int64_t)(j0 + l) * k + cc] : 0.f;
   };
 
-  float sc = 1.0f;
-  float gmax = 0.0f;
+  const int nv = j1 - j0;                                     // rows of this segment
+  const float* yp = &ypart[0][0] + j0;                        // yp[q * kRowBmax + l]
+  float xr[LR];
+#pragma unroll
+  for (int l = 0; l < LR; ++l) {
+    const int j = j0 + l;
+    xr[l] = l < nv ? (rin ? rin[j] : (j == c ? 1.0f : 0.0f)) : 0.f;
+  }
   for (int hop = 0; hop < s; ++hop) {
+    // ---- A: x of the segment's rows, T, local max ----
+    if (hop > 0) {
+#pragma unroll
+      for (int l = 0; l < LR; ++l)
+        xr[l] = l < nv ? ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
+                             inv_sqrt_k
+                       : 0.f;
+    }
     float T[CQ];
 #pragma unroll
     for (int e = 0; e < CQ; ++e) T[e] = 0.f;
-    if (in_regs) {
+    float lmax = 0.f;
 #pragma unroll
-      for (int l = 0; l < LMAX; ++l) {
-        if (j0 + l < j1) {
-          const float x = xs[j0 + l] * sc;
+    for (int l = 0; l < LR; ++l) {
+      if (REG || l < nv) {
 #pragma unroll
-          for (int e = 0; e < CQ; ++e) T[e] += x * qv[l][e];
-        }
+        for (int e = 0; e < CQ; ++e) T[e] += xr[l] * qget(l, e);
       }
-    } else {
-      for (int l = 0; l < j1 - j0; ++l) {
-        const float x = xs[j0 + l] * sc;
-#pragma unroll
-        for (int e = 0; e < CQ; ++e) T[e] += x * qget(l, e);
-      }
+      lmax = fmaxf(lmax, fabsf(xr[l]));
     }
-    // exclusive prefix over the scan order = suffix over the rows above
+    // ---- B: wave scan, totals and maxima ----
     float S[CQ];
 #pragma unroll
-    for (int e = 0; e < CQ; ++e) {
-      const float inc = wave_prefix_sum(T[e]);
-      S[e] = inc - T[e];
-      if (lane == 63) wtot[wave][e] = inc;
+    for (int e = 0; e < CQ; ++e) S[e] = T[e];
+    wave_prefix_sum_n<CQ>(S);
+    lmax = wave_max_nonneg(lmax);
+    if (lane == 63) {
+#pragma unroll
+      for (int e = 0; e < CQ; ++e) wtot[wave][e] = S[e];
+      wmax[wave] = lmax;
     }
+#pragma unroll
+    for (int e = 0; e < CQ; ++e) S[e] -= T[e];                 // exclusive
     __syncthreads();
+    float gmax = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
+    const float sc = gmax > 0.f ? 1.0f / gmax : 1.0f;
     {
-      const int w0 = p * WPQ;
+      const int wq = wave - p * WPQ;                          // earlier waves of the quarter
 #pragma unroll
-      for (int e = 0; e < CQ; ++e) {
-        float carry = 0.f;
-        for (int w2 = w0; w2 < wave; ++w2) carry += wtot[w2][e];
-        S[e] += carry;
-      }
-    }
-    if (in_regs) {
+      for (int w2 = 0; w2 < WPQ - 1; ++w2) {
+        if (w2 < wq) {
 #pragma unroll
-      for (int l = LMAX - 1; l >= 0; --l) {
-        if (j0 + l < j1) {
-          const float x = xs[j0 + l] * sc;
-          float y = 0.f;
-#pragma unroll
-          for (int e = 0; e < CQ; ++e) {
-            S[e] += x * qv[l][e];
-            y += kv[l][e] * S[e];
-          }
-          ypart[p][j0 + l] = y;
+          for (int e = 0; e < CQ; ++e) S[e] += wtot[p * WPQ + w2][e];
         }
       }
-    } else {
-      for (int l = j1 - j0 - 1; l >= 0; --l) {
-        const float x = xs[j0 + l] * sc;
+#pragma unroll
+      for (int e = 0; e < CQ; ++e) S[e] *= sc;
+    }
+    // ---- C: partial products k . S of the segment's rows, last row first ----
+    // (REG: the test is l < L, the same for the whole workgroup; rows l in
+    // [nv, L) exist only in the truncated or empty segments at the end of the
+    // row, hold zero sketches and x, and their products land on rows >= b,
+    // below kRowBmax, which no segment reads)
+#pragma unroll
+    for (int l = LR - 1; l >= 0; --l) {
+      if (REG ? l < L : l < nv) {
+        const float x = xr[l] * sc;
         float y = 0.f;
 #pragma unroll
         for (int e = 0; e < CQ; ++e) {
@@ -420,26 +485,28 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
       }
     }
     __syncthreads();
-    float lmax = 0.f;
-    for (int j = tid; j < b; j += kRowThreads) {
-      const float y = ((ypart[0][j] + ypart[1][j]) + (ypart[2][j] + ypart[3][j])) * inv_sqrt_k;
-      xs[j] = y;
-      lmax = fmaxf(lmax, fabsf(y));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
-    if (lane == 0) wmax[wave] = lmax;
-    __syncthreads();
-    gmax = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
-    sc = (gmax > 0.f) ? 1.0f / gmax : 1.0f;
   }
-  for (int j = tid; j < b_max; j += kRowThreads) {
-    float v = 0.f;
-    if (j < b && gmax > 0.f) v = xs[j] / gmax;
-    rout[j] = v;
+  // ---- final row, divided by its largest magnitude ----
+  float lmax = 0.f;
+#pragma unroll
+  for (int l = 0; l < LR; ++l) {
+    xr[l] = l < nv ? ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
+                         inv_sqrt_k
+                   : 0.f;
+    lmax = fmaxf(lmax, fabsf(xr[l]));
   }
+  lmax = wave_max_nonneg(lmax);
+  if (lane == 63) wmax[wave] = lmax;
+  __syncthreads();
+  float gmax = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
+  if (p == 0) {
+#pragma unroll
+    for (int l = 0; l < LR; ++l)
+      if (l < nv) rout[j0 + l] = gmax > 0.f ? xr[l] / gmax : 0.f;
+  }
+  for (int j = b + tid; j < b_max; j += kRowThreads) rout[j] = 0.f;
 }
 
 template <int KP>
@@ -457,9 +524,17 @@ template <int KP>
 hipError_t run_walk_row(const float* q_sk, const float* k_sk, int hq, int hkv, int k, int n_seqs,
                         const int32_t* cur_block, int b_max, int s, const float* r_prev,
                         float* r_out, hipStream_t st) {
-  dim3 grid(hq, n_seqs);
-  hipLaunchKernelGGL((walk_row_kernel<KP>), grid, dim3(kRowThreads), 0, st, q_sk, k_sk, hq, hkv,
-                     k, cur_block, b_max, s, r_prev, r_out, 1.0f / sqrtf((float)k));
+  const dim3 grid(hq * n_seqs);
+  // every row has b <= b_max blocks, so ceil(b_max / 256) bounds the segment length
+  const int l_max = (b_max + kRowSeg - 1) / kRowSeg;
+  if (k == KP && l_max <= 40 / (KP / 4))
+    hipLaunchKernelGGL((walk_row_kernel<KP, true>), grid, dim3(kRowThreads), 0, st, q_sk, k_sk,
+                       hq, hkv, k, cur_block, n_seqs, b_max, s, r_prev, r_out,
+                       1.0f / sqrtf((float)k));
+  else
+    hipLaunchKernelGGL((walk_row_kernel<KP, false>), grid, dim3(kRowThreads), 0, st, q_sk, k_sk,
+                       hq, hkv, k, cur_block, n_seqs, b_max, s, r_prev, r_out,
+                       1.0f / sqrtf((float)k));
   return hipGetLastError();
 }
 
