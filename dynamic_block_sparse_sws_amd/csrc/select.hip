@@ -4,8 +4,8 @@
 //
 // One wavefront owns one row.  Scores become order-preserving unsigned keys
 // (-0 folded onto +0 first), held in registers, 64 candidates per register.
-// The tau-th largest key T is found by a most-significant-bit-first search,
-// each step counting keys >= candidate with wave ballots.  Then every key > T
+// The tau-th largest key T is found by a radix search over its four bytes
+// (a per-wave LDS histogram and a wave scan per byte).  Then every key > T
 // is kept, plus the lowest-index keys equal to T until tau are kept; the
 // kept indices are compacted in ascending order with ballot prefix counts, so
 // the result is exactly the (score descending, index ascending) top tau.
@@ -22,34 +22,75 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+constexpr int kLoadBatch = 16;   // row values loaded per batch (registers in flight)
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Selection flags for row values row[0 .. n) (n candidates), keeping tau of
-// them.  key[] holds the keys of candidates e * 64 + lane (0 if absent).
-// Returns the threshold and the number of threshold ties to keep.
+// The tau-th largest key T of the candidates key[] (candidate e * 64 + lane,
+// n of them, 0 if absent) and the number of keys equal to T to keep, by a
+// radix search, one byte at a time from the top:
+// each pass histograms the next byte of the keys that match the bytes fixed
+// so far into a 256-bin LDS histogram owned by this wave (`hist`), and a
+// wave scan over the bins, largest first, finds the byte value where the
+// count of larger keys reaches tau.  Wave-local: LDS operations of one wave
+// complete in order, so no barrier is needed.
 template <int E>
-__device__ __forceinline__ void threshold(const uint32_t (&key)[E], int n, int tau,
-                                          uint32_t& T, int& need_eq) {
-  uint32_t t = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    int c = 0;
+__device__ __forceinline__ void threshold_radix(const uint32_t (&key)[E], int n, int tau,
+                                                uint32_t* hist, uint32_t& T, int& need_eq) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0;
+  int remaining = tau;                          // keys still to take at or below the prefix
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (e * 64 < n) c += popc64(__ballot(key[e] >= cand));
+      if (e * 64 < n) {
+        const uint32_t k = key[e];
+        const bool match = e * 64 + lane < n && (pass == 0 || (k >> (shift + 8)) == prefix);
+        if (match) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
     }
-    if (c >= tau) t = cand;
+    // lane l holds bins 255 - 4 l .. 252 - 4 l, largest first
+    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[63 - lane];
+    const int s_l = (int)(h4.x + h4.y + h4.z + h4.w);
+    int incl = s_l;
+    {
+      // inclusive prefix over lanes (row shifts, then row broadcasts)
+      int x = incl;
+      incl += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false); x = incl;
+      incl += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false); x = incl;
+      incl += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false); x = incl;
+      incl += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false); x = incl;
+      incl += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); x = incl;
+      incl += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+    }
+    const int excl = incl - s_l;
+    // (remaining == 0: nothing more to take, lane 0 and bin 255)
+    const uint64_t hit = __ballot(incl >= remaining && (excl < remaining || lane == 0));
+    const int L = (int)__builtin_ctzll(hit);    // the lane whose 4 bins hold the answer
+    // within that lane: bins in descending order w, z, y, x
+    int above = excl, digit = 0;
+    {
+      const int need = remaining;
+      const int bw = (int)h4.w, bz = (int)h4.z, by = (int)h4.y;
+      const int base = 255 - 4 * lane;          // bin of h4.w
+      if (above + bw >= need) digit = base;
+      else if (above + bw + bz >= need) { above += bw; digit = base - 1; }
+      else if (above + bw + bz + by >= need) { above += bw + bz; digit = base - 2; }
+      else { above += bw + bz + by; digit = base - 3; }
+    }
+    digit = __builtin_amdgcn_readlane(digit, L);
+    above = __builtin_amdgcn_readlane(above, L);
+    remaining -= above;
+    prefix = (prefix << 8) | (uint32_t)digit;
   }
-  int gt = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (e * 64 < n) gt += popc64(__ballot(key[e] > t));
-  }
-  T = t;
-  need_eq = tau - gt;
+  T = prefix;
+  need_eq = remaining;
 }
 
 // flags: SWS_SELECT_DENSE keeps every block <= i; SWS_SELECT_ROW_TAU gives
@@ -65,6 +106,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ R
                                                      int flags, int GS, int width,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ cnt) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][256];
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int h0 = blockIdx.y * GS;
@@ -85,20 +127,26 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ R
   }
   const float* row = R + walk_seq_offset(cu_blocks, seq, hq) + ((int64_t)h0 * b + i) * b;
   const int64_t hstride = (int64_t)b * b;
+  // loads go out (up to) 16 registers at a time, all before any is used
+  // (indices past the candidates are clamped to the last one and masked
+  // below; i > tau >= 0 here)
   uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int m = e * 64 + lane;
-    float v = 0.f;
-    if (m < i) {
-      v = row[m];
-      for (int hh = 1; hh < GS; ++hh) v += row[hh * hstride + m];
+  for (int e0 = 0; e0 < E; e0 += kLoadBatch) {
+    constexpr int NB = E < kLoadBatch ? E : kLoadBatch;
+    float v[NB];
+#pragma unroll
+    for (int e = 0; e < NB; ++e) v[e] = row[min((e0 + e) * 64 + lane, i - 1)];
+    for (int hh = 1; hh < GS; ++hh) {
+#pragma unroll
+      for (int e = 0; e < NB; ++e) v[e] += row[hh * hstride + min((e0 + e) * 64 + lane, i - 1)];
     }
-    key[e] = (m < i) ? order_key(v) : 0u;
+#pragma unroll
+    for (int e = 0; e < NB; ++e) key[e0 + e] = ((e0 + e) * 64 + lane < i) ? order_key(v[e]) : 0u;
   }
   uint32_t T;
   int need;
-  threshold<E>(key, i, tau, T, need);
+  threshold_radix<E>(key, i, tau, hist[threadIdx.x >> 6], T, need);
   int base = 0, eq_seen = 0;
   const uint64_t lt = lanemask_lt();
 #pragma unroll
@@ -139,6 +187,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
     int32_t* __restrict__ cnt, int32_t* __restrict__ union_idx,
     int32_t* __restrict__ union_cnt, uint32_t* __restrict__ union_mask, int union_width) {
   __shared__ uint32_t umask[kRowBmax];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[NT / 64][256];
   const int g = blockIdx.x;
   const int seq = blockIdx.y;
   const int G = hq / hkv;
@@ -165,20 +214,26 @@ __global__ __launch_bounds__(NT) void select_row_kernel(
       // sum (heads in ascending order), so all heads keep the same blocks
       const float* row = r + ((int64_t)seq * hq + (group ? g * G : h)) * b_max;
       const int nsum = group ? G : 1;
+      // loads go out 16 registers at a time, all before any is used (indices
+      // past the candidates are clamped to the last one and masked below)
       uint32_t key[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int m = e * 64 + lane;
-        float v = 0.f;
-        if (m < c) {
-          v = row[m];
-          for (int hh = 1; hh < nsum; ++hh) v += row[(int64_t)hh * b_max + m];
+      for (int e0 = 0; e0 < E; e0 += kLoadBatch) {
+        float v[kLoadBatch];
+#pragma unroll
+        for (int e = 0; e < kLoadBatch; ++e) v[e] = row[min((e0 + e) * 64 + lane, c - 1)];
+        for (int hh = 1; hh < nsum; ++hh) {
+#pragma unroll
+          for (int e = 0; e < kLoadBatch; ++e)
+            v[e] += row[(int64_t)hh * b_max + min((e0 + e) * 64 + lane, c - 1)];
         }
-        key[e] = (m < c) ? order_key(v) : 0u;
+#pragma unroll
+        for (int e = 0; e < kLoadBatch; ++e)
+          key[e0 + e] = ((e0 + e) * 64 + lane < c) ? order_key(v[e]) : 0u;
       }
       uint32_t T;
       int need;
-      threshold<E>(key, c, tau, T, need);
+      threshold_radix<E>(key, c, tau, hist[w], T, need);
       int base = 0, eq_seen = 0;
       const uint64_t lt = lanemask_lt();
 #pragma unroll
