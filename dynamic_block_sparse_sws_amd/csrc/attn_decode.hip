@@ -152,11 +152,15 @@ __device__ __forceinline__ float exp2_or_zero(float x) {
 // workgroup, so every workgroup streams the same number of blocks whatever
 // the union sizes are, and there is no tail of half-empty chunks.  A range
 // that crosses pair boundaries leaves one partial softmax state ("record")
-// per pair it touches; the records of a pair are contiguous.
+// per pair it touches.  Every split workgroup derives the plan itself from
+// the pairs' block counts (one scan in LDS), so no separate plan launch is
+// needed; workgroup 0 also stores it for the combine kernel.  The record of
+// workgroup w for pair p is record w + p: ranges are ordered, so a later
+// workgroup never touches an earlier pair, the index is unique, and the
+// records of one pair are consecutive.
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxWG = 2048;       // split workgroups at most (sizes the workspace)
 constexpr int kDecMaxPairs = 8192;    // sequences x KV heads at most
-constexpr int kPlanThreads = 1024;
 
 // floor(x / y) for 0 <= x < 2^53, 0 < y < 2^31, through one fp64 division
 // (exact here: a quotient below an integer k is at least 1/y < 2^-31 away
@@ -173,20 +177,14 @@ __device__ __forceinline__ int wg_of_block(int64_t A, int64_t W, int nwg) {
   return (int)floor_div((A + 1) * nwg - 1, W);
 }
 
-struct DecPlan {
-  int32_t* nwg;      // [1] workgroups with work: min(launched, W), so no range is empty
-  int32_t* pre;      // [P + 1] first block of each pair (pre[P] = W)
-  int32_t* rec;      // [P + 1] first record of each pair
-  int32_t* wfirst;   // [NWG] first pair of each workgroup's range
-};
-
-__device__ __forceinline__ DecPlan plan_of(void* ws, int P) {
-  int32_t* b = static_cast<int32_t*>(ws);
-  return {b, b + 1, b + 1 + (P + 1), b + 1 + 2 * (P + 1)};
-}
+// Stored plan: [0] workgroups with work (min(launched, W), so no range is
+// empty), then pre[P + 1], the first block of each pair (pre[P] = W).
+__device__ __forceinline__ int32_t* plan_nwg(void* ws) { return static_cast<int32_t*>(ws); }
+__device__ __forceinline__ int32_t* plan_pre(void* ws) { return static_cast<int32_t*>(ws) + 1; }
 
 // Exclusive prefix sum over the workgroup of one int per thread (wave scans
 // with lane shuffles, then the wave totals); also returns the total.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -200,7 +198,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int& total
   int base = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kPlanThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int t = wtot[w];
     base += w < wave ? t : 0;
     total += t;
@@ -209,83 +207,46 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int& total
   return base + inc - v;
 }
 
-template <int BLK>
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
-    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ ucnt, int n_seqs, int hkv,
-    int nwg, void* ws) {
-  constexpr int PER = kDecMaxPairs / kPlanThreads;
-  __shared__ int32_t spre[kDecMaxPairs + 1];
-  __shared__ int wtot[kPlanThreads / 64];
-  const int P = n_seqs * hkv;
-  const DecPlan pl = plan_of(ws, P);
+// The plan in LDS: spre[p] = first block of pair p, spre[P] = W (returned).
+// Block counts are the union sizes, or every block of the context (dense).
+template <int BLK, int NT>
+__device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
+                                          const int32_t* __restrict__ ucnt, int P, int hkv,
+                                          int32_t* spre, int* wtot) {
+  constexpr int LB = 8;                       // loads in flight per thread
   const int t = threadIdx.x;
-  // thread t owns pairs t * PER .. t * PER + PER - 1
-  // (unconditional loads of clamped indices, so they are all in flight at once)
-  int cnt[PER];
-  if (ucnt) {
+  for (int p0 = 0; p0 < P; p0 += LB * NT) {
+    int v[LB];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) cnt[u] = ucnt[min(t * PER + u, P - 1)];
-  } else {
+    for (int u = 0; u < LB; ++u) {
+      const int p = min(p0 + u * NT + t, P - 1);
+      v[u] = ucnt ? ucnt[p] : (ctx_len[p / hkv] + BLK - 1) / BLK;
+    }
 #pragma unroll
-    for (int u = 0; u < PER; ++u) cnt[u] = (ctx_len[min(t * PER + u, P - 1) / hkv] + BLK - 1) / BLK;
+    for (int u = 0; u < LB; ++u)
+      if (p0 + u * NT + t < P) spre[p0 + u * NT + t] = v[u];
   }
+  __syncthreads();
+  // thread t scans pairs t * per .. t * per + per - 1
+  const int per = (P + NT - 1) / NT;
   int run = 0;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    cnt[u] = t * PER + u < P ? cnt[u] : 0;
-    run += cnt[u];
+  for (int u = 0; u < per; ++u) {
+    const int p = t * per + u;
+    if (p < P) run += spre[p];
   }
   int total;
-  int acc = block_exclusive_scan(run, wtot, total);
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int p = t * PER + u;
-    if (p < P) spre[p] = acc;
-    acc += cnt[u];
+  int acc = block_exclusive_scan<NT>(run, wtot, total);
+  for (int u = 0; u < per; ++u) {
+    const int p = t * per + u;
+    if (p < P) {
+      const int c = spre[p];
+      spre[p] = acc;
+      acc += c;
+    }
   }
   if (t == 0) spre[P] = total;
   __syncthreads();
-  const int64_t W = total;
-  // with fewer blocks than workgroups, only the first W get a (one-block) range
-  nwg = (int)std::min<int64_t>(nwg, std::max<int64_t>(W, 1));
-  if (t == 0) *pl.nwg = nwg;
-  // records per pair: the workgroups holding its first and last block
-  run = 0;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int p = t * PER + u;
-    int r = 0;
-    if (p < P && cnt[u] > 0)
-      r = wg_of_block(spre[p] + cnt[u] - 1, W, nwg) - wg_of_block(spre[p], W, nwg) + 1;
-    cnt[u] = r;
-    run += r;
-  }
-  acc = block_exclusive_scan(run, wtot, total);
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int p = t * PER + u;
-    if (p < P) {
-      pl.pre[p] = spre[p];
-      pl.rec[p] = acc;
-    }
-    acc += cnt[u];
-  }
-  if (t == 0) {
-    pl.pre[P] = spre[P];
-    pl.rec[P] = total;
-  }
-  // first pair of each workgroup: the last pair starting at or before its
-  // range (pairs without blocks are skipped by the split kernel)
-  for (int w = t; w < nwg; w += kPlanThreads) {
-    const int64_t lo = range_lo(w, W, nwg);
-    int l = 0, h = P - 1;
-    while (l < h) {
-      const int m = (l + h + 1) >> 1;
-      if (spre[m] <= lo) l = m;
-      else h = m - 1;
-    }
-    pl.wfirst[w] = l;
-  }
+  return total;
 }
 
 // Partial state of blocks [a, b) of pair p's list for every query head of the
@@ -468,30 +429,49 @@ template <typename T, int D, int BLK, int GMAX, int UNR, typename TK>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(
     const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
-    const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth,
-    float scale_log2, void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucnt,
+    const uint32_t* __restrict__ umask, int uwidth, float scale_log2, int nwg_launched,
+    void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const int32_t* __restrict__ table, int table_width, int num_pages, float kscale,
     float vscale) {
+  __shared__ int32_t spre[kDecMaxPairs + 1];
+  __shared__ int wtot[kDecThreads / 64];
   const int P = n_seqs * hkv;
-  const DecPlan pl = plan_of(ws, P);
-  const int nwg = *pl.nwg;
+  const int64_t W = build_plan<BLK, kDecThreads>(ctx_len, uidx ? ucnt : nullptr, P, hkv, spre,
+                                                 wtot);
+  // with fewer blocks than workgroups, only the first W get a (one-block) range
+  const int nwg = (int)std::min<int64_t>(nwg_launched, std::max<int64_t>(W, 1));
   const int w = blockIdx.x;
+  if (w == 0) {
+    int32_t* pre = plan_pre(ws);
+    for (int p = threadIdx.x; p <= P; p += kDecThreads) pre[p] = spre[p];
+    if (threadIdx.x == 0) *plan_nwg(ws) = nwg;
+  }
   if (w >= nwg) return;
-  const int64_t W = pl.pre[P];
   const int64_t lo = range_lo(w, W, nwg);
   const int64_t hi = range_lo(w + 1, W, nwg);
   if (lo >= hi) return;
-  for (int p = pl.wfirst[w]; p < P; ++p) {
-    const int A = pl.pre[p];
+  // first pair: the last pair starting at or before lo (pairs without blocks
+  // are skipped below)
+  int p = 0;
+  {
+    int h = P - 1;
+    while (p < h) {
+      const int m = (p + h + 1) >> 1;
+      if (spre[m] <= lo) p = m;
+      else h = m - 1;
+    }
+  }
+  for (; p < P; ++p) {
+    const int A = spre[p];
     if (A >= hi) break;
-    const int Bn = pl.pre[p + 1];
+    const int Bn = spre[p + 1];
     const int a = (int)(max(lo, (int64_t)A) - A);
     const int b = (int)(min(hi, (int64_t)Bn) - A);
     if (a >= b) continue;
-    const int r = pl.rec[p] + (w - wg_of_block(A, W, nwg));
     decode_range<T, D, BLK, GMAX, UNR, TK>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask,
-                                           uwidth, p, a, b, r, scale_log2, ws_ml, ws_acc, table,
-                                           table_width, num_pages, kscale, vscale);
+                                           uwidth, p, a, b, w + p, scale_log2, ws_ml, ws_acc,
+                                           table, table_width, num_pages, kscale, vscale);
   }
 }
 
@@ -511,9 +491,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   const int G = hq / hkv;
   const int hh = h % G;
   const int p = seq * hkv + h / G;
-  const DecPlan pl = plan_of(const_cast<void*>(ws), n_seqs * hkv);
-  const int r0 = pl.rec[p];
-  const int ns = pl.rec[p + 1] - r0;
+  // this pair's records: those of the workgroups holding its first and last block
+  const int32_t* pre = plan_pre(const_cast<void*>(ws));
+  const int nwg = *plan_nwg(const_cast<void*>(ws));
+  const int64_t W = pre[n_seqs * hkv];
+  const int A = pre[p], Bn = pre[p + 1];
+  const int r0 = Bn > A ? wg_of_block(A, W, nwg) + p : 0;
+  const int ns = Bn > A ? wg_of_block(Bn - 1, W, nwg) + p + 1 - r0 : 0;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   float m = -INFINITY;
@@ -562,10 +546,10 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   if (lse && t == 0) lse[(int64_t)seq * hq + h] = (M + log2f(L)) * kLn2;
 }
 
-// Workspace: plan (int32: nwg, pre, rec [P + 1] each, wfirst [kDecMaxWG]), then the
-// records' (max, sum) and weighted V sums, (P + kDecMaxWG) records of G heads.
+// Workspace: plan (int32: nwg, pre [P + 1]), then the records' (max, sum) and
+// weighted V sums, (P + kDecMaxWG) records of G heads.
 size_t plan_bytes(int P) {
-  return (((size_t)1 + 2 * (P + 1) + kDecMaxWG) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return (((size_t)1 + (P + 1)) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
 // Split workgroups per launch: three resident per CU (the kernel's occupancy),
@@ -596,16 +580,12 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
   const int nwg = split_workgroups();
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan_bytes(P));
   float* ws_acc = ws_ml + (size_t)(P + kDecMaxWG) * G * 2;
-  hipLaunchKernelGGL((decode_plan_kernel<BLK>), dim3(1), dim3(kPlanThreads), 0, st, ctx_len,
-                     uidx ? ucnt : nullptr, n_seqs, hkv, nwg, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, dec_unroll<TK>(), TK>), dim3(nwg),
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
                      static_cast<const TK*>(k_cache), static_cast<const TK*>(v_cache), ctx_len,
-                     max_ctx, n_seqs, hq, hkv, uidx, umask, uwidth, scale * kLog2e, ws, ws_ml,
-                     ws_acc, table, table_width, num_pages, kscale, vscale);
-  e = hipGetLastError();
+                     max_ctx, n_seqs, hq, hkv, uidx, ucnt, umask, uwidth, scale * kLog2e, nwg, ws,
+                     ws_ml, ws_acc, table, table_width, num_pages, kscale, vscale);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(hq, n_seqs), dim3(D), 0, st, n_seqs,
                      hq, hkv, ws, ws_ml, ws_acc, static_cast<T*>(out), lse);
