@@ -424,3 +424,83 @@ def test_decode_paged_fp8(d, B, hq, hkv, lens, share):
                  else (lambda s, h: np.arange(-(-lens[s] // B))))
         _check_decode_rows(f64(out), f64(lse), f64(q), Kh, Vh, lens, lists, B, d, grp,
                            TOL_ATTN_BF16)
+
+
+def test_decode_snapshot_resume_bit_identical():
+    """The decode state (sketch caches, running block sums, walk rows) is plain
+    device memory: a copy taken after some steps, restored, and stepped again
+    reproduces every later output bit for bit (no order-dependent atomics or
+    hidden state in the kernels)."""
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=8, hkv=2, k=32)
+    B, d, kd, hq, hkv = cfg.B, cfg.d, cfg.k, cfg.hq, cfg.hkv
+    prefixes, steps, n_layers, rho = (190, 250), 20, 2, 30
+    ns = len(prefixes)
+    max_ctx = max(prefixes) + steps
+    b_max = -(-max_ctx // B)
+    signs, cols = gen.hadamard_tables(d, kd)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    layers = []
+    for l in range(n_layers):
+        full = [{w: gen.seq_tensor(cfg, l, s, w, prefixes[s] + steps, "cuda") for w in "qkv"}
+                for s in range(ns)]
+        kc = torch.zeros((ns, max_ctx, hkv, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        st = {"qsk": torch.zeros((ns, hq, b_max, kd), device="cuda"),
+              "ksk": torch.zeros((ns, hkv, b_max, kd), device="cuda"),
+              "rq": torch.zeros((ns, hq, d), device="cuda"),
+              "rk": torch.zeros((ns, hkv, d), device="cuda"),
+              "r": torch.zeros((ns, hq, b_max), device="cuda")}
+        for s, P in enumerate(prefixes):
+            kc[s, :P + steps] = full[s]["k"]
+            vc[s, :P + steps] = full[s]["v"]
+            geo = sws.Geometry([P], B)
+            sq = torch.empty((hq, geo.total_blocks, d), device="cuda")
+            sk = torch.empty((hkv, geo.total_blocks, d), device="cuda")
+            sws.sketch(full[s]["q"][:P].contiguous(), geo, kd, sd, cd, out=st["qsk"][s],
+                       ld_head=b_max * kd, sum_out=sq)
+            sws.sketch(full[s]["k"][:P].contiguous(), geo, kd, sd, cd, out=st["ksk"][s],
+                       ld_head=b_max * kd, sum_out=sk)
+            if P % B:
+                st["rq"][s] = sq[:, -1]
+                st["rk"][s] = sk[:, -1]
+        layers.append({"full": full, "kc": kc, "vc": vc, "st": st})
+    P_t = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+
+    def step(t):
+        pos = P_t + t
+        cur = pos // B
+        outs = []
+        for l, L in enumerate(layers):
+            st = L["st"]
+            qn = torch.stack([L["full"][s]["q"][prefixes[s] + t] for s in range(ns)]).contiguous()
+            kn = torch.stack([L["full"][s]["k"][prefixes[s] + t] for s in range(ns)]).contiguous()
+            sws.sketch_append(qn, pos, B, kd, sd, cd, st["rq"], st["qsk"])
+            sws.sketch_append(kn, pos, B, kd, sd, cd, st["rk"], st["ksk"])
+            sws.walk_update_row(st["qsk"], st["ksk"], cur, cfg.s,
+                                None if l == 0 else layers[l - 1]["st"]["r"], st["r"])
+            u = sws.select_topk_row(st["r"], hq, hkv, cur, b_max, rho, per_head=True)
+            lse = torch.empty((ns, hq), device="cuda")
+            out = sws.sparse_attn_decode(qn, L["kc"], L["vc"], pos + 1, B, u[0], u[1], u[2],
+                                         lse=lse)
+            # list entries past each count are unspecified: keep the defined ones
+            uidx, ucnt, umask, idx, cnt = [x.cpu() for x in u]
+            lists = [(uidx[s_, g, :ucnt[s_, g]], umask[s_, g, :ucnt[s_, g]])
+                     for s_ in range(ns) for g in range(hkv)]
+            lists += [idx[s_, h, :cnt[s_, h]] for s_ in range(ns) for h in range(hq)]
+            outs.append([st["r"].clone(), ucnt, cnt, out, lse,
+                         *[x for pair in lists[:ns * hkv] for x in pair], *lists[ns * hkv:]])
+        return outs
+
+    for t in range(8):
+        step(t)
+    snap = [{k: v.clone() for k, v in L["st"].items()} for L in layers]
+    first = [step(t) for t in range(8, steps)]
+    for L, sn in zip(layers, snap):
+        for k, v in sn.items():
+            L["st"][k].copy_(v)
+    second = [step(t) for t in range(8, steps)]
+    torch.cuda.synchronize()
+    for a_t, b_t in zip(first, second):
+        for a_l, b_l in zip(a_t, b_t):
+            for x, y in zip(a_l, b_l):
+                assert torch.equal(x, y)
