@@ -5,15 +5,15 @@
 // bf16 path: one workgroup per (query head, query block of B tokens), B/32
 // wavefronts, each owning 32 query rows.  A pre-pass writes V transposed per
 // block (keys in accumulator-row order) to a workspace.  The selected key
-// blocks are walked in steps of 32 keys: the K and V^T tiles
-// of the next step are loaded into registers while the current step
-// computes, then stored into the other half of a double-buffered, XOR-swizzled
-// LDS tile pair (one barrier per step).  Each wave runs a FlashAttention-style
+// blocks are walked in steps of 32 keys: the K and V^T tiles of the next step
+// stream from memory straight into the other half of a double-buffered,
+// XOR-swizzled LDS tile pair while the current step computes (one barrier per
+// step).  Each wave runs a FlashAttention-style
 // step on the matrix cores with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T          (A = K rows from LDS, B = this wave's Q in registers)
-//   online softmax       (a lane holds one query column: the row max over the
-//                         step is 16 in-register values plus one cross-lane
-//                         exchange with the other half-wave)
+//   online softmax       (a lane holds one query column; the reference max
+//                         is fixed after a query block's first step and only
+//                         raised if the running sum nears overflow)
 //   O^T += V^T P^T       (A = V^T from LDS, B = P^T straight from the S^T
 //                         accumulators rounded to bf16; V^T's key order in LDS
 //                         is permuted to match the accumulator layout, so P
@@ -23,8 +23,8 @@
 // longest list first, and the query heads of one KV head are mapped to the same
 // XCD (workgroup id modulo 8) so their shared K/V blocks meet in one L2.  For
 // B = 128 the register budget is capped so three waves share each SIMD (the
-// short 32-key steps keep the score and staging registers small); the extra
-// wave hides more of the softmax and load latency behind other waves' MFMAs.
+// short 32-key steps keep the score registers small); the extra wave hides
+// more of the softmax and load latency behind other waves' MFMAs.
 //
 // fp32 path: a plain kernel, one thread per query row, key-by-key online
 // softmax with K/V tiles staged in LDS; it exists for tight-tolerance checks.
@@ -121,12 +121,14 @@ __device__ __forceinline__ float max_halves(float v) {
   return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
 }
 
-// Softmax reference lag: the running maximum used for the exponentials is
-// only raised when a new score exceeds it by more than this many powers of
-// two, so most steps skip the rescale of the output accumulators.  The
-// weights stay below 2^8, and numerator, denominator and log-sum-exp all use
-// the same reference, so the result is unchanged.
-constexpr float kMaxLag = 8.0f;
+// Softmax reference: after the first step of a query block the reference m
+// used for the exponentials stays fixed, and the weights exp2(s - m) are
+// formed without the step's column maximum; only when the running sum could
+// overflow (it passes 2^100, or is not finite) is the step redone with the
+// maximum and a rescale of the output accumulators.  Numerator, denominator
+// and log-sum-exp all use the same reference, so the result is unchanged up to
+// rounding (fp32 and bf16 keep the same relative precision at any exponent).
+constexpr float kSumLimit = 0x1p100f;
 
 // One pipeline step: KT keys of the current block against this wave's 32
 // query rows.  ksb / vsb are the step's K and V^T tiles in LDS.
@@ -161,7 +163,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
-  // ---- causal mask (diagonal block only) and the step's row maximum ----
+  // ---- causal mask (diagonal block only) ----
   if (diag) {
 #pragma unroll
     for (int kt = 0; kt < KT / 32; ++kt)
@@ -171,40 +173,51 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
         if (key > qi) st[kt][r] = -INFINITY;
       }
   }
-  float mx = st[0][0];
+  // ---- P = exp2(S * scale - m), bf16; row sum from the same bf16 values ----
+  // (the first step of a query block takes the column maximum)
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8_t pb[KT / 16];
+  auto exp_step = [&](float& l_acc) {
 #pragma unroll
-  for (int kt = 0; kt < KT / 32; ++kt)
+    for (int kc = 0; kc < KT / 16; ++kc) {
+      const int kt = kc >> 1;
+      const int r0 = (kc & 1) * 8;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
-  mx = max_halves(mx);
-  const float m_cand = mx * scale_log2;
-  if (__any(m_cand > m_run + kMaxLag)) {
-    const float m_new = fmaxf(m_run, m_cand);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      for (int e = 0; e < 8; e += 2) {
+        bf16x2_t pr;
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e], scale_log2, -m_run));
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e + 1], scale_log2, -m_run));
+        l_acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_acc, false);
+        pb[kc][e] = pr[0];
+        pb[kc][e + 1] = pr[1];
+      }
+    }
+  };
+  float l_new = l_run;
+  bool redo = m_run == -INFINITY;
+  if (!redo) {
+    exp_step(l_new);
+    redo = __any(!(l_new < kSumLimit));
+  }
+  if (redo) {
+    float mx = st[0][0];
+#pragma unroll
+    for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     m_run = m_new;
+    l_new = l_run;
+    exp_step(l_new);
   }
-  // ---- P = exp2(S * scale - m), bf16; row sum from the same bf16 values ----
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8_t pb[KT / 16];
-#pragma unroll
-  for (int kc = 0; kc < KT / 16; ++kc) {
-    const int kt = kc >> 1;
-    const int r0 = (kc & 1) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      bf16x2_t pr;
-      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e], scale_log2, -m_run));
-      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e + 1], scale_log2, -m_run));
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-      pb[kc][e] = pr[0];
-      pb[kc][e + 1] = pr[1];
-    }
-  }
+  l_run = l_new;
   // ---- O^T += V^T P^T ----
 #pragma unroll
   for (int kc = 0; kc < KT / 16; ++kc) {
