@@ -75,7 +75,7 @@ int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_
   if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
   if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
   if (k < 1 || k > d || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1, min(d,64)]", fn, k);
-  if (n_seqs < 1 || total_blocks < 0 || n_heads < 1)
+  if (n_seqs < 0 || total_blocks < 0 || n_heads < 1 || (n_seqs == 0 && total_blocks != 0))
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d n_heads=%d", fn, n_seqs, total_blocks, n_heads);
   if (ld_head < (int64_t)total_blocks * k)
     return fail(SWS_ERR_SHAPE, "%s: ld_head=%lld < total_blocks*k", fn, (long long)ld_head);
@@ -123,7 +123,8 @@ int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hk
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
   if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
-  if (n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+  if (n_seqs < 0 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks ||
+      (n_seqs == 0 && total_blocks != 0))
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d max_blocks=%d", fn, n_seqs, total_blocks, max_blocks);
   if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
   return launched(sws::launch_walk(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks,
@@ -171,7 +172,8 @@ int sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, in
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
   if (k < 1 || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1,64]", fn, k);
-  if (n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+  if (n_seqs < 0 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks ||
+      (n_seqs == 0 && total_blocks != 0))
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d max_blocks=%d", fn, n_seqs, total_blocks, max_blocks);
   if (max_blocks > 4096) return fail(SWS_ERR_UNSUPPORTED, "%s: max_blocks=%d > 4096", fn, max_blocks);
   if (s < 1) return fail(SWS_ERR_SHAPE, "%s: s=%d must be >= 1", fn, s);
@@ -228,7 +230,8 @@ static int select_topk_impl(const char* fn, const float* R, int32_t hq, int32_t 
   REQUIRE_PTR(cnt);
   if (flags & ~(SWS_SELECT_DENSE | SWS_SELECT_ROW_TAU | SWS_SELECT_GROUP))
     return fail(SWS_ERR_SHAPE, "%s: unknown flags 0x%x", fn, flags);
-  if (hq < 1 || n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+  if (hq < 1 || n_seqs < 0 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks ||
+      (n_seqs == 0 && total_blocks != 0))
     return fail(SWS_ERR_SHAPE, "%s: hq=%d n_seqs=%d total_blocks=%d max_blocks=%d", fn, hq, n_seqs, total_blocks, max_blocks);
   if (hkv < 1 || hq % hkv != 0)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
@@ -313,7 +316,8 @@ int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dty
   if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(SWS_ERR_SHAPE, "%s: hq=%d hkv=%d (hq must be a multiple of hkv)", fn, hq, hkv);
-  if (n_seqs < 1 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks)
+  if (n_seqs < 0 || total_blocks < 0 || max_blocks < 0 || max_blocks > total_blocks ||
+      (n_seqs == 0 && total_blocks != 0))
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d total_blocks=%d max_blocks=%d", fn, n_seqs, total_blocks, max_blocks);
   if ((int64_t)total_blocks * hq > 0x7fffffffLL)
     return fail(SWS_ERR_SHAPE, "%s: total_blocks*hq too large", fn);

@@ -27,6 +27,8 @@
  *   cu_seqlens[s] is the first token of sequence s (cu_seqlens[n_seqs] = T)
  *   and cu_blocks[s] its first block (b_s = ceil(n_s / B) blocks; blocks never
  *   straddle sequences).
+ * - An empty batch (n_seqs = 0, and then total_blocks = 0) is valid: the
+ *   call returns SWS_OK and launches nothing.
  * - GQA: query head h reads KV head h / (hq / hkv).
  * - The library holds no state and no random generator: the Hadamard sign
  *   vector and column subset are inputs.
