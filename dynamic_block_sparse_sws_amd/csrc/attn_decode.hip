@@ -2,14 +2,16 @@
 // Attend", section 5: the same block selection for every decode step; section
 // 8.3: decode is bound by reading the KV cache).
 //
-// Split-KV over the union lists of all (sequence, KV head) pairs at once: a
-// plan kernel numbers the blocks to read across the pairs and cuts them into
-// equal ranges, one per workgroup; each workgroup computes, for all query
-// heads of the group that kept each block, the partial softmax state (max,
-// sum, weighted V sum) of every pair its range touches.  K rows are read once,
-// as 16-byte vectors, and dotted with every kept head's query; V rows are read
-// once and accumulated for every kept head.  A combine kernel merges the
-// partial states of each pair with the usual log-sum-exp rescaling.
+// Split-KV over the union lists of all (sequence, KV head) pairs at once: the
+// blocks to read across the pairs are numbered and cut into equal ranges, one
+// per workgroup; each workgroup computes, for all query heads of the group
+// that kept each block, the partial softmax state (max, sum, weighted V sum)
+// of every pair its range touches, reading every K and V row once for the
+// whole group.  A combine kernel merges the partial states of each pair with
+// the usual log-sum-exp rescaling.  bf16 queries (bf16 or fp8 e4m3 caches,
+// contiguous or paged) run the matrix-core split kernel; fp32 queries run a
+// vector-ALU split kernel (16-byte row loads, dot products per head, DPP
+// reductions) kept for tight-tolerance checks.
 #include "sws_common.h"
 
 #include <algorithm>
@@ -22,9 +24,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
-// fp8 rows are 8 bytes a lane: twice the rows per batch keeps the same bytes
-// in flight per wave as bf16 (the loop is latency-bound below that).
-template <typename TK> constexpr int dec_unroll() { return sizeof(TK) == 1 ? 2 * kDecUnroll : kDecUnroll; }
+
 
 // Sum over the TPL consecutive lanes that share a token row (TPL in {8, 16}),
 // with DPP lane permutes: swap neighbours, swap pairs, mirror within 8, mirror
@@ -63,22 +63,6 @@ template <> struct Row8<float> {
   }
 };
 
-// fp8 rows (OCP e4m3, 8 bytes per lane), decoded with v_cvt_pk_f32_fp8; the
-// per-tensor scales are applied by the caller (K's to the score, V's to the
-// partial output).
-template <> struct Row8<uint8_t> {
-  uint2 r;
-  __device__ __forceinline__ void load(const uint8_t* p) { r = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void get(float* o) const {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, true);
-    o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
-    o[4] = c[0]; o[5] = c[1]; o[6] = d[0]; o[7] = d[1];
-  }
-};
-
 // A query head's 8 features of this lane, and its dot product with a K row:
 // bf16 pairs through v_dot2_f32_bf16 (exact products, fp32 sums), fp32 with
 // plain fused multiply-adds.
@@ -114,31 +98,6 @@ template <> struct QVec<float> {
 #pragma unroll
     for (int x = 0; x < 8; ++x) a += v[x] * kf[x];
     return a;
-  }
-};
-
-// bf16 query against fp8 keys: the codes widened to bf16 (exact: e4m3 is a
-// subset of bf16) and multiplied with v_dot2_f32_bf16 like bf16 keys; the K
-// scale is applied to the score.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-struct QVecF8 {
-  uint4 r;
-  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void zero() { r = make_uint4(0u, 0u, 0u, 0u); }
-  template <bool HI> __device__ __forceinline__ static bf16x2_t pair(uint32_t w) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-    return __builtin_convertvector((f32x2_t){f[0], f[1]}, bf16x2_t);
-  }
-  __device__ __forceinline__ float dot(const Row8<uint8_t>& k) const {
-    float a = __builtin_amdgcn_fdot2_f32_bf16(pair<false>(k.r.x),
-                                              __builtin_bit_cast(bf16x2_t, r.x), 0.f, false);
-    float b = __builtin_amdgcn_fdot2_f32_bf16(pair<true>(k.r.x),
-                                              __builtin_bit_cast(bf16x2_t, r.y), 0.f, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(pair<false>(k.r.y), __builtin_bit_cast(bf16x2_t, r.z), a,
-                                        false);
-    b = __builtin_amdgcn_fdot2_f32_bf16(pair<true>(k.r.y), __builtin_bit_cast(bf16x2_t, r.w), b,
-                                        false);
-    return a + b;
   }
 };
 
@@ -259,8 +218,8 @@ __device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
 // through lane exchanges, waves through LDS.
 // KV addressing: contiguous caches [n_seqs][max_ctx][hkv][d] (table == null),
 // or pages of BLK tokens [num_pages][BLK][hkv][d] with table[seq][logical
-// block] giving the page.  TK is the cache element type (bf16, fp32, or fp8
-// e4m3 codes with per-tensor scales kscale / vscale).
+// block] giving the page.  TK is the cache element type (the query type
+// here); kscale / vscale are per-tensor scales (1 for plain caches).
 template <typename T, int D, int BLK, int GMAX, int UNR, typename TK = T>
 __device__ __forceinline__ void decode_range(
     const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
@@ -269,7 +228,7 @@ __device__ __forceinline__ void decode_range(
     int a, int b, int r, float scale_log2, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, const int32_t* __restrict__ table = nullptr, int table_width = 0,
     int num_pages = 0, float kscale = 1.0f, float vscale = 1.0f) {
-  using QV = typename std::conditional<std::is_same<TK, uint8_t>::value, QVecF8, QVec<T>>::type;
+  using QV = QVec<T>;
   constexpr int TPL = D / 8;                   // lanes per token row
   constexpr int RPW = 64 / TPL;                // token rows per wave-wide load
   constexpr int TPB = RPW * UNR;               // tokens per wave batch
@@ -426,7 +385,7 @@ __device__ __forceinline__ void decode_range(
 // Split kernel: workgroup w reads blocks [w W / NWG, (w + 1) W / NWG) of the
 // concatenated pair lists, one record per pair the range touches.
 template <typename T, int D, int BLK, int GMAX, int UNR, typename TK>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
     const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucnt,
@@ -472,6 +431,306 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))
     decode_range<T, D, BLK, GMAX, UNR, TK>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask,
                                            uwidth, p, a, b, w + p, scale_log2, ws_ml, ws_acc,
                                            table, table_width, num_pages, kscale, vscale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core form of the split kernel (bf16 queries; bf16 or fp8 e4m3 KV).
+// Same plan and records as decode_split_kernel.  A wave takes 32-key steps
+// of its workgroup's range (steps w, w + 4, ...) and, per step, with
+// v_mfma_f32_16x16x32_bf16 (16 columns = the group's query heads, zero past G):
+//   S^T = K Q^T   two 16-key tiles; A = K rows straight from memory (lane l:
+//                 key l % 16 of the tile, 8 features of group l / 16 of each
+//                 32-feature chunk), B = the queries;
+//   V^T           the step's V rows go to the wave's LDS area transposed
+//                 (features as rows, keys in the order of the S^T
+//                 accumulators, so P needs no lane exchange);
+//   softmax       a lane holds 8 scores of one head; the step's max per head
+//                 is two lane exchanges;
+//   O^T += V^T P^T  one 32-key product per 16-feature tile of O^T.
+// The K and V loads of a wave's next step are issued before the current step
+// computes, so every wave keeps a step of rows in flight.
+// fp8 rows are widened to bf16 (exact) before use; the K scale multiplies the
+// scores and the V scale the record.  The waves merge in LDS at the end of
+// each pair's range.
+// ---------------------------------------------------------------------------
+constexpr int kVtStride = 40;            // V^T row: 32 key slots + 8 pad (80 bytes)
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// Slot of key k (0..31 within a step) in a V^T row: the B operand of the
+// V product takes slots 8 j .. 8 j + 7 from lane group j, which holds the
+// scores of keys 4 j .. 4 j + 3 (first tile) and 16 + 4 j .. 16 + 4 j + 3.
+__device__ __forceinline__ int vt_slot(int k) {
+  return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
+}
+
+template <typename TK> struct KvFrag;
+template <> struct KvFrag<uint16_t> {
+  uint4 r;
+  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ bf16x8_t bf() const { return __builtin_bit_cast(bf16x8_t, r); }
+};
+template <> struct KvFrag<uint8_t> {
+  uint2 r;
+  __device__ __forceinline__ void load(const uint8_t* p) { r = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ bf16x8_t bf() const {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, true);
+    typedef float f32x8_t __attribute__((ext_vector_type(8)));
+    const f32x8_t f = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return __builtin_convertvector(f, bf16x8_t);
+  }
+};
+
+template <int D, int BLK, typename TK>
+__device__ __forceinline__ void mfma_range(
+    const uint16_t* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
+    const int32_t* __restrict__ ctx_len, int max_ctx, int hq, int hkv,
+    const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth, int p,
+    int a, int b, int r, float scale_log2, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, const int32_t* __restrict__ table, int table_width,
+    int num_pages, float kscale, float vscale, __bf16* vt_all, float* mw, float* lw) {
+  constexpr int NWV = kDecThreads / 64;
+  constexpr int KT = 32;
+  constexpr int DC = D / 32;                  // 32-feature chunks (QK operands)
+  constexpr int DT = D / 16;                  // 16-feature tiles of O^T
+  static_assert(BLK % KT == 0, "a step stays inside one block");
+  const int seq = p / hkv;
+  const int g = p % hkv;
+  const int G = hq / hkv;
+  const int ctx = max(ctx_len[seq], 1);
+  const int last_blk = (ctx - 1) / BLK;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const float sl2 = scale_log2 * kscale;
+  __bf16* vt = vt_all + wave * D * kVtStride;
+  const int64_t rstride = (int64_t)hkv * D;
+  const int64_t seq_off = table ? 0 : ((int64_t)seq * max_ctx) * rstride;
+  const TK* kb = kc + seq_off + (int64_t)g * D + grp * 8;
+  const TK* vb = vc + seq_off + (int64_t)g * D + grp * 8;
+  const int32_t* trow = table ? table + (int64_t)seq * table_width : nullptr;
+  const int32_t* ul = uidx ? uidx + (int64_t)p * uwidth : nullptr;
+  const uint32_t* um = umask ? umask + (int64_t)p * uwidth : nullptr;
+
+  // the group's queries as B operand columns (heads past G are zero)
+  bf16x8_t qf[DC];
+  {
+    const bool hv = col < G;
+    const uint16_t* qp = q + ((int64_t)seq * hq + g * G + min(col, G - 1)) * D + grp * 8;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + c * 32);
+      qf[c] = __builtin_bit_cast(bf16x8_t, hv ? raw : make_uint4(0u, 0u, 0u, 0u));
+    }
+  }
+  floatx4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) o[dt][x] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  int slot[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) slot[kt] = vt_slot(kt * 16 + col);
+
+  const int nstep = (b - a) * (BLK / KT);
+  // loads of step t (rows, block mask and first key), issued one step ahead
+  auto issue = [&](int t, KvFrag<TK> (&kf)[2][DC], KvFrag<TK> (&vf)[2][DC], uint32_t& mk,
+                   int& key0) {
+    const int tt = min(t, nstep - 1);
+    const int e = a + tt / (BLK / KT);
+    const int blk = min(max(ul ? ul[e] : e, 0), last_blk);
+    mk = um ? um[e] : 0xffffffffu;
+    key0 = blk * BLK + (tt % (BLK / KT)) * KT;
+    int64_t pbase = 0;
+    if (trow) {
+      const int pg = min(max(trow[min(blk, table_width - 1)], 0), num_pages - 1);
+      pbase = ((int64_t)pg - blk) * BLK;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int64_t row = pbase + min(key0 + kt * 16 + col, ctx - 1);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        kf[kt][c].load(kb + row * rstride + c * 32);
+        vf[kt][c].load(vb + row * rstride + c * 32);
+      }
+    }
+  };
+  KvFrag<TK> kn[2][DC], vn[2][DC];
+  uint32_t mk_n;
+  int key0_n;
+  if (wave < nstep) issue(wave, kn, vn, mk_n, key0_n);
+  for (int t = wave; t < nstep; t += NWV) {
+    KvFrag<TK> kf[2][DC], vf[2][DC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        kf[kt][c] = kn[kt][c];
+        vf[kt][c] = vn[kt][c];
+      }
+    const uint32_t mk = mk_n;
+    const int key0 = key0_n;
+    if (t + NWV < nstep) issue(t + NWV, kn, vn, mk_n, key0_n);
+    // S^T = K Q^T, two 16-key tiles
+    floatx4_t st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) st[kt][x] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][c].bf(), qf[c], st[kt], 0, 0, 0);
+    }
+    // V^T of the step into this wave's LDS area
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8_t v = vf[kt][c].bf();
+#pragma unroll
+        for (int x = 0; x < 8; ++x) vt[(c * 32 + grp * 8 + x) * kVtStride + slot[kt]] = v[x];
+      }
+    // mask (keys past the context, heads that did not keep the block), the
+    // step's max per head
+    const bool head_ok = col < G && ((mk >> col) & 1u);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int key = key0 + kt * 16 + grp * 4 + x;
+        st[kt][x] = (head_ok && key < ctx) ? st[kt][x] * sl2 : -INFINITY;
+        mx = fmaxf(mx, st[kt][x]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    if (__any(m_new > m)) {
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o[dt][x] *= alpha;
+      m = m_new;
+    }
+    bf16x8_t pb;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      bf16x2_t pr;
+      const float s0 = st[i >> 2][i & 3], s1 = st[i >> 2][(i & 3) + 1];
+      pr[0] = (__bf16)(s0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s0 - m));
+      pr[1] = (__bf16)(s1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s1 - m));
+      l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+      pb[i] = pr[0];
+      pb[i + 1] = pr[1];
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8_t av =
+          *reinterpret_cast<const bf16x8_t*>(vt + (dt * 16 + col) * kVtStride + grp * 8);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[dt], 0, 0, 0);
+    }
+  }
+  // ---- merge the waves' states and write record r ----
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  __syncthreads();                            // every wave is done with its V^T area
+  if (grp == 0) {
+    mw[wave * 16 + col] = m;
+    lw[wave * 16 + col] = l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w2 = 0; w2 < NWV; ++w2) M = fmaxf(M, mw[w2 * 16 + col]);
+  const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  // scaled O^T of this wave into LDS (the V^T area): acc[wave][head][feature]
+  float* acc = reinterpret_cast<float*>(vt_all);
+  if (col < G) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[(wave * 16 + col) * D + dt * 16 + grp * 4 + x] = o[dt][x] * f;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kDecThreads) {
+    const int h = i / D, d = i % D;
+    float s = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWV; ++w2) s += acc[(w2 * 16 + h) * D + d];
+    ws_acc[((int64_t)r * G + h) * D + d] = s * vscale;
+    if (d == 0) {
+      float Mh = -INFINITY, Lh = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NWV; ++w2) Mh = fmaxf(Mh, mw[w2 * 16 + h]);
+#pragma unroll
+      for (int w2 = 0; w2 < NWV; ++w2) {
+        const float mv = mw[w2 * 16 + h];
+        Lh += mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - Mh) * lw[w2 * 16 + h];
+      }
+      ws_ml[((int64_t)r * G + h) * 2 + 0] = Mh;
+      ws_ml[((int64_t)r * G + h) * 2 + 1] = Lh;
+    }
+  }
+  __syncthreads();                            // the LDS areas are reused by the next range
+}
+
+template <int D, int BLK, typename TK>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
+    const uint16_t* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
+    const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
+    const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucnt,
+    const uint32_t* __restrict__ umask, int uwidth, float scale_log2, int nwg_launched,
+    void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    const int32_t* __restrict__ table, int table_width, int num_pages, float kscale,
+    float vscale) {
+  constexpr int NWV = kDecThreads / 64;
+  __shared__ int32_t spre[kDecMaxPairs + 1];
+  __shared__ int wtot[NWV];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_all[NWV * D * kVtStride];
+  __shared__ float mw[NWV * 16], lw[NWV * 16];
+  static_assert(NWV * D * kVtStride * 2 >= NWV * 16 * D * 4, "merge area fits in V^T area");
+  const int P = n_seqs * hkv;
+  const int64_t W = build_plan<BLK, kDecThreads>(ctx_len, uidx ? ucnt : nullptr, P, hkv, spre,
+                                                 wtot);
+  const int nwg = (int)std::min<int64_t>(nwg_launched, std::max<int64_t>(W, 1));
+  const int w = blockIdx.x;
+  if (w == 0) {
+    int32_t* pre = plan_pre(ws);
+    for (int p = threadIdx.x; p <= P; p += kDecThreads) pre[p] = spre[p];
+    if (threadIdx.x == 0) *plan_nwg(ws) = nwg;
+  }
+  if (w >= nwg) return;
+  const int64_t lo = range_lo(w, W, nwg);
+  const int64_t hi = range_lo(w + 1, W, nwg);
+  if (lo >= hi) return;
+  int p = 0;
+  {
+    int h = P - 1;
+    while (p < h) {
+      const int m = (p + h + 1) >> 1;
+      if (spre[m] <= lo) p = m;
+      else h = m - 1;
+    }
+  }
+  for (; p < P; ++p) {
+    const int A = spre[p];
+    if (A >= hi) break;
+    const int Bn = spre[p + 1];
+    const int a = (int)(max(lo, (int64_t)A) - A);
+    const int b = (int)(min(hi, (int64_t)Bn) - A);
+    if (a >= b) continue;
+    mfma_range<D, BLK, TK>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask, uwidth, p, a, b,
+                           w + p, scale_log2, ws_ml, ws_acc, table, table_width, num_pages,
+                           kscale, vscale, vt_all, mw, lw);
   }
 }
 
@@ -580,11 +839,19 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
   const int nwg = split_workgroups();
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan_bytes(P));
   float* ws_acc = ws_ml + (size_t)(P + kDecMaxWG) * G * 2;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, dec_unroll<TK>(), TK>), dim3(nwg),
-                     dim3(kDecThreads), 0, st, static_cast<const T*>(q),
-                     static_cast<const TK*>(k_cache), static_cast<const TK*>(v_cache), ctx_len,
-                     max_ctx, n_seqs, hq, hkv, uidx, ucnt, umask, uwidth, scale * kLog2e, nwg, ws,
-                     ws_ml, ws_acc, table, table_width, num_pages, kscale, vscale);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BLK, TK>), dim3(nwg), dim3(kDecThreads), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const TK*>(k_cache),
+                       static_cast<const TK*>(v_cache), ctx_len, max_ctx, n_seqs, hq, hkv, uidx,
+                       ucnt, umask, uwidth, scale * kLog2e, nwg, ws, ws_ml, ws_acc, table,
+                       table_width, num_pages, kscale, vscale);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, kDecUnroll, TK>), dim3(nwg),
+                       dim3(kDecThreads), 0, st, static_cast<const T*>(q),
+                       static_cast<const TK*>(k_cache), static_cast<const TK*>(v_cache), ctx_len,
+                       max_ctx, n_seqs, hq, hkv, uidx, ucnt, umask, uwidth, scale * kLog2e, nwg,
+                       ws, ws_ml, ws_acc, table, table_width, num_pages, kscale, vscale);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(hq, n_seqs), dim3(D), 0, st, n_seqs,
