@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the decode steps replayed as HIP graphs")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the paged / fp8 KV decode-attention timings")
     ap.add_argument("--sweep", action="store_true", help="also time rho = 10, 30, 100")
@@ -245,11 +247,18 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         state.append({"qst": qst, "knew": knew, "kc": kc, "vc": vc, "qsk": qsk, "ksk": ksk,
                       "rq": rq, "rk": rk, "out": torch.empty((ns, hq, d), dtype=qst.dtype,
                                                              device="cuda")})
+    # every layer's new-token q and k in one tensor each, so one copy stages a
+    # step's inputs for all layers (the graph replay below)
+    q_all = torch.stack([st_["qst"] for st_ in state])            # [L, steps, ns, hq, d]
+    k_all = torch.stack([st_["knew"] for st_ in state])           # [L, steps, ns, hkv, d]
+    for l, st_ in enumerate(state):
+        st_["qst"], st_["knew"] = q_all[l], k_all[l]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     pos = torch.arange(P, P + steps, dtype=torch.int32, device="cuda")[:, None].expand(steps, ns).contiguous()
     cur = (pos // B).contiguous()
     ctx_len = (pos + 1).contiguous()
+    snap = [{k_: st_[k_].clone() for k_ in ("qsk", "ksk", "rq", "rk")} for st_ in state]
     uw = sws.union_width(cfg.rho, b_max, hq // hkv)
     ubufs = (torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"),
              torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
@@ -313,6 +322,55 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         "per_head_blocks": cfg.rho * (b_max - 1) // 100 + 1,
         "setup_s": setup_s,
     }
+    if not args.no_graph:
+        # The same steps again from the same starting state, each step one
+        # HIP graph replay of all layers' kernels (captured once on static
+        # buffers) after one copy of the step's q, k and positions into them.
+        for st_, sn in zip(state, snap):
+            for k_, v_ in sn.items():
+                st_[k_].copy_(v_)
+        del snap
+        q_buf = torch.empty_like(q_all[:, 0])
+        k_buf = torch.empty_like(k_all[:, 0])
+        pcc_all = torch.stack([pos, cur, ctx_len], dim=1).contiguous()   # [steps, 3, ns]
+        pcc = torch.empty_like(pcc_all[0])
+
+        def graph_step():
+            for l, st in enumerate(state):
+                dense = l < cfg.n_dense
+                sws.sketch_append(q_buf[l], pcc[0], B, kd, signs_d, cols_d, st["rq"], st["qsk"])
+                sws.sketch_append(k_buf[l], pcc[0], B, kd, signs_d, cols_d, st["rk"], st["ksk"])
+                sws.walk_update_row(st["qsk"], st["ksk"], pcc[1], cfg.s, None if l == 0 else r, r)
+                u = sws.select_topk_row(r, hq, hkv, pcc[1], b_max, cfg.rho, dense=dense,
+                                        out=dbufs if dense else ubufs)
+                sws.sparse_attn_decode(q_buf[l], st["kc"], st["vc"], pcc[2], B, u[0], u[1], u[2],
+                                       out=st["out"], ws=ws)
+
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            graph_step()
+
+        def stage(t):
+            q_buf.copy_(q_all[:, t])
+            k_buf.copy_(k_all[:, t])
+            pcc.copy_(pcc_all[t])
+
+        stage(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(1, steps):
+            stage(t)
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res["us_per_step_eager"] = res["us_per_step"]
+        res["us_per_step"] = e0.elapsed_time(e1) * 1e3 / timed
+        res["graph"] = "one HIP graph per step (all layers), inputs staged by 3 copies"
+        del graph
     if not args.no_serving:
         res["serving_layouts"] = serving_layouts(torch, sws, gen, state[-1], ubufs, ctx_len[-1],
                                                  B, steps - 1)

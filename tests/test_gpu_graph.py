@@ -1,0 +1,113 @@
+"""Decode steps captured once as a HIP graph (torch.cuda.CUDAGraph over the
+library's launches on static buffers) and replayed step after step, with
+eager work and synchronisations between the replays: every replay's outputs
+equal the eager calls' bit for bit."""
+import pytest
+import torch
+
+import dynamic_block_sparse_sws_amd as sws
+import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_step_graph_replays_equal_eager():
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=8, hkv=2, k=32)
+    B, d, kd, hq, hkv = cfg.B, cfg.d, cfg.k, cfg.hq, cfg.hkv
+    prefixes, steps, rho = (190, 250), 8, 30
+    ns, n_layers = len(prefixes), 2
+    max_ctx = max(prefixes) + steps
+    b_max = -(-max_ctx // B)
+    signs, cols = gen.hadamard_tables(d, kd)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    layers = []
+    for l in range(n_layers):
+        full = [{w: gen.seq_tensor(cfg, l, s, w, prefixes[s] + steps, "cuda") for w in "qkv"}
+                for s in range(ns)]
+        kc = torch.zeros((ns, max_ctx, hkv, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        st = {"qsk": torch.zeros((ns, hq, b_max, kd), device="cuda"),
+              "ksk": torch.zeros((ns, hkv, b_max, kd), device="cuda"),
+              "rq": torch.zeros((ns, hq, d), device="cuda"),
+              "rk": torch.zeros((ns, hkv, d), device="cuda")}
+        for s, P in enumerate(prefixes):
+            kc[s, :P + steps] = full[s]["k"]
+            vc[s, :P + steps] = full[s]["v"]
+            geo = sws.Geometry([P], B)
+            sq = torch.empty((hq, geo.total_blocks, d), device="cuda")
+            sk = torch.empty((hkv, geo.total_blocks, d), device="cuda")
+            sws.sketch(full[s]["q"][:P].contiguous(), geo, kd, sd, cd, out=st["qsk"][s],
+                       ld_head=b_max * kd, sum_out=sq)
+            sws.sketch(full[s]["k"][:P].contiguous(), geo, kd, sd, cd, out=st["ksk"][s],
+                       ld_head=b_max * kd, sum_out=sk)
+            if P % B:
+                st["rq"][s] = sq[:, -1]
+                st["rk"][s] = sk[:, -1]
+        qn = torch.stack([torch.stack([full[s]["q"][prefixes[s] + t] for s in range(ns)])
+                          for t in range(steps)]).contiguous()
+        kn = torch.stack([torch.stack([full[s]["k"][prefixes[s] + t] for s in range(ns)])
+                          for t in range(steps)]).contiguous()
+        layers.append({"kc": kc, "vc": vc, "st": st, "qn": qn, "kn": kn,
+                       "out": torch.empty((ns, hq, d), dtype=torch.bfloat16, device="cuda")})
+    snap = [{k: v.clone() for k, v in L["st"].items()} for L in layers]
+    P_t = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    uw = sws.union_width(rho, b_max, hq // hkv)
+    ubufs = (torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"), None, None)
+    dbufs = (torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
+             torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"), None, None)
+    ws = torch.empty(sws.decode_workspace_size(ns, hq, hkv, d, B, b_max), dtype=torch.uint8,
+                     device="cuda")
+    r = torch.empty((ns, hq, b_max), device="cuda")
+    lse = [torch.empty((ns, hq), device="cuda") for _ in layers]
+
+    def step(q_of, k_of, pos, cur, ctx):
+        for l, L in enumerate(layers):
+            st = L["st"]
+            sws.sketch_append(q_of(l), pos, B, kd, sd, cd, st["rq"], st["qsk"])
+            sws.sketch_append(k_of(l), pos, B, kd, sd, cd, st["rk"], st["ksk"])
+            sws.walk_update_row(st["qsk"], st["ksk"], cur, cfg.s, None if l == 0 else r, r)
+            u = sws.select_topk_row(r, hq, hkv, cur, b_max, rho, dense=l == 0,
+                                    out=dbufs if l == 0 else ubufs)
+            sws.sparse_attn_decode(q_of(l), L["kc"], L["vc"], ctx, B, u[0], u[1], u[2],
+                                   out=L["out"], lse=lse[l], ws=ws)
+
+    def outputs():
+        n_u = ubufs[1].clone()
+        lists = [ubufs[0][s, g, :n_u[s, g]].clone() for s in range(ns) for g in range(hkv)]
+        return [r.clone(), n_u, *lists, *[L["out"].clone() for L in layers],
+                *[x.clone() for x in lse], *[L["st"]["qsk"].clone() for L in layers]]
+
+    eager = []
+    for t in range(steps):
+        pos = P_t + t
+        step(lambda l: layers[l]["qn"][t], lambda l: layers[l]["kn"][t], pos, pos // B, pos + 1)
+        eager.append(outputs())
+    torch.cuda.synchronize()
+
+    # graph on static buffers, replayed from the same starting state
+    for L, sn in zip(layers, snap):
+        for k, v in sn.items():
+            L["st"][k].copy_(v)
+    q_buf = torch.empty_like(torch.stack([L["qn"][0] for L in layers]))
+    k_buf = torch.empty_like(torch.stack([L["kn"][0] for L in layers]))
+    pcc = torch.empty((3, ns), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(lambda l: q_buf[l], lambda l: k_buf[l], pcc[0], pcc[1], pcc[2])
+    for t in range(steps):
+        pos = P_t + t
+        for l, L in enumerate(layers):
+            q_buf[l].copy_(L["qn"][t])
+            k_buf[l].copy_(L["kn"][t])
+        pcc.copy_(torch.stack([pos, pos // B, pos + 1]))
+        graph.replay()
+        junk = torch.randn(1000, device="cuda").sum()        # eager work between replays
+        torch.cuda.synchronize()
+        got = outputs()
+        for a, b in zip(got, eager[t]):
+            assert torch.equal(a, b), t
+        del junk
