@@ -39,19 +39,8 @@ __device__ __forceinline__ float token_sum(float v) {
   return v;
 }
 
-// Eight elements of a K or V row as loaded (bf16: one 16-byte vector, fp32:
-// two), converted to fp32 only where they are used.
+// Eight fp32 elements of a K or V row as loaded (two 16-byte vectors).
 template <typename T> struct Row8;
-template <> struct Row8<uint16_t> {
-  uint4 r;
-  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void get(float* o) const {
-    o[0] = bf16_bits_to_f32(r.x & 0xffffu); o[1] = bf16_bits_to_f32(r.x >> 16);
-    o[2] = bf16_bits_to_f32(r.y & 0xffffu); o[3] = bf16_bits_to_f32(r.y >> 16);
-    o[4] = bf16_bits_to_f32(r.z & 0xffffu); o[5] = bf16_bits_to_f32(r.z >> 16);
-    o[6] = bf16_bits_to_f32(r.w & 0xffffu); o[7] = bf16_bits_to_f32(r.w >> 16);
-  }
-};
 template <> struct Row8<float> {
   float4 a, b;
   __device__ __forceinline__ void load(const float* p) {
@@ -63,27 +52,9 @@ template <> struct Row8<float> {
   }
 };
 
-// A query head's 8 features of this lane, and its dot product with a K row:
-// bf16 pairs through v_dot2_f32_bf16 (exact products, fp32 sums), fp32 with
-// plain fused multiply-adds.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// A query head's 8 features of this lane, and its dot product with a K row
+// (fused multiply-adds).
 template <typename T> struct QVec;
-template <> struct QVec<uint16_t> {
-  uint4 r;
-  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void zero() { r = make_uint4(0u, 0u, 0u, 0u); }
-  __device__ __forceinline__ float dot(const Row8<uint16_t>& k) const {
-    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.x),
-                                              __builtin_bit_cast(bf16x2_t, r.x), 0.f, false);
-    float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.y),
-                                              __builtin_bit_cast(bf16x2_t, r.y), 0.f, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.z),
-                                        __builtin_bit_cast(bf16x2_t, r.z), a, false);
-    b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.w),
-                                        __builtin_bit_cast(bf16x2_t, r.w), b, false);
-    return a + b;
-  }
-};
 template <> struct QVec<float> {
   float v[8];
   __device__ __forceinline__ void load(const float* p) { load8_f32(p, v); }
@@ -456,6 +427,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kVtStride = 40;            // V^T row: 32 key slots + 8 pad (80 bytes)
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Slot of key k (0..31 within a step) in a V^T row: the B operand of the
 // V product takes slots 8 j .. 8 j + 7 from lane group j, which holds the
@@ -811,8 +783,8 @@ size_t plan_bytes(int P) {
   return (((size_t)1 + (P + 1)) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
-// Split workgroups per launch: three resident per CU (the kernel's occupancy),
-// two rounds.
+// Split workgroups per launch: six per CU (two to three rounds of the split
+// kernels' resident workgroups; one or two rounds measure the same).
 int split_workgroups() {
   static int cached[64] = {0};
   int dev = 0;
