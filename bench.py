@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-layers", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--kv-layout", choices=("head", "token"), default="head",
+                    help="decode KV cache layout: [seq][kv head][ctx][d] (head) or "
+                         "[seq][ctx][kv head][d] (token)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -222,6 +225,7 @@ def bench_decode(args, torch, sws, gen, timer_cls):
     signs_d = torch.from_numpy(signs).cuda()
     cols_d = torch.from_numpy(cols).cuda()
     t_setup = time.perf_counter()
+    head_major = args.kv_layout == "head"
     geo_p = sws.Geometry([P], B)
     state = []
     for l in range(Lyr):
@@ -242,6 +246,9 @@ def bench_decode(args, torch, sws, gen, timer_cls):
             rk[s] = sk[:, -1]
         del qpre
         knew = kc[:, P:].permute(1, 0, 2, 3).contiguous()       # [steps, ns, hkv, d]
+        if head_major:
+            kc = kc.permute(0, 2, 1, 3).contiguous()             # [ns, hkv, ctx, d]
+            vc = vc.permute(0, 2, 1, 3).contiguous()
         if l % 8 == 7:
             print(f"[bench] decode setup: {l + 1}/{Lyr} layers", file=sys.stderr, flush=True)
         state.append({"qst": qst, "knew": knew, "kc": kc, "vc": vc, "qsk": qsk, "ksk": ksk,
@@ -282,7 +289,7 @@ def bench_decode(args, torch, sws, gen, timer_cls):
                                                           out=dbufs if dense else ubufs)
             b_ = T.ev() if T else None
             sws.sparse_attn_decode(st["qst"][t], st["kc"], st["vc"], ctx_len[t], B, uidx, ucnt,
-                                   umask, out=st["out"], ws=ws)
+                                   umask, out=st["out"], ws=ws, head_major=head_major)
             if T:
                 c_ = T.ev()
                 T.add("dense_layer" if dense else "sparse_layer", a, c_)
@@ -321,6 +328,8 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         "union_blocks_per_group": union_blocks / (ns * hkv),
         "per_head_blocks": cfg.rho * (b_max - 1) // 100 + 1,
         "setup_s": setup_s,
+        "kv_layout": ("head-major [seq][kv head][ctx][d]" if head_major
+                      else "token-major [seq][ctx][kv head][d]"),
     }
     if not args.no_graph:
         # The same steps again from the same starting state, each step one
@@ -344,7 +353,7 @@ def bench_decode(args, torch, sws, gen, timer_cls):
                 u = sws.select_topk_row(r, hq, hkv, pcc[1], b_max, cfg.rho, dense=dense,
                                         out=dbufs if dense else ubufs)
                 sws.sparse_attn_decode(q_buf[l], st["kc"], st["vc"], pcc[2], B, u[0], u[1], u[2],
-                                       out=st["out"], ws=ws)
+                                       out=st["out"], ws=ws, head_major=head_major)
 
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -373,17 +382,20 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         del graph
     if not args.no_serving:
         res["serving_layouts"] = serving_layouts(torch, sws, gen, state[-1], ubufs, ctx_len[-1],
-                                                 B, steps - 1)
+                                                 B, steps - 1, head_major)
     return res
 
 
-def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, reps=20):
+def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, head_major, reps=20):
     """Decode attention of one sparse layer at the last decode step on the
     same union lists, over the contiguous cache, a paged copy (pages of one
     block in a random order) and an fp8 e4m3 paged copy (per-tensor scales),
-    sparse and dense.  Bytes are the KV rows the lists name (K and V) plus
-    q and out; GB/s is those bytes over the average call time."""
+    each token-major and head-major ("_hm"), sparse and dense.  Bytes are the
+    KV rows the lists name (K and V) plus q and out; GB/s is those bytes over
+    the average call time."""
     kc, vc = st["kc"], st["vc"]
+    if head_major:
+        kc, vc = (x.permute(0, 2, 1, 3).contiguous() for x in (kc, vc))
     ns, max_ctx, hkv, d = kc.shape
     q = st["qst"][t]
     hq = q.shape[1]
@@ -404,6 +416,10 @@ def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, reps=20):
     vsc = float(vc.float().abs().amax()) / 448.0
     kp8 = gen.to_fp8_e4m3(kp, ksc).view(torch.float8_e4m3fn)
     vp8 = gen.to_fp8_e4m3(vp, vsc).view(torch.float8_e4m3fn)
+    hm = lambda x: x.permute(0, 2, 1, 3).contiguous()
+    kch, vch, kph, vph = hm(kc), hm(vc), hm(kp), hm(vp)
+    kph8 = hm(kp8.view(torch.uint8)).view(torch.float8_e4m3fn)
+    vph8 = hm(vp8.view(torch.uint8)).view(torch.float8_e4m3fn)
     uidx, ucnt, umask = ubufs[0], ubufs[1], ubufs[2]
     ws = torch.empty(sws.decode_workspace_size(ns, hq, hkv, d, B, nb), dtype=torch.uint8,
                      device="cuda")
@@ -419,6 +435,15 @@ def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, reps=20):
         "paged_fp8": (lambda u: sws.sparse_attn_decode_paged(q, kp8, vp8, tab, ctx, *u,
                                                              k_scale=ksc, v_scale=vsc, out=out,
                                                              ws=ws), 1),
+        "contiguous_bf16_hm": (lambda u: sws.sparse_attn_decode(q, kch, vch, ctx, B, *u, out=out,
+                                                                ws=ws, head_major=True), 2),
+        "paged_bf16_hm": (lambda u: sws.sparse_attn_decode_paged(q, kph, vph, tab, ctx, *u,
+                                                                 out=out, ws=ws,
+                                                                 head_major=True), 2),
+        "paged_fp8_hm": (lambda u: sws.sparse_attn_decode_paged(q, kph8, vph8, tab, ctx, *u,
+                                                                k_scale=ksc, v_scale=vsc,
+                                                                out=out, ws=ws,
+                                                                head_major=True), 1),
     }
     res = {"batch": ns, "context": int(ctx[0]), "reps": reps}
     for mode, u, rows in (("sparse", (uidx, ucnt, umask), union_rows),
@@ -437,7 +462,7 @@ def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, reps=20):
             nbytes = rows * d * eb * 2 + qo
             res[f"{mode}_{name}_us"] = round(us, 2)
             res[f"{mode}_{name}_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
-    del kp, vp, kp8, vp8
+    del kp, vp, kp8, vp8, kch, vch, kph, vph, kph8, vph8
     return res
 
 

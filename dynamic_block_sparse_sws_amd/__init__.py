@@ -28,6 +28,7 @@ __all__ = [
 F32 = 0
 BF16 = 1
 FP8_E4M3 = 2   # KV pages only
+KV_HEAD_MAJOR = 0x100   # layout flag for the decode calls: [.., hkv, rows, d] caches
 
 # walk modes and selection flags (include/sws.h)
 WALK_DEFAULT = 0
@@ -361,9 +362,15 @@ def decode_workspace_size(n_seqs, hq, hkv, d, B, uwidth) -> int:
 
 
 def sparse_attn_decode(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cnt, union_mask,
-                       scale: Optional[float] = None, out=None, lse=None, ws=None, stream=None):
+                       scale: Optional[float] = None, out=None, lse=None, ws=None, stream=None,
+                       head_major: bool = False):
+    """Decode attention over a contiguous cache [n_seqs][max_ctx][hkv][d], or
+    [n_seqs][hkv][max_ctx][d] with head_major=True."""
     n_seqs, hq, d = q.shape
-    _, max_ctx, hkv, _ = k_cache.shape
+    if head_major:
+        _, hkv, max_ctx, _ = k_cache.shape
+    else:
+        _, max_ctx, hkv, _ = k_cache.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     uw = union_idx.shape[2] if union_idx is not None else -(-max_ctx // B)
@@ -373,7 +380,8 @@ def sparse_attn_decode(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cn
     if out is None:
         out = torch.empty_like(q)
     _check("sws_sparse_attn_decode", lib().sws_sparse_attn_decode(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(ctx_len), n_seqs, max_ctx, hq,
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q) | (KV_HEAD_MAJOR if head_major else 0),
+        _ptr(ctx_len), n_seqs, max_ctx, hq,
         hkv, d, B, _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
@@ -382,12 +390,16 @@ def sparse_attn_decode(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cn
 def sparse_attn_decode_paged(q, k_pages, v_pages, block_table, ctx_len, union_idx, union_cnt,
                              union_mask, k_scale: float = 1.0, v_scale: float = 1.0,
                              scale: Optional[float] = None, out=None, lse=None, ws=None,
-                             stream=None):
-    """Decode attention over a paged cache: k_pages / v_pages [num_pages][B][hkv][d] in bf16
-    or torch.float8_e4m3fn (value = code * k_scale / v_scale), block_table [n_seqs][width]
-    int32 pages of each sequence's logical blocks; q and out bf16."""
+                             stream=None, head_major: bool = False):
+    """Decode attention over a paged cache: k_pages / v_pages [num_pages][B][hkv][d]
+    ([num_pages][hkv][B][d] with head_major=True) in bf16 or torch.float8_e4m3fn
+    (value = code * k_scale / v_scale), block_table [n_seqs][width] int32 pages of each
+    sequence's logical blocks; q and out bf16."""
     n_seqs, hq, d = q.shape
-    num_pages, B, hkv, _ = k_pages.shape
+    if head_major:
+        num_pages, hkv, B, _ = k_pages.shape
+    else:
+        num_pages, B, hkv, _ = k_pages.shape
     width = block_table.shape[1]
     if k_pages.dtype == torch.bfloat16:
         kv = BF16
@@ -408,7 +420,8 @@ def sparse_attn_decode_paged(q, k_pages, v_pages, block_table, ctx_len, union_id
     if out is None:
         out = torch.empty_like(q)
     _check("sws_sparse_attn_decode_paged", lib().sws_sparse_attn_decode_paged(
-        _ptr(q), _ptr(k_pages), _ptr(v_pages), kv, float(k_scale), float(v_scale),
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), kv | (KV_HEAD_MAJOR if head_major else 0),
+        float(k_scale), float(v_scale),
         _ptr(block_table), width, num_pages, _ptr(ctx_len), n_seqs, hq, hkv, d, B,
         _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

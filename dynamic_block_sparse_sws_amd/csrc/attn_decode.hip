@@ -179,6 +179,16 @@ __device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
   return total;
 }
 
+// Strides (elements) of a KV cache: row t of KV head g of sequence s is at
+// s * seq + g * head + t * row.  Token-major caches [n_seqs][max_ctx][hkv][d]
+// have (max_ctx hkv d, d, hkv d), head-major ones [n_seqs][hkv][max_ctx][d]
+// (hkv max_ctx d, max_ctx d, d).  For pages `seq` is the page stride and rows
+// count from the page's first token: [BLK][hkv][d] pages have (BLK hkv d, d,
+// hkv d), [hkv][BLK][d] pages (hkv BLK d, BLK d, d).
+struct KvLayout {
+  int64_t seq, head, row;
+};
+
 // Partial state of blocks [a, b) of pair p's list for every query head of the
 // group, written as record `r`.  The range is cut into batches of TPB tokens
 // (a batch never straddles a block); wave w takes batches w, w + 4, ...  A
@@ -187,14 +197,13 @@ __device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
 // each row group of the wave keeps its own online-softmax state (max, sum,
 // weighted V sum) for up to four query heads at a time.  Row groups merge
 // through lane exchanges, waves through LDS.
-// KV addressing: contiguous caches [n_seqs][max_ctx][hkv][d] (table == null),
-// or pages of BLK tokens [num_pages][BLK][hkv][d] with table[seq][logical
-// block] giving the page.  TK is the cache element type (the query type
+// KV addressing: a contiguous cache (table == null), or pages of BLK tokens
+// with table[seq][logical block] giving the page; L gives the strides.  TK is the cache element type (the query type
 // here); kscale / vscale are per-tensor scales (1 for plain caches).
 template <typename T, int D, int BLK, int GMAX, int UNR, typename TK = T>
 __device__ __forceinline__ void decode_range(
     const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
-    const int32_t* __restrict__ ctx_len, int max_ctx, int hq, int hkv,
+    const int32_t* __restrict__ ctx_len, KvLayout L, int hq, int hkv,
     const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth, int p,
     int a, int b, int r, float scale_log2, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, const int32_t* __restrict__ table = nullptr, int table_width = 0,
@@ -220,10 +229,9 @@ __device__ __forceinline__ void decode_range(
   const int lane = tid & 63, wave = tid >> 6;
   const int ch = lane % TPL;           // feature chunk (8 features)
   const int slot = lane / TPL;         // row group of the wave
-  const int64_t rstride = (int64_t)hkv * D;
-  const int64_t seq_off = table ? 0 : ((int64_t)seq * max_ctx) * rstride;
-  const TK* kb = kc + seq_off + (int64_t)g * D + ch * 8;
-  const TK* vb = vc + seq_off + (int64_t)g * D + ch * 8;
+  const int64_t seq_off = table ? 0 : (int64_t)seq * L.seq;
+  const TK* kb = kc + seq_off + (int64_t)g * L.head + ch * 8;
+  const TK* vb = vc + seq_off + (int64_t)g * L.head + ch * 8;
   const int32_t* trow = table ? table + (int64_t)seq * table_width : nullptr;
   const int32_t* ul = uidx ? uidx + (int64_t)p * uwidth : nullptr;
   const uint32_t* um = umask ? umask + (int64_t)p * uwidth : nullptr;
@@ -252,15 +260,15 @@ __device__ __forceinline__ void decode_range(
       int64_t pbase = 0;
       if (trow) {
         const int pg = min(max(trow[min(blk, table_width - 1)], 0), num_pages - 1);
-        pbase = ((int64_t)pg - blk) * BLK;
+        pbase = (int64_t)pg * L.seq - (int64_t)blk * BLK * L.row;
       }
       Row8<TK> kr[UNR], vr[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         // rows past ctx are masked below (the clamped row is in the same block)
-        const int64_t row = pbase + min(r0 + u * RPW, ctx - 1);
-        kr[u].load(kb + row * rstride);
-        vr[u].load(vb + row * rstride);
+        const int64_t row = min(r0 + u * RPW, ctx - 1);
+        kr[u].load(kb + pbase + row * L.row);
+        vr[u].load(vb + pbase + row * L.row);
       }
       float sc[UNR][HC];
 #pragma unroll
@@ -358,7 +366,7 @@ __device__ __forceinline__ void decode_range(
 template <typename T, int D, int BLK, int GMAX, int UNR, typename TK>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const T* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
-    const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
+    const int32_t* __restrict__ ctx_len, KvLayout L, int n_seqs, int hq, int hkv,
     const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucnt,
     const uint32_t* __restrict__ umask, int uwidth, float scale_log2, int nwg_launched,
     void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
@@ -399,7 +407,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int a = (int)(max(lo, (int64_t)A) - A);
     const int b = (int)(min(hi, (int64_t)Bn) - A);
     if (a >= b) continue;
-    decode_range<T, D, BLK, GMAX, UNR, TK>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask,
+    decode_range<T, D, BLK, GMAX, UNR, TK>(q, kc, vc, ctx_len, L, hq, hkv, uidx, umask,
                                            uwidth, p, a, b, w + p, scale_log2, ws_ml, ws_acc,
                                            table, table_width, num_pages, kscale, vscale);
   }
@@ -445,21 +453,21 @@ template <> struct KvFrag<uint16_t> {
 template <> struct KvFrag<uint8_t> {
   uint2 r;
   __device__ __forceinline__ void load(const uint8_t* p) { r = *reinterpret_cast<const uint2*>(p); }
+  // one instruction per two codes (fp8 -> bf16 directly, scale 1: exact)
   __device__ __forceinline__ bf16x8_t bf() const {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(r.x, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(r.y, true);
-    typedef float f32x8_t __attribute__((ext_vector_type(8)));
-    const f32x8_t f = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    return __builtin_convertvector(f, bf16x8_t);
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, true);
+    const bf16x8_t f = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return f;
   }
 };
 
 template <int D, int BLK, typename TK>
 __device__ __forceinline__ void mfma_range(
     const uint16_t* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
-    const int32_t* __restrict__ ctx_len, int max_ctx, int hq, int hkv,
+    const int32_t* __restrict__ ctx_len, KvLayout L, int hq, int hkv,
     const int32_t* __restrict__ uidx, const uint32_t* __restrict__ umask, int uwidth, int p,
     int a, int b, int r, float scale_log2, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, const int32_t* __restrict__ table, int table_width,
@@ -479,10 +487,9 @@ __device__ __forceinline__ void mfma_range(
   const int col = lane & 15, grp = lane >> 4;
   const float sl2 = scale_log2 * kscale;
   __bf16* vt = vt_all + wave * D * kVtStride;
-  const int64_t rstride = (int64_t)hkv * D;
-  const int64_t seq_off = table ? 0 : ((int64_t)seq * max_ctx) * rstride;
-  const TK* kb = kc + seq_off + (int64_t)g * D + grp * 8;
-  const TK* vb = vc + seq_off + (int64_t)g * D + grp * 8;
+  const int64_t seq_off = table ? 0 : (int64_t)seq * L.seq;
+  const TK* kb = kc + seq_off + (int64_t)g * L.head + grp * 8;
+  const TK* vb = vc + seq_off + (int64_t)g * L.head + grp * 8;
   const int32_t* trow = table ? table + (int64_t)seq * table_width : nullptr;
   const int32_t* ul = uidx ? uidx + (int64_t)p * uwidth : nullptr;
   const uint32_t* um = umask ? umask + (int64_t)p * uwidth : nullptr;
@@ -521,15 +528,15 @@ __device__ __forceinline__ void mfma_range(
     int64_t pbase = 0;
     if (trow) {
       const int pg = min(max(trow[min(blk, table_width - 1)], 0), num_pages - 1);
-      pbase = ((int64_t)pg - blk) * BLK;
+      pbase = (int64_t)pg * L.seq - (int64_t)blk * BLK * L.row;
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int64_t row = pbase + min(key0 + kt * 16 + col, ctx - 1);
+      const int64_t row = pbase + (int64_t)min(key0 + kt * 16 + col, ctx - 1) * L.row;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        kf[kt][c].load(kb + row * rstride + c * 32);
-        vf[kt][c].load(vb + row * rstride + c * 32);
+        kf[kt][c].load(kb + row + c * 32);
+        vf[kt][c].load(vb + row + c * 32);
       }
     }
   };
@@ -658,7 +665,7 @@ __device__ __forceinline__ void mfma_range(
 template <int D, int BLK, typename TK>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const TK* __restrict__ kc, const TK* __restrict__ vc,
-    const int32_t* __restrict__ ctx_len, int max_ctx, int n_seqs, int hq, int hkv,
+    const int32_t* __restrict__ ctx_len, KvLayout L, int n_seqs, int hq, int hkv,
     const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucnt,
     const uint32_t* __restrict__ umask, int uwidth, float scale_log2, int nwg_launched,
     void* ws, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
@@ -700,7 +707,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int a = (int)(max(lo, (int64_t)A) - A);
     const int b = (int)(min(hi, (int64_t)Bn) - A);
     if (a >= b) continue;
-    mfma_range<D, BLK, TK>(q, kc, vc, ctx_len, max_ctx, hq, hkv, uidx, umask, uwidth, p, a, b,
+    mfma_range<D, BLK, TK>(q, kc, vc, ctx_len, L, hq, hkv, uidx, umask, uwidth, p, a, b,
                            w + p, scale_log2, ws_ml, ws_acc, table, table_width, num_pages,
                            kscale, vscale, vt_all, mw, lw);
   }
@@ -801,7 +808,7 @@ int split_workgroups() {
 
 template <typename T, int D, int BLK, int GMAX, typename TK>
 hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* ctx_len, int n_seqs, int max_ctx, int hq, int hkv,
+                      const int32_t* ctx_len, int n_seqs, KvLayout L, int hq, int hkv,
                       const int32_t* uidx, const int32_t* ucnt, const uint32_t* umask,
                       int uwidth, float scale, void* out, float* lse, void* ws,
                       hipStream_t st, const int32_t* table, int table_width, int num_pages,
@@ -814,14 +821,14 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
   if constexpr (std::is_same<T, uint16_t>::value) {
     hipLaunchKernelGGL((decode_mfma_kernel<D, BLK, TK>), dim3(nwg), dim3(kDecThreads), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const TK*>(k_cache),
-                       static_cast<const TK*>(v_cache), ctx_len, max_ctx, n_seqs, hq, hkv, uidx,
+                       static_cast<const TK*>(v_cache), ctx_len, L, n_seqs, hq, hkv, uidx,
                        ucnt, umask, uwidth, scale * kLog2e, nwg, ws, ws_ml, ws_acc, table,
                        table_width, num_pages, kscale, vscale);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<T, D, BLK, GMAX, kDecUnroll, TK>), dim3(nwg),
                        dim3(kDecThreads), 0, st, static_cast<const T*>(q),
                        static_cast<const TK*>(k_cache), static_cast<const TK*>(v_cache), ctx_len,
-                       max_ctx, n_seqs, hq, hkv, uidx, ucnt, umask, uwidth, scale * kLog2e, nwg,
+                       L, n_seqs, hq, hkv, uidx, ucnt, umask, uwidth, scale * kLog2e, nwg,
                        ws, ws_ml, ws_acc, table, table_width, num_pages, kscale, vscale);
   }
   hipError_t e = hipGetLastError();
@@ -833,14 +840,14 @@ hipError_t run_decode(const void* q, const void* k_cache, const void* v_cache,
 
 template <typename T, int D, int BLK, typename TK = T>
 hipError_t pick_g(const void* q, const void* k_cache, const void* v_cache,
-                  const int32_t* ctx_len, int n_seqs, int max_ctx, int hq, int hkv,
+                  const int32_t* ctx_len, int n_seqs, KvLayout L, int hq, int hkv,
                   const int32_t* uidx, const int32_t* ucnt, const uint32_t* umask, int uwidth,
                   float scale, void* out, float* lse, void* ws, hipStream_t st,
                   const int32_t* table = nullptr, int table_width = 0, int num_pages = 0,
                   float kscale = 1.0f, float vscale = 1.0f) {
   const int G = hq / hkv;
 #define SWS_RUN(GM)                                                                            \
-  return run_decode<T, D, BLK, GM, TK>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv,  \
+  return run_decode<T, D, BLK, GM, TK>(q, k_cache, v_cache, ctx_len, n_seqs, L, hq, hkv,        \
                                        uidx, ucnt, umask, uwidth, scale, out, lse, ws, st,     \
                                        table, table_width, num_pages, kscale, vscale)
   if (G <= 1) SWS_RUN(1);
@@ -861,14 +868,16 @@ size_t decode_workspace_bytes(int n_seqs, int hq, int hkv, int d, int B, int uni
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                              int dtype, const int32_t* ctx_len, int n_seqs, int max_ctx, int hq,
-                              int hkv, int d, int B, const int32_t* union_idx,
+                              int dtype, bool head_major, const int32_t* ctx_len, int n_seqs,
+                              int max_ctx, int hq, int hkv, int d, int B, const int32_t* union_idx,
                               const int32_t* union_cnt, const uint32_t* union_mask,
                               int union_width, float scale, void* out, float* lse, void* ws,
                               hipStream_t st) {
   if (n_seqs == 0) return hipSuccess;
+  const KvLayout L = head_major ? KvLayout{(int64_t)hkv * max_ctx * d, (int64_t)max_ctx * d, d}
+                                : KvLayout{(int64_t)max_ctx * hkv * d, d, (int64_t)hkv * d};
 #define SWS_DEC(T, D, BLK)                                                                     \
-  return pick_g<T, D, BLK>(q, k_cache, v_cache, ctx_len, n_seqs, max_ctx, hq, hkv, union_idx, \
+  return pick_g<T, D, BLK>(q, k_cache, v_cache, ctx_len, n_seqs, L, hq, hkv, union_idx,       \
                            union_cnt, union_mask, union_width, scale, out, lse, ws, st)
   if (dtype == SWS_BF16) {
     if (d == 128 && B == 64) SWS_DEC(uint16_t, 128, 64);
@@ -884,15 +893,18 @@ hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_
 }
 
 hipError_t launch_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
-                                    int kv_dtype, float k_scale, float v_scale,
+                                    int kv_dtype, bool head_major, float k_scale, float v_scale,
                                     const int32_t* block_table, int table_width,
                                     int num_pages, const int32_t* ctx_len, int n_seqs, int hq, int hkv, int d,
                                     int B, const int32_t* union_idx, const int32_t* union_cnt,
                                     const uint32_t* union_mask, int union_width, float scale,
                                     void* out, float* lse, void* ws, hipStream_t st) {
   if (n_seqs == 0) return hipSuccess;
+  // a page holds B rows of every KV head: [B][hkv][d] or, head-major, [hkv][B][d]
+  const KvLayout L = head_major ? KvLayout{(int64_t)hkv * B * d, (int64_t)B * d, d}
+                                : KvLayout{(int64_t)B * hkv * d, d, (int64_t)hkv * d};
 #define SWS_DEC(TK, D, BLK)                                                                    \
-  return pick_g<uint16_t, D, BLK, TK>(q, k_pages, v_pages, ctx_len, n_seqs, 0, hq, hkv,       \
+  return pick_g<uint16_t, D, BLK, TK>(q, k_pages, v_pages, ctx_len, n_seqs, L, hq, hkv,       \
                                       union_idx, union_cnt, union_mask, union_width, scale,   \
                                       out, lse, ws, st, block_table, table_width, num_pages,  \
                                       k_scale, v_scale)

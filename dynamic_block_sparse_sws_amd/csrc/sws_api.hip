@@ -363,6 +363,8 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
   REQUIRE_PTR(out);
   if (union_idx && (!union_cnt || !union_mask))
     return fail(SWS_ERR_NULL, "%s: union_idx given without union_cnt / union_mask", fn);
+  const bool head_major = (dtype & SWS_KV_HEAD_MAJOR) != 0;
+  dtype &= ~SWS_KV_HEAD_MAJOR;
   if (!dtype_ok(dtype)) return fail(SWS_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
   if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
   if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
@@ -384,9 +386,10 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
   const size_t need = sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, uw);
   if (!ws || ws_bytes < need)
     return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
-  return launched(sws::launch_attn_decode(q, k_cache, v_cache, dtype, ctx_len, n_seqs, max_ctx,
-                                          hq, hkv, d, B, union_idx, union_cnt, union_mask, uw,
-                                          scale, out, lse, ws, (hipStream_t)stream),
+  return launched(sws::launch_attn_decode(q, k_cache, v_cache, dtype, head_major, ctx_len, n_seqs,
+                                          max_ctx, hq, hkv, d, B, union_idx, union_cnt,
+                                          union_mask, uw, scale, out, lse, ws,
+                                          (hipStream_t)stream),
                   fn);
 }
 
@@ -407,6 +410,8 @@ int sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void*
   REQUIRE_PTR(out);
   if (union_idx && (!union_cnt || !union_mask))
     return fail(SWS_ERR_NULL, "%s: union_idx given without union_cnt / union_mask", fn);
+  const bool head_major = (kv_dtype & SWS_KV_HEAD_MAJOR) != 0;
+  kv_dtype &= ~SWS_KV_HEAD_MAJOR;
   if (kv_dtype != SWS_BF16 && kv_dtype != SWS_FP8_E4M3)
     return fail(SWS_ERR_UNSUPPORTED, "%s: kv_dtype %d", fn, kv_dtype);
   if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
@@ -433,7 +438,8 @@ int sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void*
   if (!ws || ws_bytes < need)
     return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
   return launched(sws::launch_attn_decode_paged(
-                      q, k_pages, v_pages, kv_dtype, k_scale, v_scale, block_table, table_width,
+                      q, k_pages, v_pages, kv_dtype, head_major, k_scale, v_scale, block_table,
+                      table_width,
                       num_pages, ctx_len, n_seqs, hq, hkv, d, B, union_idx, union_cnt,
                       union_mask, uw, scale, out, lse, ws, (hipStream_t)stream),
                   fn);

@@ -102,13 +102,13 @@ hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, int 
                                const int32_t* idx, const int32_t* cnt, int width, float scale,
                                void* out, float* lse, void* ws, hipStream_t st);
 hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                              int dtype, const int32_t* ctx_len, int n_seqs, int max_ctx, int hq,
-                              int hkv, int d, int B, const int32_t* union_idx,
+                              int dtype, bool head_major, const int32_t* ctx_len, int n_seqs,
+                              int max_ctx, int hq, int hkv, int d, int B, const int32_t* union_idx,
                               const int32_t* union_cnt, const uint32_t* union_mask,
                               int union_width, float scale, void* out, float* lse, void* ws,
                               hipStream_t st);
 hipError_t launch_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
-                                    int kv_dtype, float k_scale, float v_scale,
+                                    int kv_dtype, bool head_major, float k_scale, float v_scale,
                                     const int32_t* block_table, int table_width,
                                     int num_pages, const int32_t* ctx_len, int n_seqs, int hq,
                                     int hkv, int d, int B, const int32_t* union_idx,

@@ -59,6 +59,16 @@ typedef enum sws_dtype {
                        value = code * per-tensor scale                        */
 } sws_dtype;
 
+/* KV-cache layout flag, OR-ed into the dtype argument of the two decode calls
+ * (sws_sparse_attn_decode, sws_sparse_attn_decode_paged).  Without it a cache
+ * is token-major ([n_seqs][max_ctx][hkv][d], pages [B][hkv][d]); with it the
+ * rows of one KV head are contiguous ([n_seqs][hkv][max_ctx][d], pages
+ * [hkv][B][d]), so a selected block is one contiguous run of B rows per head.
+ * The result is the same for either layout of the same values. */
+enum {
+  SWS_KV_HEAD_MAJOR = 0x100
+};
+
 /* Walk modes (sws_walk_update_variant, sws_walk_update_row_variant).  The
  * page writes the walk update as R^l = R^(l-1) (A^l)^s and calls s the walk
  * degree; the default reading (mode 0, sws_walk_update) is s hops with the
@@ -310,7 +320,8 @@ size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, 
  * with a log-sum-exp combine; the block's KV rows are read once for all the
  * query heads of the group that kept it.
  *
- *   q       [n_seqs][hq][d]; k_cache, v_cache [n_seqs][max_ctx][hkv][d]
+ *   q       [n_seqs][hq][d]; k_cache, v_cache [n_seqs][max_ctx][hkv][d], or
+ *           [n_seqs][hkv][max_ctx][d] with SWS_KV_HEAD_MAJOR in dtype
  *   ctx_len [n_seqs] int32: tokens in the cache including the new one
  *           (the new token is the last; its block is the open block)
  *   union_idx / union_cnt / union_mask as produced by sws_select_topk_row
@@ -343,10 +354,11 @@ size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_
  * gives on the gathered (and, for fp8, dequantised) contiguous cache.
  *
  *   q            [n_seqs][hq][d] bf16
- *   k_pages,     [num_pages][B][hkv][d], one page per KV block of B tokens,
- *   v_pages      dtype kv_dtype: SWS_BF16, or SWS_FP8_E4M3 whose value is
- *                code * k_scale (K) or code * v_scale (V); scales are
- *                ignored for SWS_BF16
+ *   k_pages,     [num_pages][B][hkv][d] ([num_pages][hkv][B][d] with
+ *   v_pages      SWS_KV_HEAD_MAJOR in kv_dtype), one page per KV block of B
+ *                tokens, dtype kv_dtype: SWS_BF16, or SWS_FP8_E4M3 whose
+ *                value is code * k_scale (K) or code * v_scale (V); scales
+ *                are ignored for SWS_BF16
  *   block_table  [n_seqs][table_width] int32: page of logical block j of
  *                sequence s.  Sequences come and go between calls
  *                (continuous batching) by rewriting their table rows; pages

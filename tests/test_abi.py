@@ -134,5 +134,12 @@ def test_other_entry_points_validation():
                                           64, P, P, P, 821, f(0.1), P, N, P, need - 1, N) == 4
     assert L.sws_sparse_attn_decode_paged(P, P, P, 2, f(float("inf")), f(1), P, 1029, 4096, P, 16,
                                           32, 8, 128, 64, P, P, P, 821, f(0.1), P, N, P, need, N) == 2
+    # the head-major layout flag does not make an unknown dtype valid
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 0x100 | 0, f(1), f(1), P, 1029, 4096, P, 16, 32,
+                                          8, 128, 64, P, P, P, 821, f(0.1), P, N, P, need, N) == 3
+    assert L.sws_sparse_attn_decode_paged(P, P, P, 0x100 | 1, f(1), f(1), P, 1029, 4096, P, 16, 32,
+                                          8, 128, 64, P, P, P, 821, f(0.1), P, N, P, need - 1, N) == 4
+    assert L.sws_sparse_attn_decode(P, P, P, 0x100 | 7, P, 16, 65536, 32, 8, 128, 64, P, P, P, 821,
+                                    f(0.1), P, N, P, need, N) == 3
     # append: b_max 0
     assert L.sws_sketch_append(P, 1, P, 2, 8, 128, 64, 32, P, P, P, P, 0, N) == 2

@@ -426,6 +426,75 @@ def test_decode_paged_fp8(d, B, hq, hkv, lens, share):
                            TOL_ATTN_BF16)
 
 
+@pytest.mark.parametrize("d,B,hq,hkv,lens,share", [
+    (128, 64, 8, 2, (1000, 2049, 64), 7),
+    (64, 128, 12, 3, (700, 1, 1281), 0),
+])
+def test_decode_head_major_layouts(d, B, hq, hkv, lens, share):
+    """Head-major caches and pages (rows of one KV head contiguous) give the
+    token-major result bit for bit: bf16 and fp32 contiguous caches, bf16 and
+    fp8 pages (NaN in every unused row and page); the bf16 head-major output
+    also against the oracle."""
+    cfg = gen.CONFIGS["C4"].with_(d=d, B=B, hq=hq, hkv=hkv)
+    ns, grp = len(lens), hq // hkv
+    _print("head-major", d, B, hq, hkv, lens, share)
+    K, V, q, table, num_pages = _paged_inputs(cfg, lens, share)
+    max_ctx = max(lens)
+    kc = torch.zeros((ns, max_ctx, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for s, n in enumerate(lens):
+        kc[s, :n] = K[s]
+        vc[s, :n] = V[s]
+    hm = lambda x: x.permute(0, 2, 1, 3).contiguous()
+    kp = _fill_pages(K, table, num_pages, B, torch.bfloat16, float("nan"))
+    vp = _fill_pages(V, table, num_pages, B, torch.bfloat16, float("nan"))
+    kp8 = _fill_pages([gen.to_fp8_e4m3(k, 0.0625) for k in K], table, num_pages, B, torch.uint8,
+                      0x7F)
+    vp8 = _fill_pages([gen.to_fp8_e4m3(v, 0.02) for v in V], table, num_pages, B, torch.uint8,
+                      0x7F)
+    f8 = lambda x: x.view(torch.float8_e4m3fn)
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cur = (ctx - 1) // B
+    b_max = -(-max_ctx // B)
+    gr = torch.Generator(device="cuda")
+    gr.manual_seed(gen.seed_for(13, d, B, hq))
+    r = torch.rand((ns, hq, b_max), generator=gr, device="cuda")
+    uidx, ucnt, umask, idx, cnt = sws.select_topk_row(r, hq, hkv, cur, b_max, 25, per_head=True)
+    tab = torch.from_numpy(table).cuda()
+    q32 = q.float()
+    for sparse in (True, False):
+        u = (uidx, ucnt, umask) if sparse else (None, None, None)
+        pairs = [
+            (lambda m: sws.sparse_attn_decode(q, hm(kc) if m else kc, hm(vc) if m else vc, ctx, B,
+                                              *u, lse=lse_of(), head_major=m)),
+            (lambda m: sws.sparse_attn_decode(q32, (hm(kc) if m else kc).float(),
+                                              (hm(vc) if m else vc).float(), ctx, B, *u,
+                                              lse=lse_of(), head_major=m)),
+            (lambda m: sws.sparse_attn_decode_paged(q, hm(kp) if m else kp, hm(vp) if m else vp,
+                                                    tab, ctx, *u, lse=lse_of(), head_major=m)),
+            (lambda m: sws.sparse_attn_decode_paged(q, f8(hm(kp8) if m else kp8),
+                                                    f8(hm(vp8) if m else vp8), tab, ctx, *u,
+                                                    k_scale=0.0625, v_scale=0.02, lse=lse_of(),
+                                                    head_major=m)),
+        ]
+        for n_call, call in enumerate(pairs):
+            lses = []
+            lse_of = lambda: lses.append(torch.empty((ns, hq), dtype=torch.float32,
+                                                     device="cuda")) or lses[-1]
+            o_t = call(False)
+            o_h = call(True)
+            torch.cuda.synchronize()
+            assert torch.equal(o_t, o_h) and torch.equal(lses[0], lses[1]), (sparse, n_call)
+            if n_call == 0:
+                Kh = [K[s].double().cpu().numpy() for s in range(ns)]
+                Vh = [V[s].double().cpu().numpy() for s in range(ns)]
+                ih, ch = idx.cpu().numpy(), cnt.cpu().numpy()
+                lists = ((lambda s, h: ih[s, h, :ch[s, h]]) if sparse
+                         else (lambda s, h: np.arange(-(-lens[s] // B))))
+                _check_decode_rows(f64(o_h), f64(lses[1]), f64(q), Kh, Vh, lens, lists, B, d,
+                                   grp, TOL_ATTN_BF16)
+
+
 def test_decode_snapshot_resume_bit_identical():
     """The decode state (sketch caches, running block sums, walk rows) is plain
     device memory: a copy taken after some steps, restored, and stepped again
