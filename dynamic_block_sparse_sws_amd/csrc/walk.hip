@@ -240,37 +240,67 @@ void walk_kernel(
 //      (LDS), T = sum over the segment of x q, and the largest |x|;
 //   B  a wave scan of T, the wave totals and maxima to LDS, barrier;
 //   C  S = exclusive scan (+ the totals of the quarter's earlier waves), all
-//      scaled by 1 / max (T is linear in x, so the scale of a hop is applied
-//      after the barrier), then the rows' partial products k . S to LDS,
-//      barrier.
+//      scaled by the power of two nearest below 1 / max (T is linear in x, so
+//      the scale of a hop is applied after the barrier), then the rows'
+//      partial products k . S to LDS, barrier.
 constexpr int kRowThreads = 1024;
 constexpr int kRowSeg = 256;        // segments (threads per component quarter)
 constexpr int kRowBmax = 4096;      // ypart capacity (largest row)
+// LDS of the row kernel: the hops' partial products (ypart, 64 KB) share it
+// with the staging of the sketch rows before the first hop (144 KB: one
+// workgroup fills a CU's registers, so it may as well use the CU's LDS, and
+// larger chunks mean fewer load round trips).
+constexpr int kRowSmemFloats = 36864;
 constexpr int kRowLStream = kRowBmax / kRowSeg;   // rows per segment, streaming form
-
-// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
-// 16-lane rows, then broadcasts of lanes 15 and 31 into the following rows).
-__device__ __forceinline__ float wave_prefix_sum(float v) {
-  int x = __builtin_bit_cast(int, v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));  // row_shr:1
-  x = __builtin_bit_cast(int, v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));  // row_shr:2
-  x = __builtin_bit_cast(int, v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));  // row_shr:4
-  x = __builtin_bit_cast(int, v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));  // row_shr:8
-  x = __builtin_bit_cast(int, v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
-  x = __builtin_bit_cast(int, v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
-  return v;
-}
 
 template <int CTRL, int RMASK>
 __device__ __forceinline__ float dpp_shifted(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                CTRL, RMASK, 0xF, false));
 }
+
+// The cross-row steps of a wave-wide inclusive scan for N values: lane 15 of
+// rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.  These are
+// DPP adds that write only the receiving rows (row_mask), which the compiler
+// only forms as a zeroed move plus a masked move plus an add, so they are
+// written out here; the s_nop gives the two wait states a DPP read of a VGPR
+// needs after a VALU write of it (before the block, between the steps when a
+// value's own previous step is too close, and after the block for whatever
+// reads the results next).
+#define SWS_BC15(i) "v_add_f32_dpp %" #i ", %" #i ", %" #i " row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+#define SWS_BC31(i) "v_add_f32_dpp %" #i ", %" #i ", %" #i " row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+template <int N> struct CrossRows;
+template <> struct CrossRows<4> {
+  static __device__ __forceinline__ void add(float (&v)[4]) {
+    asm volatile("s_nop 1\n\t" SWS_BC15(0) SWS_BC15(1) SWS_BC15(2) SWS_BC15(3)
+                 SWS_BC31(0) SWS_BC31(1) SWS_BC31(2) SWS_BC31(3) "s_nop 1"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+  }
+};
+template <> struct CrossRows<8> {
+  static __device__ __forceinline__ void add(float (&v)[8]) {
+    asm volatile("s_nop 1\n\t" SWS_BC15(0) SWS_BC15(1) SWS_BC15(2) SWS_BC15(3) SWS_BC15(4)
+                 SWS_BC15(5) SWS_BC15(6) SWS_BC15(7) SWS_BC31(0) SWS_BC31(1) SWS_BC31(2)
+                 SWS_BC31(3) SWS_BC31(4) SWS_BC31(5) SWS_BC31(6) SWS_BC31(7) "s_nop 1"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7]));
+  }
+};
+template <> struct CrossRows<16> {
+  static __device__ __forceinline__ void add(float (&v)[16]) {
+    asm volatile("s_nop 1\n\t" SWS_BC15(0) SWS_BC15(1) SWS_BC15(2) SWS_BC15(3) SWS_BC15(4)
+                 SWS_BC15(5) SWS_BC15(6) SWS_BC15(7) SWS_BC15(8) SWS_BC15(9) SWS_BC15(10)
+                 SWS_BC15(11) SWS_BC15(12) SWS_BC15(13) SWS_BC15(14) SWS_BC15(15)
+                 SWS_BC31(0) SWS_BC31(1) SWS_BC31(2) SWS_BC31(3) SWS_BC31(4) SWS_BC31(5)
+                 SWS_BC31(6) SWS_BC31(7) SWS_BC31(8) SWS_BC31(9) SWS_BC31(10) SWS_BC31(11)
+                 SWS_BC31(12) SWS_BC31(13) SWS_BC31(14) SWS_BC31(15) "s_nop 1"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                   "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+  }
+};
+#undef SWS_BC15
+#undef SWS_BC31
 
 // The same scan for N independent values at once, step by step, so the DPP
 // read of one value is separated from its last write by the others.
@@ -284,22 +314,25 @@ __device__ __forceinline__ void wave_prefix_sum_n(float (&v)[N]) {
   for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x114, 0xF>(v[e]);   // row_shr:4
 #pragma unroll
   for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x118, 0xF>(v[e]);   // row_shr:8
-#pragma unroll
-  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x142, 0xA>(v[e]);   // row_bcast:15
-#pragma unroll
-  for (int e = 0; e < N; ++e) v[e] += dpp_shifted<0x143, 0xC>(v[e]);   // row_bcast:31
+  CrossRows<N>::add(v);
 }
 
-// Maximum of non-negative values over the wave, valid in lane 63 (the scan's
-// DPP pattern with max in place of add; absent lanes contribute 0).
+// Maximum of non-negative values over the wave, valid in lane 63.  Non-negative
+// floats order like their bit patterns, so the steps are unsigned maxima
+// (absent lanes contribute 0); the cross-row steps are written out as above.
 __device__ __forceinline__ float wave_max_nonneg(float v) {
-  v = fmaxf(v, dpp_shifted<0x111, 0xF>(v));
-  v = fmaxf(v, dpp_shifted<0x112, 0xF>(v));
-  v = fmaxf(v, dpp_shifted<0x114, 0xF>(v));
-  v = fmaxf(v, dpp_shifted<0x118, 0xF>(v));
-  v = fmaxf(v, dpp_shifted<0x142, 0xA>(v));
-  v = fmaxf(v, dpp_shifted<0x143, 0xC>(v));
-  return v;
+  unsigned u = __builtin_bit_cast(unsigned, v);
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x111, 0xF, 0xF, false));
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x112, 0xF, 0xF, false));
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x114, 0xF, 0xF, false));
+  u = max(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x118, 0xF, 0xF, false));
+  asm volatile("s_nop 1\n\t"
+               "v_max_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+               "s_nop 1\n\t"
+               "v_max_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+               "s_nop 1"
+               : "+v"(u));
+  return __builtin_bit_cast(float, u);
 }
 
 template <int KP, bool REG>
@@ -311,7 +344,9 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   constexpr int LR = REG ? 40 / CQ : kRowLStream;             // rows per segment (capacity)
   constexpr int NWAVE = kRowThreads / 64;
   constexpr int WPQ = kRowSeg / 64;                           // waves per quarter
-  __shared__ float ypart[4][kRowBmax];
+  __shared__ __attribute__((aligned(16))) float smem[kRowSmemFloats];
+  static_assert(kRowSmemFloats >= 4 * kRowBmax, "ypart fits");
+  float (*ypart)[kRowBmax] = reinterpret_cast<float (*)[kRowBmax]>(smem);
   __shared__ float wtot[NWAVE][CQ];
   __shared__ float wmax[NWAVE];
 
@@ -352,15 +387,15 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   float* rout = r_out + ((int64_t)seq * hq + h) * b_max;
 
   // sketch rows of the segment (REG), zero past the segment's end.  They go
-  // through LDS (the ypart area, unused until the first hop) in chunks of
+  // through LDS (the smem area, ypart's only after the first hop) in chunks of
   // whole segments, read from memory with contiguous 16-byte loads; the
   // 16-byte slots of a staged row are XOR-swizzled by the row index so the
   // threads of consecutive segments (rows L apart) read distinct banks.
   float qv[REG ? LR : 1][CQ], kv[REG ? LR : 1][CQ];
   if (REG) {
     constexpr int V4 = KP / 4;                  // float4 per row
-    constexpr int R = 8192 / KP;                // staged rows: q and k fill 64 KB
-    float4* stq = reinterpret_cast<float4*>(&ypart[0][0]);
+    constexpr int R = kRowSmemFloats / 2 / KP;  // staged rows: q and k fill smem
+    float4* stq = reinterpret_cast<float4*>(smem);
     float4* stk = stq + R * V4;
 #pragma unroll
     for (int l = 0; l < LR; ++l)
@@ -418,28 +453,34 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   for (int hop = 0; hop < s; ++hop) {
     // ---- A: x of the segment's rows, T, local max ----
     if (hop > 0) {
+      // REG: rows past the segment read LDS inside smem and are dropped (no
+      // branch); the streaming form's 16 rows would hold too many registers
 #pragma unroll
-      for (int l = 0; l < LR; ++l)
-        xr[l] = l < nv ? ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
-                             inv_sqrt_k
-                       : 0.f;
+      for (int l = 0; l < LR; ++l) {
+        if (REG) {
+          const float y = ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
+                          inv_sqrt_k;
+          xr[l] = l < nv ? y : 0.f;
+        } else {
+          xr[l] = l < nv ? ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
+                               inv_sqrt_k
+                         : 0.f;
+        }
+      }
     }
-    float T[CQ];
+    float S[CQ];                                              // T, then its scan
 #pragma unroll
-    for (int e = 0; e < CQ; ++e) T[e] = 0.f;
+    for (int e = 0; e < CQ; ++e) S[e] = 0.f;
     float lmax = 0.f;
 #pragma unroll
     for (int l = 0; l < LR; ++l) {
       if (REG || l < nv) {
 #pragma unroll
-        for (int e = 0; e < CQ; ++e) T[e] += xr[l] * qget(l, e);
+        for (int e = 0; e < CQ; ++e) S[e] += xr[l] * qget(l, e);
       }
       lmax = fmaxf(lmax, fabsf(xr[l]));
     }
     // ---- B: wave scan, totals and maxima ----
-    float S[CQ];
-#pragma unroll
-    for (int e = 0; e < CQ; ++e) S[e] = T[e];
     wave_prefix_sum_n<CQ>(S);
     lmax = wave_max_nonneg(lmax);
     if (lane == 63) {
@@ -447,15 +488,24 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
       for (int e = 0; e < CQ; ++e) wtot[wave][e] = S[e];
       wmax[wave] = lmax;
     }
+    // exclusive: the inclusive scan shifted up one lane (wave_shr:1, lane 0
+    // gets 0), so T need not stay live through the scan
 #pragma unroll
-    for (int e = 0; e < CQ; ++e) S[e] -= T[e];                 // exclusive
+    for (int e = 0; e < CQ; ++e)
+      S[e] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, S[e]), 0x138, 0xF, 0xF, true));
     __syncthreads();
     float gmax = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
-    const float sc = gmax > 0.f ? 1.0f / gmax : 1.0f;
+    // the hop's scale: a power of two near 1 / gmax (exact products; any
+    // positive scale leaves the row's direction, and so the result, unchanged)
+    const float sc =
+        gmax > 0.f ? __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(gmax), 126))
+                   : 1.0f;
     {
-      const int wq = wave - p * WPQ;                          // earlier waves of the quarter
+      // earlier waves of the quarter (uniform over the wave)
+      const int wq = __builtin_amdgcn_readfirstlane(wave - p * WPQ);
 #pragma unroll
       for (int w2 = 0; w2 < WPQ - 1; ++w2) {
         if (w2 < wq) {
