@@ -281,8 +281,8 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         for l, st in enumerate(state):
             dense = l < cfg.n_dense
             a = T.ev() if T else None
-            sws.sketch_append(st["qst"][t], pos[t], B, kd, signs_d, cols_d, st["rq"], st["qsk"])
-            sws.sketch_append(st["knew"][t], pos[t], B, kd, signs_d, cols_d, st["rk"], st["ksk"])
+            sws.sketch_append_qk(st["qst"][t], st["knew"][t], pos[t], B, kd, signs_d, cols_d,
+                                 st["rq"], st["rk"], st["qsk"], st["ksk"])
             sws.walk_update_row(st["qsk"], st["ksk"], cur[t], cfg.s, None if l == 0 else r, r)
             uidx, ucnt, umask, _, _ = sws.select_topk_row(r, hq, hkv, cur[t], b_max, cfg.rho,
                                                           dense=dense,
@@ -347,8 +347,8 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         def graph_step():
             for l, st in enumerate(state):
                 dense = l < cfg.n_dense
-                sws.sketch_append(q_buf[l], pcc[0], B, kd, signs_d, cols_d, st["rq"], st["qsk"])
-                sws.sketch_append(k_buf[l], pcc[0], B, kd, signs_d, cols_d, st["rk"], st["ksk"])
+                sws.sketch_append_qk(q_buf[l], k_buf[l], pcc[0], B, kd, signs_d, cols_d,
+                                     st["rq"], st["rk"], st["qsk"], st["ksk"])
                 sws.walk_update_row(st["qsk"], st["ksk"], pcc[1], cfg.s, None if l == 0 else r, r)
                 u = sws.select_topk_row(r, hq, hkv, pcc[1], b_max, cfg.rho, dense=dense,
                                         out=dbufs if dense else ubufs)

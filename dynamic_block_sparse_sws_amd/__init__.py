@@ -16,9 +16,9 @@ import numpy as np
 import torch
 
 __all__ = [
-    "SwsError", "lib", "F32", "BF16", "FP8_E4M3", "WALK_DEFAULT", "WALK_POWER", "WALK_SOFTMAX",
+    "SwsError", "lib", "F32", "BF16", "FP8_E4M3", "KV_HEAD_MAJOR", "WALK_DEFAULT", "WALK_POWER", "WALK_SOFTMAX",
     "SELECT_DENSE", "SELECT_ROW_TAU", "SELECT_GROUP", "Geometry", "geometry", "walk_state_numel",
-    "sketch", "sketch_append", "walk_update", "walk_update_row", "walk_update_variant",
+    "sketch", "sketch_append", "sketch_append_qk", "walk_update", "walk_update_row", "walk_update_variant",
     "walk_variant_workspace_size", "select_topk",
     "select_topk_row", "sparse_attn_prefill", "sparse_attn_decode", "decode_workspace_size",
     "sparse_attn_decode_paged",
@@ -43,7 +43,7 @@ LIB_PATH = os.path.join(_HERE, "libsws.so")
 
 EXPORTED_SYMBOLS = (
     "sws_version", "sws_status_string", "sws_last_error_detail", "sws_sketch",
-    "sws_sketch_append", "sws_walk_update", "sws_walk_update_row", "sws_select_topk",
+    "sws_sketch_append", "sws_sketch_append_qk", "sws_walk_update", "sws_walk_update_row", "sws_select_topk",
     "sws_select_topk_row", "sws_sparse_attn_prefill", "sws_sparse_attn_decode",
     "sws_decode_workspace_size", "sws_prefill_workspace_size", "sws_select_topk_flags",
     "sws_walk_update_variant", "sws_walk_variant_workspace_size", "sws_walk_update_row_variant",
@@ -74,6 +74,8 @@ _SIGS = {
                    ctypes.c_int),
     "sws_sketch_append": ([_P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P],
                           ctypes.c_int),
+    "sws_sketch_append_qk": ([_P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                              _P, _P, _I, _P], ctypes.c_int),
     "sws_walk_update": ([_P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P], ctypes.c_int),
     "sws_walk_update_row": ([_P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P], ctypes.c_int),
     "sws_walk_update_variant": ([_P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _I64, _P,
@@ -211,6 +213,23 @@ def sketch_append(x_new: torch.Tensor, pos: torch.Tensor, B: int, k: int, signs,
     _check("sws_sketch_append", lib().sws_sketch_append(
         _ptr(x_new), _dtype_code(x_new), _ptr(pos), n_seqs, H, d, B, k, _ptr(signs), _ptr(cols),
         _ptr(run_sum), _ptr(sketch_cache), b_max, _stream(stream)))
+
+
+def sketch_append_qk(q_new: torch.Tensor, k_new: torch.Tensor, pos: torch.Tensor, B: int, k: int,
+                     signs, cols, run_q: torch.Tensor, run_k: torch.Tensor, q_cache: torch.Tensor,
+                     k_cache: torch.Tensor, stream=None):
+    """sketch_append of the query rows and of the key rows in one launch."""
+    n_seqs, hq, d = q_new.shape
+    hkv = k_new.shape[1]
+    if k_new.dtype != q_new.dtype:
+        raise TypeError("q_new and k_new must share a dtype")
+    b_max = q_cache.shape[2]
+    if k_cache.shape[2] != b_max:
+        raise ValueError("q_cache and k_cache differ in b_max")
+    _check("sws_sketch_append_qk", lib().sws_sketch_append_qk(
+        _ptr(q_new), _ptr(k_new), _dtype_code(q_new), _ptr(pos), n_seqs, hq, hkv, d, B, k,
+        _ptr(signs), _ptr(cols), _ptr(run_q), _ptr(run_k), _ptr(q_cache), _ptr(k_cache), b_max,
+        _stream(stream)))
 
 
 def walk_update(q_sk: torch.Tensor, k_sk: torch.Tensor, geo: Geometry, s: int,

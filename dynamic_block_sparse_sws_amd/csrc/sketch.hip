@@ -98,15 +98,31 @@ __global__ __launch_bounds__(kThreads) void sketch_kernel(
   }
 }
 
+// One tensor of new-token rows to append: x [n_seqs][n_heads][D], its running
+// block sums and its sketch cache; `slices` workgroups per sequence cover its
+// heads, hpw at a time.
+template <typename T>
+struct AppendSet {
+  const T* x;
+  float* run_sum;
+  float* cache;
+  int n_heads, hpw, slices;
+};
+
+// Workgroup (s, y) appends the new token of sequence s for one slice of heads
+// of set a0 (y < a0.slices) or a1 (the rest), so the query and key rows of a
+// decode step can share one launch.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void sketch_append_kernel(
-    const T* __restrict__ x_new, const int32_t* __restrict__ pos, int n_heads, int hpw, int B,
-    int k, const int8_t* __restrict__ signs, const int32_t* __restrict__ cols,
-    float* __restrict__ run_sum, float* __restrict__ cache, int b_max, float inv_sqrt_k) {
+    AppendSet<T> a0, AppendSet<T> a1, const int32_t* __restrict__ pos, int B, int k,
+    const int8_t* __restrict__ signs, const int32_t* __restrict__ cols, int b_max,
+    float inv_sqrt_k) {
   __shared__ float f[kSliceElems];
   const int s = blockIdx.x;
-  const int h0 = blockIdx.y * hpw;
-  const int nh = min(hpw, n_heads - h0);
+  const bool second = (int)blockIdx.y >= a0.slices;
+  const AppendSet<T> a = second ? a1 : a0;
+  const int h0 = (second ? blockIdx.y - a0.slices : blockIdx.y) * a.hpw;
+  const int nh = min(a.hpw, a.n_heads - h0);
   const int p = pos[s];
   const int c = p / B;
   const int off = p - c * B;
@@ -114,10 +130,10 @@ __global__ __launch_bounds__(kThreads) void sketch_append_kernel(
   const int width = nh * D;
   const int col = threadIdx.x * 8;
   if (col < width) {
-    const int64_t base = ((int64_t)s * n_heads + h0) * D + col;
+    const int64_t base = ((int64_t)s * a.n_heads + h0) * D + col;
     float v[8];
-    load8_f32(x_new + base, v);
-    float* rs = run_sum + base;
+    load8_f32(a.x + base, v);
+    float* rs = a.run_sum + base;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float sum = (off == 0) ? v[e] : rs[e] + v[e];
@@ -131,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void sketch_append_kernel(
   for (int e = threadIdx.x; e < nh * k; e += kThreads) {
     const int hh = e / k;
     const int cc = e % k;
-    cache[(((int64_t)s * n_heads + h0 + hh) * b_max + c) * k + cc] = f[hh * D + cols[cc]] * inv_sqrt_k;
+    a.cache[(((int64_t)s * a.n_heads + h0 + hh) * b_max + c) * k + cc] =
+        f[hh * D + cols[cc]] * inv_sqrt_k;
   }
 }
 
@@ -152,14 +169,22 @@ hipError_t run_sketch(const void* x, const int32_t* cu_seqlens, const int32_t* c
 }
 
 template <typename T, int D>
-hipError_t run_append(const void* x_new, const int32_t* pos, int n_seqs, int n_heads, int B,
-                      int k, const int8_t* signs, const int32_t* cols, float* run_sum,
-                      float* cache, int b_max, hipStream_t st) {
+AppendSet<T> append_set(const void* x, int n_heads, float* run_sum, float* cache) {
   const int hpw = min(n_heads, kSliceElems / D);
-  dim3 grid(n_seqs, (n_heads + hpw - 1) / hpw);
-  hipLaunchKernelGGL((sketch_append_kernel<T, D>), grid, dim3(kThreads), 0, st,
-                     static_cast<const T*>(x_new), pos, n_heads, hpw, B, k, signs, cols,
-                     run_sum, cache, b_max, 1.0f / sqrtf((float)k));
+  return AppendSet<T>{static_cast<const T*>(x), run_sum, cache, n_heads, hpw,
+                      n_heads > 0 ? (n_heads + hpw - 1) / hpw : 0};
+}
+
+// Appends set 0 and, when its head count is positive, set 1 in one launch.
+template <typename T, int D>
+hipError_t run_append(const void* x0, int nh0, float* rs0, float* c0, const void* x1, int nh1,
+                      float* rs1, float* c1, const int32_t* pos, int n_seqs, int B, int k,
+                      const int8_t* signs, const int32_t* cols, int b_max, hipStream_t st) {
+  const AppendSet<T> a0 = append_set<T, D>(x0, nh0, rs0, c0);
+  const AppendSet<T> a1 = append_set<T, D>(x1, nh1, rs1, c1);
+  dim3 grid(n_seqs, a0.slices + a1.slices);
+  hipLaunchKernelGGL((sketch_append_kernel<T, D>), grid, dim3(kThreads), 0, st, a0, a1, pos, B,
+                     k, signs, cols, b_max, 1.0f / sqrtf((float)k));
   return hipGetLastError();
 }
 
@@ -184,23 +209,21 @@ hipError_t launch_sketch(const void* x, int dtype, const int32_t* cu_seqlens,
                                signs, cols, sketch_out, ld_head, sum_out, st);
 }
 
-hipError_t launch_sketch_append(const void* x_new, int dtype, const int32_t* pos, int n_seqs,
-                                int n_heads, int d, int B, int k, const int8_t* signs,
-                                const int32_t* cols, float* run_sum, float* sketch_cache,
-                                int b_max, hipStream_t st) {
+hipError_t launch_sketch_append(const void* x0, int nh0, float* rs0, float* c0, const void* x1,
+                                int nh1, float* rs1, float* c1, int dtype, const int32_t* pos,
+                                int n_seqs, int d, int B, int k, const int8_t* signs,
+                                const int32_t* cols, int b_max, hipStream_t st) {
   if (n_seqs == 0) return hipSuccess;
+#define SWS_APPEND(T, D)                                                                       \
+  return run_append<T, D>(x0, nh0, rs0, c0, x1, nh1, rs1, c1, pos, n_seqs, B, k, signs, cols,  \
+                          b_max, st)
   if (dtype == SWS_BF16) {
-    if (d == 128)
-      return run_append<uint16_t, 128>(x_new, pos, n_seqs, n_heads, B, k, signs, cols, run_sum,
-                                       sketch_cache, b_max, st);
-    return run_append<uint16_t, 64>(x_new, pos, n_seqs, n_heads, B, k, signs, cols, run_sum,
-                                    sketch_cache, b_max, st);
+    if (d == 128) SWS_APPEND(uint16_t, 128);
+    SWS_APPEND(uint16_t, 64);
   }
-  if (d == 128)
-    return run_append<float, 128>(x_new, pos, n_seqs, n_heads, B, k, signs, cols, run_sum,
-                                  sketch_cache, b_max, st);
-  return run_append<float, 64>(x_new, pos, n_seqs, n_heads, B, k, signs, cols, run_sum,
-                               sketch_cache, b_max, st);
+  if (d == 128) SWS_APPEND(float, 128);
+  SWS_APPEND(float, 64);
+#undef SWS_APPEND
 }
 
 }  // namespace sws

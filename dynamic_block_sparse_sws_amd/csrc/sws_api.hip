@@ -105,9 +105,40 @@ int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t 
     return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d n_heads=%d b_max=%d", fn, n_seqs, n_heads, b_max);
   if (!aligned16(x_new) || !aligned16(run_sum))
     return fail(SWS_ERR_SHAPE, "%s: x_new / run_sum not 16-byte aligned", fn);
-  return launched(sws::launch_sketch_append(x_new, dtype, pos, n_seqs, n_heads, d, B, k, signs,
-                                            cols, run_sum, sketch_cache, b_max,
-                                            (hipStream_t)stream),
+  return launched(sws::launch_sketch_append(x_new, n_heads, run_sum, sketch_cache, nullptr, 0,
+                                            nullptr, nullptr, dtype, pos, n_seqs, d, B, k, signs,
+                                            cols, b_max, (hipStream_t)stream),
+                  fn);
+}
+
+int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const int32_t* pos,
+                         int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                         int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
+                         float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
+                         void* stream) {
+  const char* fn = "sws_sketch_append_qk";
+  REQUIRE_PTR(q_new);
+  REQUIRE_PTR(k_new);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(signs);
+  REQUIRE_PTR(cols);
+  REQUIRE_PTR(run_sum_q);
+  REQUIRE_PTR(run_sum_k);
+  REQUIRE_PTR(q_cache);
+  REQUIRE_PTR(k_cache);
+  if (!dtype_ok(dtype)) return fail(SWS_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (d != 64 && d != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: d=%d not in {64,128}", fn, d);
+  if (B != 64 && B != 128) return fail(SWS_ERR_UNSUPPORTED, "%s: B=%d not in {64,128}", fn, B);
+  if (k < 1 || k > d || k > 64) return fail(SWS_ERR_UNSUPPORTED, "%s: k=%d outside [1, min(d,64)]", fn, k);
+  if (n_seqs < 0 || hq < 1 || hkv < 1 || b_max < 1)
+    return fail(SWS_ERR_SHAPE, "%s: n_seqs=%d hq=%d hkv=%d b_max=%d", fn, n_seqs, hq, hkv, b_max);
+  if ((int64_t)hq + hkv > 65535)
+    return fail(SWS_ERR_SHAPE, "%s: hq + hkv = %lld > 65535", fn, (long long)hq + hkv);
+  if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(run_sum_q) || !aligned16(run_sum_k))
+    return fail(SWS_ERR_SHAPE, "%s: q_new / k_new / run sums not 16-byte aligned", fn);
+  return launched(sws::launch_sketch_append(q_new, hq, run_sum_q, q_cache, k_new, hkv, run_sum_k,
+                                            k_cache, dtype, pos, n_seqs, d, B, k, signs, cols,
+                                            b_max, (hipStream_t)stream),
                   fn);
 }
 

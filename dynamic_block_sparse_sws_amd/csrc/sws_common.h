@@ -71,10 +71,12 @@ hipError_t launch_sketch(const void* x, int dtype, const int32_t* cu_seqlens,
                          const int32_t* cu_blocks, int n_seqs, int total_blocks, int n_heads,
                          int d, int B, int k, const int8_t* signs, const int32_t* cols,
                          float* sketch_out, int64_t ld_head, float* sum_out, hipStream_t st);
-hipError_t launch_sketch_append(const void* x_new, int dtype, const int32_t* pos, int n_seqs,
-                                int n_heads, int d, int B, int k, const int8_t* signs,
-                                const int32_t* cols, float* run_sum, float* sketch_cache,
-                                int b_max, hipStream_t st);
+// Appends the new-token rows of one tensor (x0, nh0 heads) and, if nh1 > 0, of
+// a second one, in one launch.
+hipError_t launch_sketch_append(const void* x0, int nh0, float* rs0, float* c0, const void* x1,
+                                int nh1, float* rs1, float* c1, int dtype, const int32_t* pos,
+                                int n_seqs, int d, int B, int k, const int8_t* signs,
+                                const int32_t* cols, int b_max, hipStream_t st);
 hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
                        const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks,
                        int s, const float* R_prev, float* R_out, hipStream_t st);

@@ -155,6 +155,22 @@ int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t 
                       void* stream);
 
 /*
+ * sws_sketch_append_qk - sws_sketch_append of a decode step's query and key
+ * rows in one launch (the same section: both sketches take the new token
+ * each step).  Equal, bit for bit, to sws_sketch_append on (q_new, hq heads,
+ * run_sum_q, q_cache) and on (k_new, hkv heads, run_sum_k, k_cache) with the
+ * same pos, B, k, signs and cols; dtype applies to both q_new and k_new.
+ *   q_new [n_seqs][hq][d], k_new [n_seqs][hkv][d]; run_sum_q [n_seqs][hq][d],
+ *   run_sum_k [n_seqs][hkv][d]; q_cache [n_seqs][hq][b_max][k], k_cache
+ *   [n_seqs][hkv][b_max][k]; hq + hkv <= 65535
+ */
+int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const int32_t* pos,
+                         int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                         int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
+                         float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
+                         void* stream);
+
+/*
  * sws_walk_update - the walk state of one layer (blog page, section 4:
  * R^0 = (A^0)^s, R^l = R^(l-1) (A^l)^s), with A = M, the causal sketched
  * block scores M[i][j] = qs_i . ks_j / sqrt(k) for j <= i and 0 for j > i

@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     L = sws.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -143,3 +143,9 @@ def test_other_entry_points_validation():
                                     f(0.1), P, N, P, need, N) == 3
     # append: b_max 0
     assert L.sws_sketch_append(P, 1, P, 2, 8, 128, 64, 32, P, P, P, P, 0, N) == 2
+    # fused query / key append: k_new NULL, hkv 0, bad k, misaligned run sum
+    assert L.sws_sketch_append_qk(P, N, 1, P, 2, 32, 8, 128, 64, 32, P, P, P, P, P, P, 9, N) == 1
+    assert L.sws_sketch_append_qk(P, P, 1, P, 2, 32, 0, 128, 64, 32, P, P, P, P, P, P, 9, N) == 2
+    assert L.sws_sketch_append_qk(P, P, 1, P, 2, 32, 8, 128, 64, 65, P, P, P, P, P, P, 9, N) == 3
+    assert L.sws_sketch_append_qk(P, P, 1, P, 2, 32, 8, 128, 64, 32, P, P, P,
+                                  ctypes.c_void_p(4100), P, P, 9, N) == 2

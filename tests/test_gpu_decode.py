@@ -495,6 +495,38 @@ def test_decode_head_major_layouts(d, B, hq, hkv, lens, share):
                                    grp, TOL_ATTN_BF16)
 
 
+@pytest.mark.parametrize("dtype,d,B,kd,hq,hkv", [
+    (torch.bfloat16, 128, 64, 32, 12, 3),
+    (torch.float32, 64, 128, 16, 4, 4),
+])
+def test_sketch_append_qk_matches_two_appends(dtype, d, B, kd, hq, hkv):
+    """The fused query / key append leaves the running sums and both sketch
+    caches bit for bit where two separate appends leave them, over steps that
+    open, fill and complete blocks."""
+    _print("append_qk", dtype, d, B, kd, hq, hkv)
+    ns, steps = 3, 2 * B + 5
+    pos0 = torch.tensor([0, B - 1, B + 7], dtype=torch.int32, device="cuda")
+    b_max = int((pos0.max() + steps) // B) + 1
+    gr = torch.Generator(device="cuda")
+    gr.manual_seed(gen.seed_for(14, d, B, hq))
+    q = torch.randn((steps, ns, hq, d), generator=gr, device="cuda").to(dtype)
+    k = torch.randn((steps, ns, hkv, d), generator=gr, device="cuda").to(dtype)
+    signs, cols = gen.hadamard_tables(d, kd)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    st = [[torch.zeros((ns, h, d), device="cuda"), torch.zeros((ns, h, b_max, kd), device="cuda")]
+          for _ in range(2) for h in (hq, hkv)]
+    for t in range(steps):
+        pos = pos0 + t
+        sws.sketch_append(q[t], pos, B, kd, sd, cd, st[0][0], st[0][1])
+        sws.sketch_append(k[t], pos, B, kd, sd, cd, st[1][0], st[1][1])
+        sws.sketch_append_qk(q[t], k[t], pos, B, kd, sd, cd, st[2][0], st[3][0], st[2][1],
+                             st[3][1])
+        if t % 17 == 0 or t == steps - 1:
+            torch.cuda.synchronize()
+            for a, b in ((st[0], st[2]), (st[1], st[3])):
+                assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), t
+
+
 def test_decode_snapshot_resume_bit_identical():
     """The decode state (sketch caches, running block sums, walk rows) is plain
     device memory: a copy taken after some steps, restored, and stepped again

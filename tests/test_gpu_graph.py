@@ -1,7 +1,7 @@
 """Decode steps captured once as a HIP graph (torch.cuda.CUDAGraph over the
 library's launches on static buffers) and replayed step after step, with
 eager work and synchronisations between the replays: every replay's outputs
-equal the eager calls' bit for bit."""
+equal the eager calls' bit for bit (token-major and head-major caches)."""
 import pytest
 import torch
 
@@ -47,7 +47,10 @@ def test_decode_step_graph_replays_equal_eager():
                           for t in range(steps)]).contiguous()
         kn = torch.stack([torch.stack([full[s]["k"][prefixes[s] + t] for s in range(ns)])
                           for t in range(steps)]).contiguous()
-        layers.append({"kc": kc, "vc": vc, "st": st, "qn": qn, "kn": kn,
+        hm = l == 1                      # layer 1 keeps a head-major cache
+        if hm:
+            kc, vc = (x.permute(0, 2, 1, 3).contiguous() for x in (kc, vc))
+        layers.append({"kc": kc, "vc": vc, "hm": hm, "st": st, "qn": qn, "kn": kn,
                        "out": torch.empty((ns, hq, d), dtype=torch.bfloat16, device="cuda")})
     snap = [{k: v.clone() for k, v in L["st"].items()} for L in layers]
     P_t = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
@@ -66,13 +69,13 @@ def test_decode_step_graph_replays_equal_eager():
     def step(q_of, k_of, pos, cur, ctx):
         for l, L in enumerate(layers):
             st = L["st"]
-            sws.sketch_append(q_of(l), pos, B, kd, sd, cd, st["rq"], st["qsk"])
-            sws.sketch_append(k_of(l), pos, B, kd, sd, cd, st["rk"], st["ksk"])
+            sws.sketch_append_qk(q_of(l), k_of(l), pos, B, kd, sd, cd, st["rq"], st["rk"],
+                                 st["qsk"], st["ksk"])
             sws.walk_update_row(st["qsk"], st["ksk"], cur, cfg.s, None if l == 0 else r, r)
             u = sws.select_topk_row(r, hq, hkv, cur, b_max, rho, dense=l == 0,
                                     out=dbufs if l == 0 else ubufs)
             sws.sparse_attn_decode(q_of(l), L["kc"], L["vc"], ctx, B, u[0], u[1], u[2],
-                                   out=L["out"], lse=lse[l], ws=ws)
+                                   out=L["out"], lse=lse[l], ws=ws, head_major=L["hm"])
 
     def outputs():
         n_u = ubufs[1].clone()
