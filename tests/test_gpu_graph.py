@@ -1,7 +1,8 @@
 """Decode steps captured once as a HIP graph (torch.cuda.CUDAGraph over the
 library's launches on static buffers) and replayed step after step, with
 eager work and synchronisations between the replays: every replay's outputs
-equal the eager calls' bit for bit (token-major and head-major caches)."""
+equal the eager calls' bit for bit (token-major and head-major caches; one
+stream, or the select chain on a side stream one layer ahead)."""
 import pytest
 import torch
 
@@ -11,11 +12,15 @@ import gen
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_step_graph_replays_equal_eager():
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_decode_step_graph_replays_equal_eager(two_streams):
+    """two_streams: each layer's select chain is captured on a side stream,
+    one layer ahead of the attention on the capturing stream (list buffers
+    alternate between layers)."""
     cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=8, hkv=2, k=32)
     B, d, kd, hq, hkv = cfg.B, cfg.d, cfg.k, cfg.hq, cfg.hkv
     prefixes, steps, rho = (190, 250), 8, 30
-    ns, n_layers = len(prefixes), 2
+    ns, n_layers = len(prefixes), 4
     max_ctx = max(prefixes) + steps
     b_max = -(-max_ctx // B)
     signs, cols = gen.hadamard_tables(d, kd)
@@ -47,7 +52,7 @@ def test_decode_step_graph_replays_equal_eager():
                           for t in range(steps)]).contiguous()
         kn = torch.stack([torch.stack([full[s]["k"][prefixes[s] + t] for s in range(ns)])
                           for t in range(steps)]).contiguous()
-        hm = l == 1                      # layer 1 keeps a head-major cache
+        hm = l % 2 == 1                  # odd layers keep head-major caches
         if hm:
             kc, vc = (x.permute(0, 2, 1, 3).contiguous() for x in (kc, vc))
         layers.append({"kc": kc, "vc": vc, "hm": hm, "st": st, "qn": qn, "kn": kn,
@@ -55,32 +60,63 @@ def test_decode_step_graph_replays_equal_eager():
     snap = [{k: v.clone() for k, v in L["st"].items()} for L in layers]
     P_t = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
     uw = sws.union_width(rho, b_max, hq // hkv)
-    ubufs = (torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"),
-             torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
-             torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"), None, None)
-    dbufs = (torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"),
-             torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
-             torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"), None, None)
+    # list buffers alternate between layers (sparse lists "u", dense "d")
+    bufs = [{"u": (torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"),
+                   torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
+                   torch.empty((ns, hkv, uw), dtype=torch.int32, device="cuda"), None, None),
+             "d": (torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"),
+                   torch.empty((ns, hkv), dtype=torch.int32, device="cuda"),
+                   torch.empty((ns, hkv, b_max), dtype=torch.int32, device="cuda"), None, None)}
+            for _ in range(2)]
     ws = torch.empty(sws.decode_workspace_size(ns, hq, hkv, d, B, b_max), dtype=torch.uint8,
                      device="cuda")
     r = torch.empty((ns, hq, b_max), device="cuda")
     lse = [torch.empty((ns, hq), device="cuda") for _ in layers]
 
+    def chain(l, q_of, k_of, pos, cur):
+        st = layers[l]["st"]
+        sws.sketch_append_qk(q_of(l), k_of(l), pos, B, kd, sd, cd, st["rq"], st["rk"],
+                             st["qsk"], st["ksk"])
+        sws.walk_update_row(st["qsk"], st["ksk"], cur, cfg.s, None if l == 0 else r, r)
+        return sws.select_topk_row(r, hq, hkv, cur, b_max, rho, dense=l == 0,
+                                   out=bufs[l % 2]["d" if l == 0 else "u"])
+
+    def attend(l, q_of, ctx, u):
+        L = layers[l]
+        sws.sparse_attn_decode(q_of(l), L["kc"], L["vc"], ctx, B, u[0], u[1], u[2],
+                               out=L["out"], lse=lse[l], ws=ws, head_major=L["hm"])
+
     def step(q_of, k_of, pos, cur, ctx):
-        for l, L in enumerate(layers):
-            st = L["st"]
-            sws.sketch_append_qk(q_of(l), k_of(l), pos, B, kd, sd, cd, st["rq"], st["rk"],
-                                 st["qsk"], st["ksk"])
-            sws.walk_update_row(st["qsk"], st["ksk"], cur, cfg.s, None if l == 0 else r, r)
-            u = sws.select_topk_row(r, hq, hkv, cur, b_max, rho, dense=l == 0,
-                                    out=dbufs if l == 0 else ubufs)
-            sws.sparse_attn_decode(q_of(l), L["kc"], L["vc"], ctx, B, u[0], u[1], u[2],
-                                   out=L["out"], lse=lse[l], ws=ws, head_major=L["hm"])
+        for l in range(n_layers):
+            attend(l, q_of, ctx, chain(l, q_of, k_of, pos, cur))
+
+    side = torch.cuda.Stream()
+
+    def step_2s(q_of, k_of, pos, cur, ctx):
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        done_attn = []
+        for l in range(n_layers):
+            with torch.cuda.stream(side):
+                if l >= 2:                   # layer l - 2's lists are read until then
+                    side.wait_event(done_attn[l - 2])
+                u = chain(l, q_of, k_of, pos, cur)
+                ev = torch.cuda.Event()
+                ev.record(side)
+            main.wait_event(ev)
+            attend(l, q_of, ctx, u)
+            done_attn.append(torch.cuda.Event())
+            done_attn[-1].record(main)
+        main.wait_stream(side)
 
     def outputs():
-        n_u = ubufs[1].clone()
-        lists = [ubufs[0][s, g, :n_u[s, g]].clone() for s in range(ns) for g in range(hkv)]
-        return [r.clone(), n_u, *lists, *[L["out"].clone() for L in layers],
+        out = []
+        for ub in (bufs[0]["u"], bufs[1]["u"]):          # layers 2 and 3
+            n_u = ub[1].clone()
+            out += [n_u] + [ub[0][s, g, :n_u[s, g]].clone() for s in range(ns)
+                            for g in range(hkv)]
+        lists = out
+        return [r.clone(), *lists, *[L["out"].clone() for L in layers],
                 *[x.clone() for x in lse], *[L["st"]["qsk"].clone() for L in layers]]
 
     eager = []
@@ -100,7 +136,8 @@ def test_decode_step_graph_replays_equal_eager():
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step(lambda l: q_buf[l], lambda l: k_buf[l], pcc[0], pcc[1], pcc[2])
+        (step_2s if two_streams else step)(lambda l: q_buf[l], lambda l: k_buf[l], pcc[0],
+                                           pcc[1], pcc[2])
     for t in range(steps):
         pos = P_t + t
         for l, L in enumerate(layers):
