@@ -47,6 +47,43 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
   return v;
 }
 
+// Final pass over a workgroup's rows i0 .. i0 + nrows - 1 (those inside the
+// sequence): each row divided by its largest magnitude m[r] (an all-zero row
+// stays zero), entries above the diagonal set to zero.  The rows are walked as
+// one flat range, four accesses per thread at a time, all loads before any
+// store, so every thread keeps several loads in flight (row by row, each
+// thread's single load per row would expose the memory latency once per row).
+template <int NT>
+__device__ __forceinline__ void finalize_rows(float* Rh, const float* m, int i0, int nrows,
+                                              int b) {
+  const int rows = min(nrows, b - i0);
+  if (rows <= 0) return;
+  const int total = rows * b;                 // <= 64 * 4096
+  const float inv_b = 1.0f / (float)b;
+  float* base = Rh + (int64_t)i0 * b;
+  for (int e0 = threadIdx.x; e0 < total; e0 += 4 * NT) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * NT;
+      v[u] = e < total ? base[e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * NT;
+      if (e < total) {
+        // row and column of e (the float quotient is off by at most one)
+        int rr = (int)((float)e * inv_b);
+        int j = e - rr * b;
+        if (j < 0) { --rr; j += b; }
+        else if (j >= b) { ++rr; j -= b; }
+        const float mm = m[rr];
+        base[e] = (j <= i0 + rr && mm > 0.f) ? v[u] / mm : 0.f;
+      }
+    }
+  }
+}
+
 constexpr int kWalkThreads = 256;
 constexpr int kTileJ = 64;
 
@@ -213,17 +250,275 @@ void walk_kernel(
   if (part == 0) smax[r] = mx;
   __syncthreads();
   // final pass: divide by the row maximum, zero the upper triangle
-  for (int rr = 0; rr < ROWS; ++rr) {
-    const int ii = i0 + rr;
-    if (ii >= b) break;
-    const float m = smax[rr];
-    float* row = Rh + (int64_t)ii * b;
-    for (int j = tid; j < b; j += kWalkThreads) {
-      float v = 0.f;
-      if (j <= ii && m > 0.f) v = row[j] / m;
-      row[j] = v;
+  finalize_rows<kWalkThreads>(Rh, smax, i0, ROWS, b);
+}
+
+// ---------------------------------------------------------------------------
+// prefill on the matrix cores (fp32 MFMA, k <= 32)
+// ---------------------------------------------------------------------------
+// The same walk, one workgroup per 64-row tile I of one head, its s hops
+// streaming the 64-column tiles J from the diagonal tile down.  Within a
+// tile, the suffix scan becomes two products: with M_J the tile's own
+// lower-triangular block of M and C the carry (rows i: sum over the later
+// tiles of x[i][m] q_m),
+//   Y_IJ = X_IJ M_J + C K_J^T,     C += X_IJ Q_J,
+// all on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate).  That is about
+// twice the multiply-adds of the scan, on units with twice the vector rate
+// and none of its per-column shuffles.  Wave (wi, wj) owns the 32 x 32
+// quadrant (rows 32 wi.., columns 32 wj..) of Y; it also forms quadrant
+// (wj, wi) of M_J^T and the part of X Q_J over the columns m in 32 wj.. (two
+// carry partials, summed when read).  Operand layouts for 32x32x2: lane l
+// feeds A[l % 32][l / 32] and B[l / 32][l % 32], and holds D[8 (r / 4) +
+// 4 (l / 32) + r % 4][l % 32] in accumulator r; the two k slots of an
+// instruction take two contiguous halves of the contraction (slot h, step t:
+// index h * n / 2 + t), so every lane reads its operands as contiguous runs.
+constexpr int kWmRows = 64;
+constexpr int kWmK = 32;
+
+// Workgroup barrier that orders LDS only: __syncthreads also waits for every
+// outstanding global load and store, which would expose the next tile's
+// prefetch and this tile's write-back at each of a tile's barriers.  Global
+// writes that other threads read later are ordered by full barriers placed
+// once per hop (see the kernel).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+constexpr int kWmPad = 68;        // LDS row pitch of 64-wide tiles (floats)
+constexpr int kWmPadK = 36;       // LDS row pitch of 32-wide tiles
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ k_sk, int hq,
+                      int hkv, int k, const int32_t* __restrict__ cu_blocks, int n_seqs,
+                      int total_blocks, int n_row_tiles, int s, const float* R_prev,
+                      float* R_out, float inv_sqrt_k) {
+  __shared__ __attribute__((aligned(16))) float Xs[kWmRows][kWmPad];     // X tile, then Y tile
+  __shared__ __attribute__((aligned(16))) float Ms[kWmRows][kWmPad];     // M_J^T [j][m]
+  __shared__ __attribute__((aligned(16))) float Qs[kWmRows][kWmPadK];    // Q_J [m][c]
+  __shared__ __attribute__((aligned(16))) float QTs[kWmK][kWmPad];       // Q_J^T [c][m]
+  __shared__ __attribute__((aligned(16))) float Ks[kWmRows][kWmPadK];    // K_J [j][c]
+  __shared__ __attribute__((aligned(16))) float Cs[2][kWmRows][kWmPadK]; // carry partials
+  __shared__ float rmax[kWmRows], rsc[kWmRows];
+
+  // Workgroup id -> (sequence, head, row tile).  Tile I costs I + 1 column
+  // tiles per hop, so the ids are laid out for the usual dispatch order (the
+  // first half of the grid takes one slot per CU, the second half the other):
+  // the first half holds the long tiles, longest first, and id + N / 2 gets
+  // the complementary short tile, so each CU's two workgroups sum to about the
+  // same work and the longest tiles do not share a CU with each other.
+  const int P = hq * n_seqs;
+  const int pid = (int)blockIdx.x % P;
+  const int slot = (int)blockIdx.x / P;
+  const int half = (n_row_tiles + 1) / 2;
+  const int I = slot < half ? n_row_tiles - 1 - slot : slot - half;
+  const int seq = pid / hq;
+  const int h = pid % hq;
+  const int b0 = cu_blocks[seq];
+  const int b = cu_blocks[seq + 1] - b0;
+  const int i0 = I * kWmRows;
+  if (i0 >= b) return;
+  const int64_t roff = walk_seq_offset(cu_blocks, seq, hq) + (int64_t)h * b * b;
+  float* Rh = R_out + roff;
+  const float* Rp = R_prev ? R_prev + roff : nullptr;
+  const int grp = hq / hkv;
+  const float* qs = q_sk + ((int64_t)h * total_blocks + b0) * k;
+  const float* ks = k_sk + ((int64_t)(h / grp) * total_blocks + b0) * k;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wi = w >> 1, wj = w & 1;
+  const int lc = lane & 31, lh = lane >> 5;
+  // staging: thread t loads row t / 4 of a tile, columns 16 (t % 4) .. (X) or
+  // 8 (t % 4) .. (sketches)
+  const int sr = tid >> 2, sp = tid & 3;
+
+  float4 xv[4], qv[2], kv[2];
+  // Tiles strictly below the diagonal tile, with all 64 rows inside the
+  // sequence and 16-byte aligned rows, take plain 16-byte loads and stores;
+  // the others (the diagonal tile, a sequence's last rows, odd b) go through
+  // clamped, always valid addresses with the out-of-range values replaced.
+  const bool plain_rows = i0 + kWmRows <= b && (b & 3) == 0;
+  auto fetch = [&](int hop, int jt) {
+    const int ig = i0 + sr;
+    const int jg0 = jt * kWmRows + sp * 16;
+    const float* src = hop == 0 ? Rp : Rh;
+    if (!src) {                                   // the identity (uniform)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = (ig < b && jg0 + 4 * e + x == ig) ? 1.f : 0.f;
+        xv[e] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else if (plain_rows && jt < I) {           // uniform
+      const float4* p4 = reinterpret_cast<const float4*>(src + (int64_t)ig * b + jg0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[e] = p4[e];
+    } else {
+      const float* row = src + (int64_t)min(ig, b - 1) * b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int jg = jg0 + 4 * e + x;
+          const float t = row[min(jg, b - 1)];
+          v[x] = (ig < b && jg <= ig) ? t : 0.f;
+        }
+        xv[e] = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
+    // sketch rows (k = 32): rows past the sequence read its last row and
+    // are zeroed
+    const int mg = jt * kWmRows + sr;
+    const int64_t mrow = (int64_t)min(mg, b - 1) * kWmK + sp * 8;
+    const float4* pq = reinterpret_cast<const float4*>(qs + mrow);
+    const float4* pk = reinterpret_cast<const float4*>(ks + mrow);
+    qv[0] = pq[0]; qv[1] = pq[1];
+    kv[0] = pk[0]; kv[1] = pk[1];
+    if (mg >= b) qv[0] = qv[1] = kv[0] = kv[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto stash = [&]() {
+    const float sc = rsc[sr];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float4 v = xv[e];
+      v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+      *reinterpret_cast<float4*>(&Xs[sr][sp * 16 + 4 * e]) = v;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      *reinterpret_cast<float4*>(&Qs[sr][sp * 8 + 4 * e]) = qv[e];
+      *reinterpret_cast<float4*>(&Ks[sr][sp * 8 + 4 * e]) = kv[e];
+      QTs[sp * 8 + 4 * e + 0][sr] = qv[e].x;
+      QTs[sp * 8 + 4 * e + 1][sr] = qv[e].y;
+      QTs[sp * 8 + 4 * e + 2][sr] = qv[e].z;
+      QTs[sp * 8 + 4 * e + 3][sr] = qv[e].w;
+    }
+  };
+
+  if (tid < kWmRows) {
+    rmax[tid] = 0.f;
+    rsc[tid] = 1.f;
   }
+  const int ntiles = I + 1;                 // column tiles I, I - 1, ..., 0
+  const int nsteps = s * ntiles;
+  fetch(0, I);
+  for (int st = 0; st < nsteps; ++st) {
+    const int hop = st / ntiles;
+    const int jt = I - st % ntiles;
+    if (st % ntiles == 0) {
+      // a new hop: this hop's row scales from the last one's maxima (a power
+      // of two, so the scaling is exact), and an empty carry
+      __syncthreads();
+      if (tid < kWmRows) {
+        const float m = rmax[tid];
+        rsc[tid] = (hop == 0 || !(m > 0.f))
+                       ? 1.f
+                       : __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(m), 126));
+        rmax[tid] = 0.f;
+      }
+      for (int e = tid; e < 2 * kWmRows * kWmPadK; e += 256) (&Cs[0][0][0])[e] = 0.f;
+      __syncthreads();
+    }
+    stash();
+    // The next step's tiles are fetched right after this barrier.  On a hop's
+    // last tile that fetch reads the next hop's top tile, written back by
+    // other threads a whole hop earlier: a full barrier (one per hop) makes
+    // those stores visible; the other tiles of the next hop are fetched after
+    // the full barriers that open it.  With a single tile the fetch waits for
+    // the write-back below instead.
+    const bool last = st + 1 == nsteps;
+    const bool late = ntiles == 1;
+    if (st % ntiles == ntiles - 1) __syncthreads();
+    else lds_barrier();
+    if (!last && !late) fetch((st + 1) / ntiles, I - (st + 1) % ntiles);
+    // ---- M_J^T quadrant (rows j of 32 wj.., columns m of 32 wi..) ----
+    floatx16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kWmK / 2; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[32 * wj + lc][16 * lh + t],
+                                                 Qs[32 * wi + lc][16 * lh + t], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * wj + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int m = 32 * wi + lc;
+      Ms[j][m] = j <= m ? acc[r] : 0.f;
+    }
+    lds_barrier();
+    // ---- Y quadrant (rows 32 wi.., columns 32 wj..) and the carry part ----
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll 8
+    for (int t = 0; t < kWmRows / 2; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[32 * wi + lc][32 * lh + t],
+                                                 Ms[32 * wj + lc][32 * lh + t], acc, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kWmK / 2; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(
+          Cs[0][32 * wi + lc][16 * lh + t] + Cs[1][32 * wi + lc][16 * lh + t],
+          Ks[32 * wj + lc][16 * lh + t], acc, 0, 0, 0);
+    floatx16_t cp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cp[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kWmRows / 4; ++t)
+      cp = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[32 * wi + lc][32 * wj + 16 * lh + t],
+                                                QTs[lc][32 * wj + 16 * lh + t], cp, 0, 0, 0);
+    lds_barrier();
+    // carry partial wj of rows 32 wi.. (this wave's own block), Y into Xs
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * wi + 8 * (r >> 2) + 4 * lh + (r & 3);
+      Cs[wj][i][lc] += cp[r];
+      const int j = 32 * wj + lc;
+      const bool ok = i0 + i < b && jt * kWmRows + j <= i0 + i;
+      Xs[i][j] = ok ? acc[r] * inv_sqrt_k : 0.f;
+    }
+    lds_barrier();
+    // ---- write the tile back, row maxima ----
+    {
+      const int ig = i0 + sr;
+      const int jg0 = jt * kWmRows + sp * 16;
+      float mx = 0.f;
+      float4 v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = *reinterpret_cast<const float4*>(&Xs[sr][sp * 16 + 4 * e]);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)),
+                             fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
+      }
+      float* dst = Rh + (int64_t)ig * b + jg0;
+      if (plain_rows && jt < I) {                 // uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float4*>(dst)[e] = v[e];
+      } else if (ig < b) {
+        // diagonal tile or last rows: only entries on or below the diagonal
+        // (so never past the row's end)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jg = jg0 + 4 * e;
+          if (jg <= ig) dst[4 * e] = v[e].x;
+          if (jg + 1 <= ig) dst[4 * e + 1] = v[e].y;
+          if (jg + 2 <= ig) dst[4 * e + 2] = v[e].z;
+          if (jg + 3 <= ig) dst[4 * e + 3] = v[e].w;
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      if (sp == 0) rmax[sr] = fmaxf(rmax[sr], mx);
+    }
+    if (!last && late) {
+      __syncthreads();
+      fetch((st + 1) / ntiles, I - (st + 1) % ntiles);
+    }
+    if (last) __syncthreads();        // the final pass reads other threads' stores
+    else lds_barrier();
+  }
+  // final pass: divide by the row maximum, zero the upper triangle
+  finalize_rows<256>(Rh, rmax, i0, kWmRows, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -594,6 +889,14 @@ hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, in
                        const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks,
                        int s, const float* R_prev, float* R_out, hipStream_t st) {
   if (total_blocks == 0 || max_blocks == 0) return hipSuccess;
+  if (k == kWmK) {
+    const int n_row_tiles = (max_blocks + kWmRows - 1) / kWmRows;
+    dim3 grid(n_row_tiles * hq * n_seqs);
+    hipLaunchKernelGGL(walk_mfma_kernel, grid, dim3(256), 0, st, q_sk, k_sk, hq, hkv, k,
+                       cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
+                       1.0f / sqrtf((float)k));
+    return hipGetLastError();
+  }
   if (k <= 16)
     return run_walk<16>(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks, s,
                         R_prev, R_out, st);
