@@ -495,6 +495,90 @@ def test_decode_head_major_layouts(d, B, hq, hkv, lens, share):
                                    grp, TOL_ATTN_BF16)
 
 
+def test_decode_paged_continuous_batching():
+    """Continuous batching over one page pool: between two calls a sequence
+    leaves (its pages go back to the pool), a new one joins on pages taken
+    from the pool (some of them the leaver's, overwritten), the others grow
+    by one token (the second crossing into a fresh page), and the batch
+    slots are reordered; only the block table and ctx_len change.  Every
+    pool page no sequence maps holds NaN.  Both calls equal the contiguous
+    kernel on the gathered caches bit for bit, and the oracle."""
+    cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=8, hkv=2)
+    B, d, hq, hkv = cfg.B, cfg.d, cfg.hq, cfg.hkv
+    grp = hq // hkv
+    num_pages = 40
+    rng = np.random.default_rng(gen.seed_for(15, d, B, hq))
+    free = list(rng.permutation(num_pages))
+    kp = torch.full((num_pages, B, hkv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    seqs = {}                                   # name -> dict(K, V, q, pages)
+
+    def add_tokens(name, n_new, layer):
+        st = seqs[name]
+        n0 = st["K"].shape[0] if st["K"] is not None else 0
+        k = gen.seq_tensor(cfg, layer, st["sid"], "k", n0 + n_new, "cuda")
+        v = gen.seq_tensor(cfg, layer, st["sid"], "v", n0 + n_new, "cuda")
+        st["K"], st["V"] = k, v
+        st["q"] = gen.seq_tensor(cfg, layer, st["sid"], "q", n0 + n_new, "cuda")[-1]
+        for j in range(-(-(n0 + n_new) // B)):
+            if j >= len(st["pages"]):
+                st["pages"].append(int(free.pop(0)))
+            pg = st["pages"][j]
+            rows = slice(j * B, min((j + 1) * B, n0 + n_new))
+            kp[pg, :rows.stop - rows.start] = k[rows]
+            vp[pg, :rows.stop - rows.start] = v[rows]
+
+    def run(order, layer_seed):
+        lens = [seqs[n]["K"].shape[0] for n in order]
+        width = max(len(seqs[n]["pages"]) for n in order) + 2
+        table = np.full((len(order), width), -1, dtype=np.int32)
+        for s, n in enumerate(order):
+            table[s, :len(seqs[n]["pages"])] = seqs[n]["pages"]
+        tab = torch.from_numpy(table).cuda()
+        ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        q = torch.stack([seqs[n]["q"] for n in order]).contiguous()
+        cur = (ctx - 1) // B
+        b_max = width
+        gr = torch.Generator(device="cuda")
+        gr.manual_seed(layer_seed)
+        r = torch.rand((len(order), hq, b_max), generator=gr, device="cuda")
+        uidx, ucnt, umask, idx, cnt = sws.select_topk_row(r, hq, hkv, cur, b_max, 25,
+                                                          per_head=True)
+        lse_p = torch.empty((len(order), hq), dtype=torch.float32, device="cuda")
+        out_p = sws.sparse_attn_decode_paged(q, kp, vp, tab, ctx, uidx, ucnt, umask, lse=lse_p)
+        kc = torch.zeros((len(order), max(lens), hkv, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        for s, n in enumerate(order):
+            kc[s, :lens[s]] = seqs[n]["K"]
+            vc[s, :lens[s]] = seqs[n]["V"]
+        lse_c = torch.empty_like(lse_p)
+        out_c = sws.sparse_attn_decode(q, kc, vc, ctx, B, uidx, ucnt, umask, lse=lse_c)
+        torch.cuda.synchronize()
+        assert torch.equal(out_p, out_c) and torch.equal(lse_p, lse_c)
+        Kh = [O.gather_pages(f64(kp), table[s], n, B) for s, n in enumerate(lens)]
+        Vh = [O.gather_pages(f64(vp), table[s], n, B) for s, n in enumerate(lens)]
+        ih, ch = idx.cpu().numpy(), cnt.cpu().numpy()
+        _check_decode_rows(f64(out_p), f64(lse_p), f64(q), Kh, Vh, lens,
+                           lambda s, h: ih[s, h, :ch[s, h]], B, d, grp, TOL_ATTN_BF16)
+
+    _print("continuous batching")
+    for sid, (name, n) in enumerate((("A", 300), ("B", 500), ("C", 2 * B))):
+        seqs[name] = {"sid": sid, "K": None, "V": None, "q": None, "pages": []}
+        add_tokens(name, n, 0)
+    run(["A", "B", "C"], 101)
+    # A leaves: its pages return to the pool (and are poisoned until reused)
+    for pg in seqs.pop("A")["pages"]:
+        kp[pg] = float("nan")
+        vp[pg] = float("nan")
+        free.insert(0, pg)
+    seqs["D"] = {"sid": 3, "K": None, "V": None, "q": None, "pages": []}
+    add_tokens("D", 200, 0)                     # takes the leaver's pages first
+    add_tokens("B", 1, 0)
+    add_tokens("C", 1, 0)                       # crosses into a new page
+    assert len(seqs["C"]["pages"]) == 3
+    run(["C", "D", "B"], 102)
+
+
 @pytest.mark.parametrize("dtype,d,B,kd,hq,hkv", [
     (torch.bfloat16, 128, 64, 32, 12, 3),
     (torch.float32, 64, 128, 16, 4, 4),
