@@ -84,6 +84,20 @@ __device__ __forceinline__ void finalize_rows(float* Rh, const float* m, int i0,
   }
 }
 
+// Workgroup id -> (pair p = sequence * hq + head, row tile I) for the
+// prefill walk kernels.  Row tile I costs I + 1 column tiles per hop, so the
+// ids are laid out for the usual dispatch order (the first half of the grid
+// takes one slot per CU, the second half the next): the first half holds the
+// long tiles, longest first, and id + N / 2 gets the complementary short
+// tile, so the workgroups sharing a CU add up to about the same work and the
+// longest tiles do not share a CU with each other.
+__device__ __forceinline__ void walk_tile_of(int id, int P, int n_row_tiles, int& p, int& I) {
+  p = id % P;
+  const int slot = id / P;
+  const int half = (n_row_tiles + 1) / 2;
+  I = slot < half ? n_row_tiles - 1 - slot : slot - half;
+}
+
 constexpr int kWalkThreads = 256;
 constexpr int kTileJ = 64;
 
@@ -99,7 +113,7 @@ template <int KP>
 __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void walk_kernel(
     const float* __restrict__ q_sk, const float* __restrict__ k_sk, int hq, int hkv, int k,
-    const int32_t* __restrict__ cu_blocks, int n_seqs, int total_blocks, int s,
+    const int32_t* __restrict__ cu_blocks, int n_seqs, int total_blocks, int n_row_tiles, int s,
     const float* R_prev, float* R_out, float inv_sqrt_k) {
   using WT = WalkTile<KP>;
   constexpr int LPR = WT::LPR, ROWS = WT::ROWS, XPT = WT::XPT, SPT = WT::SPT;
@@ -108,11 +122,13 @@ void walk_kernel(
   __shared__ float sx[2][ROWS][kTileJ + 1];
   __shared__ float smax[ROWS];
 
-  const int seq = blockIdx.z;
-  const int h = blockIdx.y;
+  int pid, tile;
+  walk_tile_of((int)blockIdx.x, hq * n_seqs, n_row_tiles, pid, tile);
+  const int seq = pid / hq;
+  const int h = pid % hq;
   const int b0 = cu_blocks[seq];
   const int b = cu_blocks[seq + 1] - b0;
-  const int i0 = blockIdx.x * ROWS;
+  const int i0 = tile * ROWS;
   if (i0 >= b) return;
   const int64_t roff = walk_seq_offset(cu_blocks, seq, hq) + (int64_t)h * b * b;
   float* Rh = R_out + roff;
@@ -254,7 +270,7 @@ void walk_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// prefill on the matrix cores (fp32 MFMA, k <= 32)
+// prefill on the matrix cores (fp32 MFMA, k <= 32 and a multiple of 4)
 // ---------------------------------------------------------------------------
 // The same walk, one workgroup per 64-row tile I of one head, its s hops
 // streaming the 64-column tiles J from the diagonal tile down.  Within a
@@ -286,6 +302,7 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kWmPad = 68;        // LDS row pitch of 64-wide tiles (floats)
 constexpr int kWmPadK = 36;       // LDS row pitch of 32-wide tiles
 
+template <bool K32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ k_sk, int hq,
                       int hkv, int k, const int32_t* __restrict__ cu_blocks, int n_seqs,
@@ -299,17 +316,8 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) float Cs[2][kWmRows][kWmPadK]; // carry partials
   __shared__ float rmax[kWmRows], rsc[kWmRows];
 
-  // Workgroup id -> (sequence, head, row tile).  Tile I costs I + 1 column
-  // tiles per hop, so the ids are laid out for the usual dispatch order (the
-  // first half of the grid takes one slot per CU, the second half the other):
-  // the first half holds the long tiles, longest first, and id + N / 2 gets
-  // the complementary short tile, so each CU's two workgroups sum to about the
-  // same work and the longest tiles do not share a CU with each other.
-  const int P = hq * n_seqs;
-  const int pid = (int)blockIdx.x % P;
-  const int slot = (int)blockIdx.x / P;
-  const int half = (n_row_tiles + 1) / 2;
-  const int I = slot < half ? n_row_tiles - 1 - slot : slot - half;
+  int pid, I;
+  walk_tile_of((int)blockIdx.x, hq * n_seqs, n_row_tiles, pid, I);
   const int seq = pid / hq;
   const int h = pid % hq;
   const int b0 = cu_blocks[seq];
@@ -368,15 +376,30 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
         xv[e] = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
-    // sketch rows (k = 32): rows past the sequence read its last row and
-    // are zeroed
+    // sketch rows: rows past the sequence (and, for k < 32, components
+    // past k) are zero, read from clamped addresses and then replaced
     const int mg = jt * kWmRows + sr;
-    const int64_t mrow = (int64_t)min(mg, b - 1) * kWmK + sp * 8;
-    const float4* pq = reinterpret_cast<const float4*>(qs + mrow);
-    const float4* pk = reinterpret_cast<const float4*>(ks + mrow);
-    qv[0] = pq[0]; qv[1] = pq[1];
-    kv[0] = pk[0]; kv[1] = pk[1];
-    if (mg >= b) qv[0] = qv[1] = kv[0] = kv[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (K32) {
+      const int64_t mrow = (int64_t)min(mg, b - 1) * kWmK + sp * 8;
+      const float4* pq = reinterpret_cast<const float4*>(qs + mrow);
+      const float4* pk = reinterpret_cast<const float4*>(ks + mrow);
+      qv[0] = pq[0]; qv[1] = pq[1];
+      kv[0] = pk[0]; kv[1] = pk[1];
+      if (mg >= b) qv[0] = qv[1] = kv[0] = kv[1] = z;
+    } else {
+      const int64_t mrow = (int64_t)min(mg, b - 1) * k;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c0 = sp * 8 + 4 * e;
+        const int64_t off = mrow + min(c0, k - 4);
+        const float4 a = *reinterpret_cast<const float4*>(qs + off);
+        const float4 c = *reinterpret_cast<const float4*>(ks + off);
+        const bool ok = mg < b && c0 < k;
+        qv[e] = ok ? a : z;
+        kv[e] = ok ? c : z;
+      }
+    }
   };
   auto stash = [&]() {
     const float sc = rsc[sr];
@@ -859,9 +882,11 @@ hipError_t run_walk(const float* q_sk, const float* k_sk, int hq, int hkv, int k
                     const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks, int s,
                     const float* R_prev, float* R_out, hipStream_t st) {
   constexpr int ROWS = kWalkThreads / (KP / 8);
-  dim3 grid((max_blocks + ROWS - 1) / ROWS, hq, n_seqs);
+  const int n_row_tiles = (max_blocks + ROWS - 1) / ROWS;
+  dim3 grid(n_row_tiles * hq * n_seqs);
   hipLaunchKernelGGL((walk_kernel<KP>), grid, dim3(kWalkThreads), 0, st, q_sk, k_sk, hq, hkv, k,
-                     cu_blocks, n_seqs, total_blocks, s, R_prev, R_out, 1.0f / sqrtf((float)k));
+                     cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
+                     1.0f / sqrtf((float)k));
   return hipGetLastError();
 }
 
@@ -889,12 +914,17 @@ hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, in
                        const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks,
                        int s, const float* R_prev, float* R_out, hipStream_t st) {
   if (total_blocks == 0 || max_blocks == 0) return hipSuccess;
-  if (k == kWmK) {
+  if (k <= kWmK && (k & 3) == 0) {
     const int n_row_tiles = (max_blocks + kWmRows - 1) / kWmRows;
     dim3 grid(n_row_tiles * hq * n_seqs);
-    hipLaunchKernelGGL(walk_mfma_kernel, grid, dim3(256), 0, st, q_sk, k_sk, hq, hkv, k,
-                       cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
-                       1.0f / sqrtf((float)k));
+    if (k == kWmK)
+      hipLaunchKernelGGL(walk_mfma_kernel<true>, grid, dim3(256), 0, st, q_sk, k_sk, hq, hkv, k,
+                         cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
+                         1.0f / sqrtf((float)k));
+    else
+      hipLaunchKernelGGL(walk_mfma_kernel<false>, grid, dim3(256), 0, st, q_sk, k_sk, hq, hkv,
+                         k, cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
+                         1.0f / sqrtf((float)k));
     return hipGetLastError();
   }
   if (k <= 16)
