@@ -452,7 +452,7 @@ template <> struct KvFrag<uint16_t> {
 };
 template <> struct KvFrag<uint8_t> {
   uint2 r;
-  __device__ __forceinline__ void load(const uint8_t* p) { r = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void set(uint32_t lo, uint32_t hi) { r = make_uint2(lo, hi); }
   // one instruction per two codes (fp8 -> bf16 directly, scale 1: exact)
   __device__ __forceinline__ bf16x8_t bf() const {
     const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, false);
@@ -488,20 +488,27 @@ __device__ __forceinline__ void mfma_range(
   const float sl2 = scale_log2 * kscale;
   __bf16* vt = vt_all + wave * D * kVtStride;
   const int64_t seq_off = table ? 0 : (int64_t)seq * L.seq;
-  const TK* kb = kc + seq_off + (int64_t)g * L.head + grp * 8;
-  const TK* vb = vc + seq_off + (int64_t)g * L.head + grp * 8;
+  const TK* kb = kc + seq_off + (int64_t)g * L.head;
+  const TK* vb = vc + seq_off + (int64_t)g * L.head;
   const int32_t* trow = table ? table + (int64_t)seq * table_width : nullptr;
   const int32_t* ul = uidx ? uidx + (int64_t)p * uwidth : nullptr;
   const uint32_t* um = umask ? umask + (int64_t)p * uwidth : nullptr;
+  // The features lane group grp feeds to the MFMA of 32-feature chunk c (any
+  // assignment works if K and Q use the same): bf16 rows take 8 contiguous
+  // features per chunk (16 bytes); fp8 rows take 16 contiguous bytes for the
+  // chunk pair (2m, 2m + 1), so one 16-byte load serves two chunks and a
+  // step needs half the load instructions.
+  constexpr bool F8 = sizeof(TK) == 1;
+  auto feat = [&](int c) { return F8 ? (c >> 1) * 64 + grp * 16 + (c & 1) * 8 : c * 32 + grp * 8; };
 
   // the group's queries as B operand columns (heads past G are zero)
   bf16x8_t qf[DC];
   {
     const bool hv = col < G;
-    const uint16_t* qp = q + ((int64_t)seq * hq + g * G + min(col, G - 1)) * D + grp * 8;
+    const uint16_t* qp = q + ((int64_t)seq * hq + g * G + min(col, G - 1)) * D;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qp + c * 32);
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + feat(c));
       qf[c] = __builtin_bit_cast(bf16x8_t, hv ? raw : make_uint4(0u, 0u, 0u, 0u));
     }
   }
@@ -533,10 +540,22 @@ __device__ __forceinline__ void mfma_range(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int64_t row = pbase + (int64_t)min(key0 + kt * 16 + col, ctx - 1) * L.row;
+      if constexpr (F8) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        kf[kt][c].load(kb + row + c * 32);
-        vf[kt][c].load(vb + row + c * 32);
+        for (int c = 0; c < DC; c += 2) {
+          const uint4 ku = *reinterpret_cast<const uint4*>(kb + row + feat(c));
+          const uint4 vu = *reinterpret_cast<const uint4*>(vb + row + feat(c));
+          kf[kt][c].set(ku.x, ku.y);
+          kf[kt][c + 1].set(ku.z, ku.w);
+          vf[kt][c].set(vu.x, vu.y);
+          vf[kt][c + 1].set(vu.z, vu.w);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          kf[kt][c].load(kb + row + feat(c));
+          vf[kt][c].load(vb + row + feat(c));
+        }
       }
     }
   };
@@ -573,7 +592,7 @@ __device__ __forceinline__ void mfma_range(
       for (int c = 0; c < DC; ++c) {
         const bf16x8_t v = vf[kt][c].bf();
 #pragma unroll
-        for (int x = 0; x < 8; ++x) vt[(c * 32 + grp * 8 + x) * kVtStride + slot[kt]] = v[x];
+        for (int x = 0; x < 8; ++x) vt[(feat(c) + x) * kVtStride + slot[kt]] = v[x];
       }
     // mask (keys past the context, heads that did not keep the block), the
     // step's max per head
