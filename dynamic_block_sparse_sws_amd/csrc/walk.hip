@@ -9,12 +9,14 @@
 // all b rows costs s b^2 k per head instead of forming M^s.
 //
 // Prefill: a workgroup owns a chunk of rows of one head and runs all s hops
-// on them, streaming the rows through LDS tile by tile from the last column
-// down (the scan order), overwriting each tile in place in R_out.  Lanes of a
-// row split the k components of S and combine their partial dot products with
-// cross-lane shuffles.  Every hop rescales its rows by their largest
-// magnitude (positive row scaling commutes with the right-multiplication, so
-// only the final division is visible), which keeps s * layers hops in fp32.
+// on them, streaming the rows tile by tile from the last column down (the
+// scan order), overwriting each tile in place in R_out.  For k <= 32 (a
+// multiple of 4) the scan within a tile runs as fp32 matrix-core products
+// (walk_mfma_kernel); otherwise lanes of a row split the k components of S
+// and combine their partial dot products with cross-lane shuffles
+// (walk_kernel).  Every hop rescales its rows by their largest magnitude
+// (positive row scaling commutes with the right-multiplication, so only the
+// final division is visible), which keeps s * layers hops in fp32.
 //
 // Decode: one workgroup per (sequence, query head) walks the single row of
 // the open block; the j range is cut into segments, one per thread of a
