@@ -299,6 +299,9 @@ hipError_t launch_select(const float* R, int hq, int hkv, const int32_t* cu_bloc
   else if (max_blocks <= 1024)
     hipLaunchKernelGGL((select_kernel<16>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
                        total_blocks, rho, flags, GS, width, idx, cnt);
+  else if (max_blocks <= 2048)
+    hipLaunchKernelGGL((select_kernel<32>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
+                       total_blocks, rho, flags, GS, width, idx, cnt);
   else
     hipLaunchKernelGGL((select_kernel<64>), grid, dim3(256), 0, st, R, hq, cu_blocks, n_seqs,
                        total_blocks, rho, flags, GS, width, idx, cnt);
