@@ -345,47 +345,44 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         pcc = torch.empty_like(pcc_all[0])
 
         snap2 = [{k_: st_[k_].clone() for k_ in ("qsk", "ksk", "rq", "rk")} for st_ in state]
-        # second set of list buffers: with two streams the lists of layer l + 1
-        # are built while the attention of layer l still reads those of layer l
-        ubufs2 = (ubufs, tuple(None if x is None else torch.empty_like(x) for x in ubufs))
-        dbufs2 = (dbufs, tuple(None if x is None else torch.empty_like(x) for x in dbufs))
 
-        def chain(l, st, par):
+        def chain(l, st, sl):
             dense = l < cfg.n_dense
-            sws.sketch_append_qk(q_buf[l], k_buf[l], pcc[0], B, kd, signs_d, cols_d,
-                                 st["rq"], st["rk"], st["qsk"], st["ksk"])
-            sws.walk_update_row(st["qsk"], st["ksk"], pcc[1], cfg.s, None if l == 0 else r, r)
-            return sws.select_topk_row(r, hq, hkv, pcc[1], b_max, cfg.rho, dense=dense,
-                                       out=(dbufs2 if dense else ubufs2)[par])
+            bufs = dbufs if dense else ubufs
+            sws.sketch_append_qk(q_buf[l][sl], k_buf[l][sl], pcc[0][sl], B, kd, signs_d, cols_d,
+                                 st["rq"][sl], st["rk"][sl], st["qsk"][sl], st["ksk"][sl])
+            sws.walk_update_row(st["qsk"][sl], st["ksk"][sl], pcc[1][sl], cfg.s,
+                                None if l == 0 else r[sl], r[sl])
+            return sws.select_topk_row(r[sl], hq, hkv, pcc[1][sl], b_max, cfg.rho, dense=dense,
+                                       out=tuple(None if x is None else x[sl] for x in bufs))
 
-        def attend(l, st, u):
-            sws.sparse_attn_decode(q_buf[l], st["kc"], st["vc"], pcc[2], B, u[0], u[1], u[2],
-                                   out=st["out"], ws=ws, head_major=head_major)
+        def attend(l, st, u, sl, ws_):
+            sws.sparse_attn_decode(q_buf[l][sl], st["kc"][sl], st["vc"][sl], pcc[2][sl], B, u[0],
+                                   u[1], u[2], out=st["out"][sl], ws=ws_, head_major=head_major)
+
+        whole = slice(0, ns)
 
         def graph_step():
             for l, st in enumerate(state):
-                attend(l, st, chain(l, st, 0))
+                attend(l, st, chain(l, st, whole), whole, ws)
 
+        # Two micro-batches, the two halves of the batch, on two streams: each
+        # half runs every layer in order (its select chain, then its
+        # attention), exactly the dependencies of a model whose layer l + 1
+        # reads layer l's output; the halves are independent, so one half's
+        # select chain (vector ALU and latency bound) can run beside the other
+        # half's attention (HBM bound).  Each half has its own workspace.
         side = torch.cuda.Stream()
+        halves = (slice(0, ns // 2), slice(ns // 2, ns))
+        ws_half = (ws, torch.empty_like(ws))
 
         def graph_step_2s():
-            # the select chain (append, walk row, select) runs on a side
-            # stream, one layer ahead of the attention on the main stream:
-            # chain(l + 1) may overlap attend(l); chain(l + 2) reuses the
-            # list buffers of layer l only after attend(l)
             main = torch.cuda.current_stream()
             side.wait_stream(main)
-            done_chain = [torch.cuda.Event() for _ in state]
-            done_attn = [torch.cuda.Event() for _ in state]
-            for l, st in enumerate(state):
-                with torch.cuda.stream(side):
-                    if l >= 2:
-                        side.wait_event(done_attn[l - 2])
-                    u = chain(l, st, l % 2)
-                    done_chain[l].record(side)
-                main.wait_event(done_chain[l])
-                attend(l, st, u)
-                done_attn[l].record(main)
+            for sl, strm, ws_ in zip(halves, (main, side), ws_half):
+                with torch.cuda.stream(strm):
+                    for l, st in enumerate(state):
+                        attend(l, st, chain(l, st, sl), sl, ws_)
             main.wait_stream(side)
 
         def stage(t):
@@ -419,8 +416,8 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         res["us_per_step_graph_1stream"] = time_graph(graph_step)
         res["us_per_step"] = res["us_per_step_graph_2streams"] = time_graph(graph_step_2s)
         res["graph"] = ("one HIP graph per step (all layers), inputs staged by 3 copies; "
-                        "us_per_step: the select chain on a side stream one layer ahead "
-                        "of the attention")
+                        "us_per_step: the batch as two micro-batches of 8 sequences on two "
+                        "streams, each running the layers in order")
         del snap2
     if not args.no_serving:
         res["serving_layouts"] = serving_layouts(torch, sws, gen, state[-1], ubufs, ctx_len[-1],

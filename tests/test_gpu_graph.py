@@ -14,9 +14,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("two_streams", [False, True])
 def test_decode_step_graph_replays_equal_eager(two_streams):
-    """two_streams: each layer's select chain is captured on a side stream,
-    one layer ahead of the attention on the capturing stream (list buffers
-    alternate between layers)."""
+    """two_streams: the batch as two micro-batches (one sequence each) on two
+    streams, each running every layer in order; each has its own decode
+    workspace."""
     cfg = gen.CONFIGS["C4"].with_(d=128, B=64, hq=8, hkv=2, k=32)
     B, d, kd, hq, hkv = cfg.B, cfg.d, cfg.k, cfg.hq, cfg.hkv
     prefixes, steps, rho = (190, 250), 8, 30
@@ -73,41 +73,43 @@ def test_decode_step_graph_replays_equal_eager(two_streams):
     r = torch.empty((ns, hq, b_max), device="cuda")
     lse = [torch.empty((ns, hq), device="cuda") for _ in layers]
 
-    def chain(l, q_of, k_of, pos, cur):
-        st = layers[l]["st"]
-        sws.sketch_append_qk(q_of(l), k_of(l), pos, B, kd, sd, cd, st["rq"], st["rk"],
-                             st["qsk"], st["ksk"])
-        sws.walk_update_row(st["qsk"], st["ksk"], cur, cfg.s, None if l == 0 else r, r)
-        return sws.select_topk_row(r, hq, hkv, cur, b_max, rho, dense=l == 0,
-                                   out=bufs[l % 2]["d" if l == 0 else "u"])
+    ws2 = torch.empty_like(ws)
 
-    def attend(l, q_of, ctx, u):
+    def chain(l, q_of, k_of, pos, cur, sl):
+        st = layers[l]["st"]
+        out = tuple(None if x is None else x[sl] for x in bufs[l % 2]["d" if l == 0 else "u"])
+        sws.sketch_append_qk(q_of(l)[sl], k_of(l)[sl], pos[sl], B, kd, sd, cd, st["rq"][sl],
+                             st["rk"][sl], st["qsk"][sl], st["ksk"][sl])
+        sws.walk_update_row(st["qsk"][sl], st["ksk"][sl], cur[sl], cfg.s,
+                            None if l == 0 else r[sl], r[sl])
+        return sws.select_topk_row(r[sl], hq, hkv, cur[sl], b_max, rho, dense=l == 0, out=out)
+
+    def attend(l, q_of, ctx, u, sl, ws_):
         L = layers[l]
-        sws.sparse_attn_decode(q_of(l), L["kc"], L["vc"], ctx, B, u[0], u[1], u[2],
-                               out=L["out"], lse=lse[l], ws=ws, head_major=L["hm"])
+        sws.sparse_attn_decode(q_of(l)[sl], L["kc"][sl], L["vc"][sl], ctx[sl], B, u[0], u[1],
+                               u[2], out=L["out"][sl], lse=lse[l][sl], ws=ws_,
+                               head_major=L["hm"])
+
+    whole = slice(0, ns)
 
     def step(q_of, k_of, pos, cur, ctx):
         for l in range(n_layers):
-            attend(l, q_of, ctx, chain(l, q_of, k_of, pos, cur))
+            attend(l, q_of, ctx, chain(l, q_of, k_of, pos, cur, whole), whole, ws)
 
     side = torch.cuda.Stream()
 
-    def step_2s(q_of, k_of, pos, cur, ctx):
+    def step_2s(q_of, k_of, pos, cur, ctx, eager=False):
+        # (the eager reference runs the same micro-batch calls on one stream:
+        # a micro-batch's split-KV ranges differ from the whole batch's, so
+        # its rounding does too)
         main = torch.cuda.current_stream()
-        side.wait_stream(main)
-        done_attn = []
-        for l in range(n_layers):
-            with torch.cuda.stream(side):
-                if l >= 2:                   # layer l - 2's lists are read until then
-                    side.wait_event(done_attn[l - 2])
-                u = chain(l, q_of, k_of, pos, cur)
-                ev = torch.cuda.Event()
-                ev.record(side)
-            main.wait_event(ev)
-            attend(l, q_of, ctx, u)
-            done_attn.append(torch.cuda.Event())
-            done_attn[-1].record(main)
-        main.wait_stream(side)
+        other = main if eager else side
+        other.wait_stream(main)
+        for sl, strm, ws_ in zip((slice(0, 1), slice(1, 2)), (main, other), (ws, ws2)):
+            with torch.cuda.stream(strm):
+                for l in range(n_layers):
+                    attend(l, q_of, ctx, chain(l, q_of, k_of, pos, cur, sl), sl, ws_)
+        main.wait_stream(other)
 
     def outputs():
         out = []
@@ -122,7 +124,12 @@ def test_decode_step_graph_replays_equal_eager(two_streams):
     eager = []
     for t in range(steps):
         pos = P_t + t
-        step(lambda l: layers[l]["qn"][t], lambda l: layers[l]["kn"][t], pos, pos // B, pos + 1)
+        if two_streams:
+            step_2s(lambda l: layers[l]["qn"][t], lambda l: layers[l]["kn"][t], pos, pos // B,
+                    pos + 1, eager=True)
+        else:
+            step(lambda l: layers[l]["qn"][t], lambda l: layers[l]["kn"][t], pos, pos // B,
+                 pos + 1)
         eager.append(outputs())
     torch.cuda.synchronize()
 
