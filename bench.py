@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-layers", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--microbatches", type=int, default=2,
+                    help="decode graph: the batch as this many micro-batches on as many streams")
     ap.add_argument("--kv-layout", choices=("head", "token"), default="head",
                     help="decode KV cache layout: [seq][kv head][ctx][d] (head) or "
                          "[seq][ctx][kv head][d] (token)")
@@ -372,18 +374,21 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         # reads layer l's output; the halves are independent, so one half's
         # select chain (vector ALU and latency bound) can run beside the other
         # half's attention (HBM bound).  Each half has its own workspace.
-        side = torch.cuda.Stream()
-        halves = (slice(0, ns // 2), slice(ns // 2, ns))
-        ws_half = (ws, torch.empty_like(ws))
+        nmb = max(1, min(args.microbatches, ns))
+        sides = [torch.cuda.Stream() for _ in range(nmb - 1)]
+        parts = [slice(ns * i // nmb, ns * (i + 1) // nmb) for i in range(nmb)]
+        ws_part = [ws] + [torch.empty_like(ws) for _ in range(nmb - 1)]
 
         def graph_step_2s():
             main = torch.cuda.current_stream()
-            side.wait_stream(main)
-            for sl, strm, ws_ in zip(halves, (main, side), ws_half):
+            for sd in sides:
+                sd.wait_stream(main)
+            for sl, strm, ws_ in zip(parts, [main] + sides, ws_part):
                 with torch.cuda.stream(strm):
                     for l, st in enumerate(state):
                         attend(l, st, chain(l, st, sl), sl, ws_)
-            main.wait_stream(side)
+            for sd in sides:
+                main.wait_stream(sd)
 
         def stage(t):
             q_buf.copy_(q_all[:, t])
@@ -414,10 +419,10 @@ def bench_decode(args, torch, sws, gen, timer_cls):
 
         res["us_per_step_eager"] = res["us_per_step"]
         res["us_per_step_graph_1stream"] = time_graph(graph_step)
-        res["us_per_step"] = res["us_per_step_graph_2streams"] = time_graph(graph_step_2s)
+        res["us_per_step"] = res["us_per_step_graph_microbatches"] = time_graph(graph_step_2s)
         res["graph"] = ("one HIP graph per step (all layers), inputs staged by 3 copies; "
-                        "us_per_step: the batch as two micro-batches of 8 sequences on two "
-                        "streams, each running the layers in order")
+                        f"us_per_step: the batch as {nmb} micro-batches on {nmb} streams, "
+                        "each running the layers in order")
         del snap2
     if not args.no_serving:
         res["serving_layouts"] = serving_layouts(torch, sws, gen, state[-1], ubufs, ctx_len[-1],
