@@ -2,7 +2,7 @@
 library's launches on static buffers) and replayed step after step, with
 eager work and synchronisations between the replays: every replay's outputs
 equal the eager calls' bit for bit (token-major and head-major caches; one
-stream, or the select chain on a side stream one layer ahead)."""
+stream, or the batch as two micro-batches on two streams)."""
 import pytest
 import torch
 
