@@ -11,9 +11,11 @@
 // step).  Each wave runs a FlashAttention-style
 // step on the matrix cores with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T          (A = K rows from LDS, B = this wave's Q in registers)
-//   online softmax       (a lane holds one query column; the reference max
-//                         is fixed after a query block's first step and only
-//                         raised if the running sum nears overflow)
+//   online softmax       (Q is pre-scaled by scale * log2(e), so scores are
+//                         in log2 units; a lane holds one query column; the
+//                         reference max is fixed after a query block's first
+//                         step, at 0 when that step's maximum is within +-64,
+//                         and only raised if the running sum nears overflow)
 //   O^T += V^T P^T       (A = V^T from LDS, B = P^T straight from the S^T
 //                         accumulators rounded to bf16; V^T's key order in LDS
 //                         is permuted to match the accumulator layout, so P
@@ -29,6 +31,8 @@
 // fp32 path: a plain kernel, one thread per query row, key-by-key online
 // softmax with K/V tiles staged in LDS; it exists for tight-tolerance checks.
 #include "sws_common.h"
+
+#include <type_traits>
 
 namespace sws {
 namespace {
@@ -128,7 +132,12 @@ __device__ __forceinline__ float max_halves(float v) {
 // maximum and a rescale of the output accumulators.  Numerator, denominator
 // and log-sum-exp all use the same reference, so the result is unchanged up to
 // rounding (fp32 and bf16 keep the same relative precision at any exponent).
+// When the first step's maximum lies within +-kZeroRefRange the reference is
+// exactly 0: the weights are then exp2(s) with no subtraction (a wave takes
+// that form when all its columns have reference 0), and 2^-64 .. 2^64 weights
+// plus sums below 2^100 stay far inside the fp32 and bf16 range.
 constexpr float kSumLimit = 0x1p100f;
+constexpr float kZeroRefRange = 64.f;
 
 // One pipeline step: KT keys of the current block against this wave's 32
 // query rows.  ksb / vsb are the step's K and V^T tiles in LDS.
@@ -138,7 +147,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
                                           const int (&k_rd)[D / 16],
                                           const int (&v_rd)[PrefillTile<D, BLK>::KT / 16],
                                           floatx16_t (&o)[D / 32], float& m_run, float& l_run,
-                                          float scale_log2, int qi, int hl) {
+                                          int qi, int hl) {
   constexpr int KT = PrefillTile<D, BLK>::KT;
   // ---- S^T = K Q^T ----
   floatx16_t st[KT / 32];
@@ -177,7 +186,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
   // (the first step of a query block takes the column maximum)
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8_t pb[KT / 16];
-  auto exp_step = [&](float& l_acc) {
+  auto exp_step = [&](float& l_acc, auto zero_ref) {
 #pragma unroll
     for (int kc = 0; kc < KT / 16; ++kc) {
       const int kt = kc >> 1;
@@ -185,18 +194,27 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         bf16x2_t pr;
-        pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e], scale_log2, -m_run));
-        pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[kt][r0 + e + 1], scale_log2, -m_run));
+        if constexpr (decltype(zero_ref)::value) {
+          pr[0] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e]);
+          pr[1] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e + 1]);
+        } else {
+          pr[0] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e] - m_run);
+          pr[1] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e + 1] - m_run);
+        }
         l_acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_acc, false);
         pb[kc][e] = pr[0];
         pb[kc][e + 1] = pr[1];
       }
     }
   };
+  auto exp_any = [&](float& l_acc) {
+    if (__all(m_run == 0.f)) exp_step(l_acc, std::true_type{});
+    else exp_step(l_acc, std::false_type{});
+  };
   float l_new = l_run;
   bool redo = m_run == -INFINITY;
   if (!redo) {
-    exp_step(l_new);
+    exp_any(l_new);
     redo = __any(!(l_new < kSumLimit));
   }
   if (redo) {
@@ -206,7 +224,11 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
     mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * scale_log2);
+    // a query block's first step takes the reference 0 when its maximum is
+    // within +-64 (no subtraction in the later steps' exponentials), else the
+    // maximum itself
+    const float m_new = m_run == -INFINITY ? (fabsf(mx) <= kZeroRefRange ? 0.f : mx)
+                                           : fmaxf(m_run, mx);
     const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
@@ -215,7 +237,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
       for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     m_run = m_new;
     l_new = l_run;
-    exp_step(l_new);
+    exp_any(l_new);
   }
   l_run = l_new;
   // ---- O^T += V^T P^T ----
@@ -283,7 +305,11 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     for (int dc = 0; dc < D / 16; ++dc) {
       u32x4_t raw = {0u, 0u, 0u, 0u};
       if (qrow < n) raw = *reinterpret_cast<const u32x4_t*>(qp + dc * 16);
+      // scaled once by scale * log2(e) (rounded to bf16), so the scores come
+      // out of the matrix cores in log2 units
       qf[dc] = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[dc][e] = (__bf16)((float)qf[dc][e] * scale_log2);
     }
   }
 
@@ -376,7 +402,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
       if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
       else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
       attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd, o,
-                        m_run, l_run, scale_log2, qi, hl);
+                        m_run, l_run, qi, hl);
       step_barrier();
     }
     j = j_next;
