@@ -346,7 +346,9 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     // non-negative (a sub-step of a partial block may start past the end)
     const uint16_t* ks = kbase + (int64_t)j * BLK * kstride;
     const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
-    const int last_off = (n - 1 - j * BLK) * (int)kstride;
+    // (the row distance is clamped to the block first: every offset below is
+    // under BLK rows anyway, and the product stays in 32 bits at any length)
+    const int last_off = min(n - 1 - j * BLK, BLK - 1) * (int)kstride;
     const int sub_off = sub * KT * (int)kstride;
 #pragma unroll
     for (int u = 0; u < TL::LOADS; ++u) {
