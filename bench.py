@@ -615,6 +615,7 @@ def diagnostics(args, torch, sws, gen, ctx):
     sweep = []
     for (kk, s, rho) in [(32, 1, 20), (32, 2, 20), (32, 4, 20), (32, 8, 20), (32, 16, 20),
                          (16, 8, 20), (64, 8, 20), (32, 8, 10), (32, 8, 30)]:
+        run(geo, kk, s, rho)                                # warm-up (first launches)
         idx, cnt, t = run(geo, kk, s, rho)
         rec = {"B": B, "k": kk, "s": s, "rho": rho, "stage_us": t,
                "executed_block_pairs": int(cnt.long().sum()),
@@ -633,6 +634,7 @@ def diagnostics(args, torch, sws, gen, ctx):
         print(f"[diag] walk variant {name}: walk {t['walk'] / 1e3:.2f} ms", file=sys.stderr,
               flush=True)
     geo64 = sws.Geometry([n], 64)
+    run(geo64, 32, 8, 20)                                   # warm-up (first launches)
     idx, cnt, t = run(geo64, 32, 8, 20)
     sweep.append({"B": 64, "k": 32, "s": 8, "rho": 20, "stage_us": t,
                   "executed_block_pairs": int(cnt.long().sum()),
