@@ -1,7 +1,8 @@
 """GPU edge cases: empty batches, the largest rows the decode kernels accept
 (4096 blocks, the streaming form of the row walk, group size 16), sketch
-dimensions that are not a power of two, and prefill selection over more than
-1024 blocks per sequence.  Everything is checked against the oracle."""
+dimensions that are not a power of two, prefill selection over more than
+1024 blocks per sequence, and prefill attention on a sequence whose K and V
+span more than 2^31 elements.  Everything is checked against the oracle."""
 import ctypes
 
 import numpy as np
@@ -11,7 +12,7 @@ import torch
 import dynamic_block_sparse_sws_amd as sws
 import gen
 import oracle as O
-from gpu_util import f64, rowwise_rel_err, TOL_WALK
+from gpu_util import f64, rowwise_rel_err, TOL_ATTN_BF16, TOL_WALK
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +142,53 @@ def test_prefill_select_more_than_1024_blocks():
                 gb = geo.cu_blocks_host[si] + i
                 want = (np.arange(i + 1) if i <= tau else O.select_row(Rm[i], i, tau)).tolist()
                 assert idx[h, gb, :cnt[h, gb]].tolist() == want, (si, h, i)
+
+
+def test_prefill_attention_offsets_past_2_31():
+    """Prefill attention on a sequence whose K and V span more than 2^31
+    elements (n * hkv * d > 2^31: 64 KV heads, d = 128, 262,545 tokens), with
+    every query block keeping block 0, the block farthest from the sequence's
+    end, plus blocks i // 2, i - 1 and itself: sampled query blocks (first,
+    middle, the partial last one) of the first and last head against the
+    oracle."""
+    d, B, hq, hkv = 128, 128, 64, 64
+    n = (1 << 31) // (hkv * d) + 3 * B + 17
+    geo = sws.Geometry([n], B)
+    b = geo.blocks[0]
+    _print("offsets past 2^31: n", n, "blocks", b)
+
+    def bf16_rand(heads, seed):
+        x = torch.empty((n, heads, d), dtype=torch.bfloat16, device="cuda")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(gen.seed_for(31, seed))
+        for t0 in range(0, n, 65536):
+            t1 = min(n, t0 + 65536)
+            x[t0:t1] = torch.randn((t1 - t0, heads, d), generator=g, device="cuda").bfloat16()
+        return x
+
+    q, k, v = bf16_rand(hq, 91), bf16_rand(hkv, 92), bf16_rand(hkv, 93)
+    lists = [sorted({0, i // 2, max(i - 1, 0), i}) for i in range(b)]
+    width = 4
+    idx_h = np.zeros((hq, b, width), dtype=np.int32)
+    cnt_h = np.zeros((hq, b), dtype=np.int32)
+    for i, lst in enumerate(lists):
+        idx_h[:, i, :len(lst)] = lst
+        cnt_h[:, i] = len(lst)
+    idx = torch.from_numpy(idx_h).cuda()
+    cnt = torch.from_numpy(cnt_h).cuda()
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    out = sws.sparse_attn_prefill(q, k, v, geo, idx, cnt, lse=lse)
+    torch.cuda.synchronize()
+    rows = [0, 1, b // 2, b - 1]
+    scale = 1.0 / np.sqrt(d)
+    for h in (0, hq - 1):
+        want = O.sparse_attention_rows(f64(q[:, h]), f64(k[:, h]), f64(v[:, h]), lists, B,
+                                       scale, rows)
+        for i in rows:
+            a, e = i * B, min((i + 1) * B, n)
+            o_w, lse_w = want[i]
+            err = float(np.abs(f64(out[a:e, h]) - o_w).max())
+            lerr = float(np.abs(f64(lse[h, a:e]) - lse_w).max())
+            assert err <= TOL_ATTN_BF16, (h, i, err)
+            assert lerr <= TOL_ATTN_BF16, (h, i, lerr)
+        _print("head", h, "ok")
