@@ -306,15 +306,17 @@ int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
  * renormalised over those keys; out = weights . V.
  *
  *   q [T][hq][d], k and v [T][hkv][d]; out [T][hq][d] (same dtype)
- *   dtype SWS_BF16: bf16 MFMA kernel (fp32 softmax / accumulation, output
- *   rounded to nearest even); SWS_F32: fp32 kernel
+ *   dtype SWS_BF16: bf16 MFMA kernel (q is multiplied by scale * log2(e)
+ *   and rounded to bf16 once, so the scores come out in log2 units; fp32
+ *   softmax and accumulation; output rounded to nearest even); SWS_F32:
+ *   fp32 kernel (no such rounding)
  *   idx, cnt as produced by sws_select_topk; idx == NULL means dense causal
  *   (every block <= i); cnt ignored then
  *   lse  optional [hq][T] fp32: natural-log sum of exp of the scaled scores
  *   ws   workspace of at least sws_prefill_workspace_size(...) bytes (the
  *        bf16 path stages V transposed per block there; may be NULL when the
  *        size is 0)
- *   d in {64, 128}; B in {64, 128}
+ *   d in {64, 128}; B in {64, 128}; q, k, v, out and ws 16-byte aligned
  */
 int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
                             const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
