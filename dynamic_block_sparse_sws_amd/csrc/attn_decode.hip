@@ -757,6 +757,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   const int ns = Bn > A ? wg_of_block(Bn - 1, W, nwg) + p + 1 - r0 : 0;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
+  // the first records' partial outputs are loaded now, beside the maxima, so
+  // the weighted sum below does not wait for a third round of loads
+  constexpr int kPre = 16;
+  float av[kPre];
+#pragma unroll
+  for (int si = 0; si < kPre; ++si)
+    av[si] = si < ns ? ws_acc[((int64_t)(r0 + si) * G + hh) * D + t] : 0.f;
   float m = -INFINITY;
   for (int si = t; si < ns; si += D) {
     const float v = ws_ml[((int64_t)(r0 + si) * G + hh) * 2];
@@ -793,8 +800,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   }
   __syncthreads();
   float acc = 0.f;
+#pragma unroll
+  for (int si = 0; si < kPre; ++si)
+    if (si < ns) acc += wgt[si] * av[si];
 #pragma unroll 8
-  for (int si = 0; si < ns; ++si) acc += wgt[si] * ws_acc[((int64_t)(r0 + si) * G + hh) * D + t];
+  for (int si = kPre; si < ns; ++si)
+    acc += wgt[si] * ws_acc[((int64_t)(r0 + si) * G + hh) * D + t];
   const float L = s_L;
   const float o = L > 0.f ? acc / L : 0.f;
   T* op = out + ((int64_t)seq * hq + h) * D + t;
