@@ -55,7 +55,7 @@ __all__ = [
     "rownorm", "walk_update", "walk_row", "n_select", "select_row", "select", "n_select_row",
     "select_rows_tau", "group_scores", "transition", "walk_update_variant",
     "walk_row_variant", "sparse_attention",
-    "sparse_attention_rows", "prefill_layer", "prefill", "decode_step", "SeqPrefill",
+    "sparse_attention_rows", "query_attention", "prefill_layer", "prefill", "decode_step", "SeqPrefill",
     "fp8_e4m3_value", "gather_pages",
 ]
 
@@ -220,12 +220,13 @@ def n_select(rho: int, b: int) -> int:
 def select_row(row: np.ndarray, i: int, tau: int) -> np.ndarray:
     """Blocks kept for query block i: the tau best earlier blocks m < i ordered
     by (row[m] descending, m ascending), plus block i itself; ascending."""
-    cand = list(range(i))
-    if len(cand) > tau:
-        vals = [float(row[m]) + 0.0 for m in cand]          # -0.0 -> +0.0
-        cand.sort(key=lambda m: (-vals[m], m))
-        cand = cand[:tau]
-    return np.array(sorted(cand) + [i], dtype=np.int64)
+    cand = np.arange(i, dtype=np.int64)
+    if i > tau:
+        vals = np.asarray(row[:i], np.float64) + 0.0        # -0.0 -> +0.0
+        # lexsort orders by its last key first: value descending, then index
+        order = np.lexsort((cand, -vals))
+        cand = np.sort(cand[order[:tau]])
+    return np.concatenate([cand, [i]]).astype(np.int64)
 
 
 def select(R: np.ndarray, rho: int, dense: bool = False):
@@ -345,6 +346,22 @@ def sparse_attention_rows(Q, K, V, lists, B: int, scale: float, rows: Sequence[i
     return out
 
 
+def query_attention(q, K, V, lst, B: int, p: int, scale: float):
+    """Attention of the single query token at position p (a decode step) over
+    the keys u <= p that lie in the blocks of `lst`: the softmax of
+    q . K[u] * scale renormalised over those keys, applied to V.  This is row p
+    of sparse_attention_rows for the block holding p, without the block's
+    other rows.  Returns (o [d], lse)."""
+    q = np.asarray(q, np.float64)
+    keys = np.concatenate([np.arange(j * B, min((j + 1) * B, p + 1)) for j in lst])
+    Kr = np.asarray(K[keys], np.float64)
+    Vr = np.asarray(V[keys], np.float64)
+    z = (Kr @ q) * scale
+    zmax = z.max()
+    w = np.exp(z - zmax)
+    return (w @ Vr) / w.sum(), float(zmax + math.log(w.sum()))
+
+
 def sparse_attention(Q, K, V, lists, B: int, scale: Optional[float] = None):
     """Full single-head attention output O [n, d] and log-sum-exp [n]."""
     Q = np.asarray(Q, np.float64)
@@ -444,13 +461,10 @@ def decode_step(layers_prefix, signs, cols, B: int, s: int, rho: int, n_dense: i
             b = c + 1
             lst = (np.arange(b, dtype=np.int64) if l < n_dense
                    else select_row(r[h], c, n_select(rho, b)))
-            keys = np.concatenate([np.arange(j * B, min((j + 1) * B, n)) for j in lst])
-            z = (K[keys, g, :] @ Q[p, h, :]) / math.sqrt(d)
-            zmax = z.max()
-            w = np.exp(z - zmax)
-            o = (w @ V[keys, g, :]) / w.sum()
+            o, lse = query_attention(Q[p, h, :], K[:, g, :], V[:, g, :], lst, B, p,
+                                     1.0 / math.sqrt(d))
             heads.append({"qs": qs, "ks": ks_all[g], "r": r[h].copy(), "lst": lst, "o": o,
-                          "lse": zmax + math.log(w.sum())})
+                          "lse": lse})
         out.append(heads)
     return out
 

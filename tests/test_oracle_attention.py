@@ -84,3 +84,30 @@ def test_single_block_list_is_plain_attention_over_that_block():
         z = np.where(np.tril(np.ones((B, B), bool)), z, -np.inf)
         p = np.exp(z - z.max(1, keepdims=True))
         np.testing.assert_allclose(o[sl], (p / p.sum(1, keepdims=True)) @ V[sl], atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_query_attention_equals_masked_sdpa_row(seed):
+    """One decode query at position p over the listed blocks (keys u <= p)
+    equals torch's masked SDPA on that row, output and log-sum-exp."""
+    rng = np.random.default_rng(300 + seed)
+    B = int(rng.choice([4, 8]))
+    n = int(rng.integers(2, 12 * B))
+    d = 8
+    Q, K, V = (rng.normal(size=(n, d)) for _ in range(3))
+    p = int(rng.integers(0, n))
+    c = p // B
+    earlier = rng.permutation(c)[:int(rng.integers(0, c + 1))]
+    lst = np.sort(np.concatenate([earlier, [c]])).astype(np.int64)
+    mask = np.zeros((1, n), bool)
+    for j in lst:
+        mask[0, j * B:(j + 1) * B] = True
+    mask[0, p + 1:] = False
+    o, lse = O.query_attention(Q[p], K, V, lst, B, p, 1 / math.sqrt(d))
+    o_ref, lse_ref = _sdpa_masked(Q[p:p + 1], K, V, mask, 1 / math.sqrt(d))
+    np.testing.assert_allclose(o, o_ref[0], rtol=1e-12, atol=1e-12)
+    assert abs(lse - lse_ref[0]) <= 1e-12
+    # and it is row p of the block-row form
+    rows = O.sparse_attention_rows(Q[:p + 1], K[:p + 1], V[:p + 1], {c: lst}, B,
+                                   1 / math.sqrt(d), [c])
+    np.testing.assert_allclose(o, rows[c][0][-1], rtol=1e-12, atol=1e-12)
