@@ -52,6 +52,15 @@ __device__ __forceinline__ int seq_of_block(const int32_t* cu_blocks, int n_seqs
   return s;
 }
 
+// Dynamic range of the walk state: after every hop, entries smaller in
+// magnitude than this fraction of their row's largest magnitude are zero.
+// Without a floor the walk over many layers keeps row entries hundreds of
+// binary orders of magnitude below the row maximum that grow back layers
+// later, so its value would depend on the number format's exponent range;
+// 2^-64 keeps every retained value, and its products with the scores, well
+// inside the normal fp32 range.
+constexpr float kWalkFloor = 0x1p-64f;
+
 // Offset (in elements) of sequence s in the packed walk-state layout.
 __device__ __forceinline__ int64_t walk_seq_offset(const int32_t* cu_blocks, int s, int hq) {
   int64_t off = 0;

@@ -51,7 +51,8 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
 
 // Final pass over a workgroup's rows i0 .. i0 + nrows - 1 (those inside the
 // sequence): each row divided by its largest magnitude m[r] (an all-zero row
-// stays zero), entries above the diagonal set to zero.  The rows are walked as
+// stays zero), entries below the walk floor and above the diagonal set to
+// zero.  The rows are walked as
 // one flat range, four accesses per thread at a time, all loads before any
 // store, so every thread keeps several loads in flight (row by row, each
 // thread's single load per row would expose the memory latency once per row).
@@ -80,7 +81,8 @@ __device__ __forceinline__ void finalize_rows(float* Rh, const float* m, int i0,
         if (j < 0) { --rr; j += b; }
         else if (j >= b) { ++rr; j -= b; }
         const float mm = m[rr];
-        base[e] = (j <= i0 + rr && mm > 0.f) ? v[u] / mm : 0.f;
+        const float x = v[u] / mm;
+        base[e] = (j <= i0 + rr && mm > 0.f && fabsf(x) >= kWalkFloor) ? x : 0.f;
       }
     }
   }
@@ -205,8 +207,8 @@ void walk_kernel(
   const int ntiles = top_tile / kTileJ + 1;
   const int nsteps = s * ntiles;
   float sc = 1.0f;   // rescale of this row's input for the current hop
+  float thr = 0.0f;  // the walk floor of this row's scaled input (0: none)
   float mx = 0.0f;   // largest |y| of this row in the current hop
-  float mx_prev = 0.0f;
   float S[8];
   int buf = 0;
   // With a single column tile the next hop re-reads the tile this step writes,
@@ -224,10 +226,12 @@ void walk_kernel(
       const int t = st % ntiles;
       const int jt = top_tile - t * kTileJ;
       if (t == 0) {
-        // a new hop: reset the scan, rescale by the previous hop's maximum
+        // a new hop: reset the scan, rescale by the previous hop's maximum (a
+        // power of two, so exactly) and cut its output to the walk floor
         if (st > 0) {
-          mx_prev = mx;
-          sc = (mx > 0.f) ? 1.0f / mx : 1.0f;
+          sc = mx > 0.f ? __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(mx), 126))
+                        : 1.0f;
+          thr = (mx * sc) * kWalkFloor;
         }
         mx = 0.0f;
 #pragma unroll
@@ -235,7 +239,8 @@ void walk_kernel(
       }
 #pragma unroll 4
       for (int jj = kTileJ - 1; jj >= 0; --jj) {
-        const float x = sx[buf][r][jj] * sc;
+        float x = sx[buf][r][jj] * sc;
+        x = fabsf(x) < thr ? 0.f : x;
         const float4 qa = *reinterpret_cast<const float4*>(&sq[buf][jj][part * 8]);
         const float4 qb = *reinterpret_cast<const float4*>(&sq[buf][jj][part * 8 + 4]);
         const float4 ka = *reinterpret_cast<const float4*>(&sk[buf][jj][part * 8]);
@@ -264,7 +269,6 @@ void walk_kernel(
     if (st + 1 < nsteps) stash(buf);
     __syncthreads();
   }
-  (void)mx_prev;
   if (part == 0) smax[r] = mx;
   __syncthreads();
   // final pass: divide by the row maximum, zero the upper triangle
@@ -316,7 +320,7 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) float QTs[kWmK][kWmPad];       // Q_J^T [c][m]
   __shared__ __attribute__((aligned(16))) float Ks[kWmRows][kWmPadK];    // K_J [j][c]
   __shared__ __attribute__((aligned(16))) float Cs[2][kWmRows][kWmPadK]; // carry partials
-  __shared__ float rmax[kWmRows], rsc[kWmRows];
+  __shared__ float rmax[kWmRows], rsc[kWmRows], rthr[kWmRows];
 
   int pid, I;
   walk_tile_of((int)blockIdx.x, hq * n_seqs, n_row_tiles, pid, I);
@@ -404,11 +408,13 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
     }
   };
   auto stash = [&]() {
-    const float sc = rsc[sr];
+    // the previous hop's output, scaled and cut to the walk floor
+    const float sc = rsc[sr], th = rthr[sr];
+    auto cut = [&](float x) { x *= sc; return fabsf(x) < th ? 0.f : x; };
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float4 v = xv[e];
-      v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+      v.x = cut(v.x); v.y = cut(v.y); v.z = cut(v.z); v.w = cut(v.w);
       *reinterpret_cast<float4*>(&Xs[sr][sp * 16 + 4 * e]) = v;
     }
 #pragma unroll
@@ -425,6 +431,7 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   if (tid < kWmRows) {
     rmax[tid] = 0.f;
     rsc[tid] = 1.f;
+    rthr[tid] = 0.f;
   }
   const int ntiles = I + 1;                 // column tiles I, I - 1, ..., 0
   const int nsteps = s * ntiles;
@@ -434,13 +441,17 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
     const int jt = I - st % ntiles;
     if (st % ntiles == 0) {
       // a new hop: this hop's row scales from the last one's maxima (a power
-      // of two, so the scaling is exact), and an empty carry
+      // of two, so the scaling is exact) and the walk floor relative to them,
+      // and an empty carry
       __syncthreads();
       if (tid < kWmRows) {
         const float m = rmax[tid];
-        rsc[tid] = (hop == 0 || !(m > 0.f))
-                       ? 1.f
-                       : __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(m), 126));
+        const bool rescale = hop > 0 && m > 0.f;
+        const float sc =
+            rescale ? __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(m), 126))
+                    : 1.f;
+        rsc[tid] = sc;
+        rthr[tid] = rescale ? (m * sc) * kWalkFloor : 0.f;
         rmax[tid] = 0.f;
       }
       for (int e = tid; e < 2 * kWmRows * kWmPadK; e += 256) (&Cs[0][0][0])[e] = 0.f;
@@ -557,12 +568,13 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
 // otherwise they are re-read from memory every hop.  The segment's x values
 // live in registers too.  A hop:
 //   A  x of the segment's rows from the previous hop's four partial products
-//      (LDS), T = sum over the segment of x q, and the largest |x|;
-//   B  a wave scan of T, the wave totals and maxima to LDS, barrier;
-//   C  S = exclusive scan (+ the totals of the quarter's earlier waves), all
-//      scaled by the power of two nearest below 1 / max (T is linear in x, so
-//      the scale of a hop is applied after the barrier), then the rows'
-//      partial products k . S to LDS, barrier.
+//      (LDS) and the row's largest |x| (wave maxima to LDS, barrier), then x
+//      scaled by the power of two nearest below 1 / max and cut to the walk
+//      floor (which needs the maximum before any sum over x);
+//   B  T = sum over the segment of x q, a wave scan of T, the wave totals to
+//      LDS, barrier;
+//   C  S = exclusive scan (+ the totals of the quarter's earlier waves), then
+//      the rows' partial products k . S to LDS, barrier.
 constexpr int kRowThreads = 1024;
 constexpr int kRowSeg = 256;        // segments (threads per component quarter)
 constexpr int kRowBmax = 4096;      // ypart capacity (largest row)
@@ -771,42 +783,55 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
     xr[l] = l < nv ? (rin ? rin[j] : (j == c ? 1.0f : 0.0f)) : 0.f;
   }
   for (int hop = 0; hop < s; ++hop) {
-    // ---- A: x of the segment's rows, T, local max ----
+    // ---- A: x of the segment's rows and the row's largest |x| ----
     if (hop > 0) {
       // REG: rows past the segment read LDS inside smem and are dropped (no
       // branch); the streaming form's 16 rows would hold too many registers
 #pragma unroll
       for (int l = 0; l < LR; ++l) {
-        if (REG) {
-          const float y = ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
-                          inv_sqrt_k;
-          xr[l] = l < nv ? y : 0.f;
-        } else {
-          xr[l] = l < nv ? ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
-                               inv_sqrt_k
-                         : 0.f;
-        }
+        const float y = ((yp[l] + yp[kRowBmax + l]) + (yp[2 * kRowBmax + l] + yp[3 * kRowBmax + l])) *
+                        inv_sqrt_k;
+        xr[l] = l < nv ? y : 0.f;
       }
     }
+    float lmax = 0.f;
+#pragma unroll
+    for (int l = 0; l < LR; ++l) lmax = fmaxf(lmax, fabsf(xr[l]));
+    lmax = wave_max_nonneg(lmax);
+    if (lane == 63) wmax[wave] = lmax;
+    __syncthreads();
+    float gmax = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
+    // the hop's scale, a power of two near 1 / gmax (exact; any positive scale
+    // leaves the row's direction unchanged), and the previous hop's output
+    // cut to the walk floor
+    {
+      const float sc =
+          gmax > 0.f ? __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(gmax), 126))
+                     : 1.0f;
+      const float thr = hop > 0 ? (gmax * sc) * kWalkFloor : 0.f;
+#pragma unroll
+      for (int l = 0; l < LR; ++l) {
+        const float x = xr[l] * sc;
+        xr[l] = fabsf(x) < thr ? 0.f : x;
+      }
+    }
+    // ---- B: T = sum over the segment of x q, its wave scan and totals ----
     float S[CQ];                                              // T, then its scan
 #pragma unroll
     for (int e = 0; e < CQ; ++e) S[e] = 0.f;
-    float lmax = 0.f;
 #pragma unroll
     for (int l = 0; l < LR; ++l) {
       if (REG || l < nv) {
 #pragma unroll
         for (int e = 0; e < CQ; ++e) S[e] += xr[l] * qget(l, e);
       }
-      lmax = fmaxf(lmax, fabsf(xr[l]));
     }
-    // ---- B: wave scan, totals and maxima ----
     wave_prefix_sum_n<CQ>(S);
-    lmax = wave_max_nonneg(lmax);
     if (lane == 63) {
 #pragma unroll
       for (int e = 0; e < CQ; ++e) wtot[wave][e] = S[e];
-      wmax[wave] = lmax;
     }
     // exclusive: the inclusive scan shifted up one lane (wave_shr:1, lane 0
     // gets 0), so T need not stay live through the scan
@@ -815,14 +840,6 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
       S[e] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                            0, __builtin_bit_cast(int, S[e]), 0x138, 0xF, 0xF, true));
     __syncthreads();
-    float gmax = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
-    // the hop's scale: a power of two near 1 / gmax (exact products; any
-    // positive scale leaves the row's direction, and so the result, unchanged)
-    const float sc =
-        gmax > 0.f ? __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(gmax), 126))
-                   : 1.0f;
     {
       // earlier waves of the quarter (uniform over the wave)
       const int wq = __builtin_amdgcn_readfirstlane(wave - p * WPQ);
@@ -833,8 +850,6 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
           for (int e = 0; e < CQ; ++e) S[e] += wtot[p * WPQ + w2][e];
         }
       }
-#pragma unroll
-      for (int e = 0; e < CQ; ++e) S[e] *= sc;
     }
     // ---- C: partial products k . S of the segment's rows, last row first ----
     // (REG: the test is l < L, the same for the whole workgroup; rows l in
@@ -844,7 +859,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
 #pragma unroll
     for (int l = LR - 1; l >= 0; --l) {
       if (REG ? l < L : l < nv) {
-        const float x = xr[l] * sc;
+        const float x = xr[l];
         float y = 0.f;
 #pragma unroll
         for (int e = 0; e < CQ; ++e) {
@@ -873,8 +888,12 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   for (int w2 = 0; w2 < NWAVE; ++w2) gmax = fmaxf(gmax, wmax[w2]);
   if (p == 0) {
 #pragma unroll
-    for (int l = 0; l < LR; ++l)
-      if (l < nv) rout[j0 + l] = gmax > 0.f ? xr[l] / gmax : 0.f;
+    for (int l = 0; l < LR; ++l) {
+      if (l < nv) {
+        const float x = xr[l] / gmax;
+        rout[j0 + l] = gmax > 0.f && fabsf(x) >= kWalkFloor ? x : 0.f;
+      }
+    }
   }
   for (int j = b + tid; j < b_max; j += kRowThreads) rout[j] = 0.f;
 }

@@ -177,6 +177,11 @@ int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const 
  * (section 3.2).  s hops per layer; each output row is divided by its largest
  * magnitude (an all-zero row stays zero).  Per sequence and query head:
  *   R_out = rownorm(R_prev * M^s)        (R_prev NULL: the identity)
+ * with a finite dynamic range: after every hop, entries smaller in magnitude
+ * than 2^-64 times their row's largest magnitude are set to zero (the page
+ * fixes no number format; without a floor the walk over many layers keeps
+ * entries hundreds of binary orders of magnitude below the row maximum that
+ * grow back layers later, so its value would depend on the format).
  *
  *   q_sk  [hq][total_blocks][k] fp32, k_sk [hkv][total_blocks][k] fp32
  *         (sws_sketch output with ld_head = total_blocks * k)
@@ -195,7 +200,7 @@ int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hk
 /*
  * sws_walk_update_row - decode form of sws_walk_update: only the row of the
  * open block c = cur_block[seq] (blog page, section 5).  Equals row c of
- * sws_walk_update over the first c + 1 blocks.
+ * sws_walk_update over the first c + 1 blocks (same hops, same floor).
  *
  *   q_sk_cache [n_seqs][hq][b_max][k], k_sk_cache [n_seqs][hkv][b_max][k] fp32,
  *              both 16-byte aligned

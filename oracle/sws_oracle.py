@@ -28,6 +28,12 @@ reason in the design notes of this repository):
 * R^(-1) = I; each row of R^l is divided by its largest magnitude after every
   layer (positive row scaling commutes with right-multiplication, so rankings
   are unchanged);
+* the walk state has a finite dynamic range: after every hop, entries smaller
+  in magnitude than WALK_FLOOR = 2^-64 times their row's largest magnitude are
+  set to zero.  Without it the walk over many layers is not computable in any
+  fixed floating-point format: row entries fall hundreds of binary orders of
+  magnitude below the row maximum and grow back to dominate the row several
+  layers later, so the result depends on the format's exponent range;
 * the Hadamard projection is H_d[r, c] = sign[r] * H_syl[r, cols[c]] / sqrt(k)
   with H_syl the natural-order Sylvester matrix; sign and cols are inputs;
 * a partial last block is averaged over the tokens it holds;
@@ -52,7 +58,7 @@ import numpy as np
 __all__ = [
     "n_blocks", "block_ranges", "block_sums", "block_means", "a_true", "a_true_bruteforce",
     "sylvester", "fwht", "hadamard_projection", "sketch_from_means", "sketch", "sketched_scores",
-    "rownorm", "walk_update", "walk_row", "n_select", "select_row", "select", "n_select_row",
+    "rownorm", "WALK_FLOOR", "floor_rows", "walk_update", "walk_row", "n_select", "select_row", "select", "n_select_row",
     "select_rows_tau", "group_scores", "transition", "walk_update_variant",
     "walk_row_variant", "sparse_attention",
     "sparse_attention_rows", "query_attention", "prefill_layer", "prefill", "decode_step", "SeqPrefill",
@@ -184,17 +190,32 @@ def rownorm(X: np.ndarray) -> np.ndarray:
     return np.where(m > 0, X / np.where(m > 0, m, 1.0), 0.0)
 
 
-def walk_update(R_prev: Optional[np.ndarray], M: np.ndarray, s: int) -> np.ndarray:
+WALK_FLOOR = 2.0 ** -64
+
+
+def floor_rows(X: np.ndarray, floor: float = WALK_FLOOR) -> np.ndarray:
+    """Entries smaller in magnitude than floor times their row's largest
+    magnitude set to zero (the walk state's dynamic range; floor = 0 keeps
+    every entry)."""
+    X = np.atleast_2d(np.asarray(X, np.float64))
+    m = np.abs(X).max(axis=1, keepdims=True)
+    return np.where(np.abs(X) < floor * m, 0.0, X)
+
+
+def walk_update(R_prev: Optional[np.ndarray], M: np.ndarray, s: int,
+                floor: float = WALK_FLOOR) -> np.ndarray:
     """R^l = rownorm(R^(l-1) M^s) with R^(-1) = I (section 4): s successive
-    right-multiplications by the layer's sketched score matrix."""
+    right-multiplications by the layer's sketched score matrix, each hop's
+    rows cut to the walk state's dynamic range (floor_rows)."""
     M = np.asarray(M, np.float64)
     X = np.eye(M.shape[0]) if R_prev is None else np.asarray(R_prev, np.float64).copy()
     for _ in range(s):
-        X = X @ M
+        X = floor_rows(X @ M, floor)
     return rownorm(X)
 
 
-def walk_row(r_prev: Optional[np.ndarray], M: np.ndarray, i: int, s: int) -> np.ndarray:
+def walk_row(r_prev: Optional[np.ndarray], M: np.ndarray, i: int, s: int,
+             floor: float = WALK_FLOOR) -> np.ndarray:
     """Row i of walk_update, computed as a row vector (decode): r <- r M, s times."""
     M = np.asarray(M, np.float64)
     if r_prev is None:
@@ -203,7 +224,7 @@ def walk_row(r_prev: Optional[np.ndarray], M: np.ndarray, i: int, s: int) -> np.
     else:
         x = np.asarray(r_prev, np.float64).copy()
     for _ in range(s):
-        x = x @ M
+        x = floor_rows(x @ M, floor)[0]
     m = np.abs(x).max()
     return x / m if m > 0 else x
 

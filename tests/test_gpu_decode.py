@@ -122,15 +122,12 @@ def run_decode_case(cfg, prefixes, steps, n_layers, rho, n_dense, check_steps, d
                     got = rec["idx"][s, h, :rec["cnt"][s, h]]
                     assert got.tolist() == lst.tolist(), (t, l, s, h, got, lst)
                     # attention of token p over the selected blocks
-                    keys = np.concatenate([np.arange(j * B, min((j + 1) * B, p + 1)) for j in lst])
-                    z = (H["k"][keys, g] @ H["q"][p, h]) / math.sqrt(d)
-                    zm = z.max()
-                    wgt = np.exp(z - zm)
-                    o_want = (wgt @ H["v"][keys, g]) / wgt.sum()
+                    o_want, lse_want = O.query_attention(H["q"][p, h], H["k"][:, g], H["v"][:, g],
+                                                         lst, B, p, 1.0 / math.sqrt(d))
                     e = float(np.abs(rec["out"][s, h] - o_want).max())
                     worst["attn"] = max(worst["attn"], e)
                     assert e <= tol_attn, (t, l, s, h, "attn", e)
-                    assert abs(rec["lse"][s, h] - (zm + math.log(wgt.sum()))) <= max(tol_attn, 1e-4)
+                    assert abs(rec["lse"][s, h] - lse_want) <= max(tol_attn, 1e-4)
                 # union list and masks of every group
                 for g in range(hkv):
                     want = {}
@@ -247,11 +244,9 @@ def test_decode_group_shared_selection():
             assert uidx[s, g, :n_u].tolist() == want
             assert (umask[s, g, :n_u].cpu().numpy().astype(np.uint32) == (1 << grp) - 1).all()
             H = {w: f64(full[s][w]) for w in "qkv"}
-            keys = np.concatenate([np.arange(j * B, min((j + 1) * B, P + 1)) for j in want])
             for h in range(g * grp, (g + 1) * grp):
-                z = (H["k"][keys, g] @ H["q"][P, h]) / math.sqrt(cfg.d)
-                wgt = np.exp(z - z.max())
-                o_want = (wgt @ H["v"][keys, g]) / wgt.sum()
+                o_want, _ = O.query_attention(H["q"][P, h], H["k"][:, g], H["v"][:, g],
+                                              np.array(want), B, P, 1.0 / math.sqrt(cfg.d))
                 assert np.abs(f64(out[s, h]) - o_want).max() <= TOL_ATTN_BF16, (s, h)
 
 
@@ -330,14 +325,12 @@ def _check_decode_rows(out, lse, qh, Kh, Vh, lens, lists, B, d, grp, tol):
     for s, n in enumerate(lens):
         for h in range(out.shape[1]):
             g = h // grp
-            keys = np.concatenate([np.arange(j * B, min((j + 1) * B, n)) for j in lists(s, h)])
-            z = (Kh[s][keys, g] @ qh[s, h]) / math.sqrt(d)
-            zm = z.max()
-            w = np.exp(z - zm)
-            o_want = (w @ Vh[s][keys, g]) / w.sum()
+            o_want, lse_want = O.query_attention(qh[s, h], Kh[s][:, g], Vh[s][:, g],
+                                                 np.asarray(lists(s, h)), B, n - 1,
+                                                 1.0 / math.sqrt(d))
             e = float(np.abs(out[s, h] - o_want).max())
             assert e <= tol, (s, h, e)
-            assert abs(lse[s, h] - (zm + math.log(w.sum()))) <= max(tol, 1e-4), (s, h)
+            assert abs(lse[s, h] - lse_want) <= max(tol, 1e-4), (s, h)
 
 
 @pytest.mark.parametrize("d,B,hq,hkv,lens,share", [

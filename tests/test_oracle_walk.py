@@ -169,3 +169,37 @@ def test_variant_walks_reduce_to_closed_forms():
         assert np.allclose(O.walk_row_variant(Rp[4], M, 4, s, mode), full[4])
         full0 = O.walk_update_variant(None, M, s, mode)
         assert np.allclose(O.walk_row_variant(None, M, 6, s, mode), full0[6])
+
+
+def test_floor_hand_case():
+    """Dynamic range of the walk state, worked by hand: the row (1, 1) walked
+    s = 8 hops with M = diag(1, 2^-10) becomes (1, 2^-10 h) after hop h, so
+    the second entry drops below 2^-64 of the row maximum at hop 7 and is zero
+    from then on; without the floor it is 2^-80."""
+    M = np.diag([1.0, 2.0 ** -10])
+    x = np.array([[1.0, 1.0]])
+    assert O.walk_update(x, M, 8).tolist() == [[1.0, 0.0]]
+    assert O.walk_update(x, M, 8, floor=0.0).tolist() == [[1.0, 2.0 ** -80]]
+    assert O.walk_update(x, M, 6).tolist() == [[1.0, 2.0 ** -60]]        # still inside
+    assert O.walk_row(x[0], M, 1, 8).tolist() == [1.0, 0.0]
+    # the comparison is strict: exactly 2^-64 of the maximum stays
+    assert O.floor_rows(np.array([[4.0, 2.0 ** -62, -2.0 ** -62 / 2]])).tolist() == \
+        [[4.0, 2.0 ** -62, 0.0]]
+    # an all-zero row stays zero; rows are cut independently
+    assert O.floor_rows(np.array([[0.0, 0.0], [1.0, 2.0 ** -70]])).tolist() == \
+        [[0.0, 0.0], [1.0, 0.0]]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_floor_leaves_well_scaled_walks_unchanged(seed):
+    """With entries inside 64 binary orders of magnitude of their row maximum
+    the floor changes nothing: the floored walk equals the plain one."""
+    rng = np.random.default_rng(50 + seed)
+    M = _lower(rng, 10, 2.0)
+    Rp = O.rownorm(np.tril(rng.uniform(0.5, 1.0, size=(10, 10))))
+    a = O.walk_update(Rp, M, 4)
+    b = O.walk_update(Rp, M, 4, floor=0.0)
+    assert np.abs(np.abs(Rp @ np.linalg.matrix_power(M, 4)) /
+                  np.abs(Rp @ np.linalg.matrix_power(M, 4)).max(1, keepdims=True))[
+        np.tril(np.ones((10, 10), bool))].min() > 2.0 ** -64
+    np.testing.assert_array_equal(a, b)
