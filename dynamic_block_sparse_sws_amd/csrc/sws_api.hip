@@ -11,7 +11,7 @@ namespace {
 
 thread_local std::string g_detail;
 
-int fail(int code, const char* fmt, ...) {
+sws_status fail(sws_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -21,12 +21,12 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+sws_status ok() {
   g_detail.clear();
   return SWS_OK;
 }
 
-int launched(hipError_t e, const char* what) {
+sws_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SWS_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
@@ -45,8 +45,8 @@ int tau_of(int rho, int b) { return (int)(((int64_t)rho * b) / 100); }
 extern "C" {
 
 int sws_version(void) { return 100; }
-
-const char* sws_status_string(int status) {
+                
+                const char* sws_status_string(sws_status status) {
   switch (status) {
     case SWS_OK: return "SWS_OK";
     case SWS_ERR_NULL: return "SWS_ERR_NULL";
@@ -59,11 +59,11 @@ const char* sws_status_string(int status) {
 }
 
 const char* sws_last_error_detail(void) { return g_detail.c_str(); }
-
-int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
-               int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
-               int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
-               int64_t ld_head, float* sum_out, void* stream) {
+                                  
+                                  sws_status sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                  int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
+                                  int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
+                                  int64_t ld_head, float* sum_out, void* stream) {
   const char* fn = "sws_sketch";
   REQUIRE_PTR(x);
   REQUIRE_PTR(cu_seqlens);
@@ -86,10 +86,10 @@ int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_
                   fn);
 }
 
-int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t n_seqs,
-                      int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
-                      const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
-                      void* stream) {
+sws_status sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t n_seqs,
+                             int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
+                             const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
+                             void* stream) {
   const char* fn = "sws_sketch_append";
   REQUIRE_PTR(x_new);
   REQUIRE_PTR(pos);
@@ -111,11 +111,11 @@ int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t 
                   fn);
 }
 
-int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const int32_t* pos,
-                         int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
-                         int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
-                         float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
-                         void* stream) {
+sws_status sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const int32_t* pos,
+                                int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
+                                float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
+                                void* stream) {
   const char* fn = "sws_sketch_append_qk";
   REQUIRE_PTR(q_new);
   REQUIRE_PTR(k_new);
@@ -142,10 +142,10 @@ int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const 
                   fn);
 }
 
-int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv, int32_t k,
-                    const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
-                    int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
-                    void* stream) {
+sws_status sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv, int32_t k,
+                           const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
+                           int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
+                           void* stream) {
   const char* fn = "sws_walk_update";
   REQUIRE_PTR(q_sk);
   REQUIRE_PTR(k_sk);
@@ -163,10 +163,10 @@ int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hk
                   fn);
 }
 
-int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
-                        int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
-                        int32_t b_max, int32_t s, const float* r_prev, float* r_out,
-                        void* stream) {
+sws_status sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                               int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
+                               int32_t b_max, int32_t s, const float* r_prev, float* r_out,
+                               void* stream) {
   const char* fn = "sws_walk_update_row";
   REQUIRE_PTR(q_sk_cache);
   REQUIRE_PTR(k_sk_cache);
@@ -185,11 +185,11 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
                   fn);
 }
 
-int sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv,
-                            int32_t k, const int32_t* cu_blocks, int32_t n_seqs,
-                            int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
-                            const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
-                            size_t ws_bytes, void* stream) {
+sws_status sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv,
+                                   int32_t k, const int32_t* cu_blocks, int32_t n_seqs,
+                                   int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
+                                   const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
+                                   size_t ws_bytes, void* stream) {
   const char* fn = "sws_walk_update_variant";
   if (mode == SWS_WALK_DEFAULT)
     return sws_walk_update(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks,
@@ -224,10 +224,10 @@ size_t sws_walk_variant_workspace_size(int64_t walk_numel) {
   return walk_numel > 0 ? sws::walk_variant_workspace_bytes(walk_numel) : 0;
 }
 
-int sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
-                                int32_t hkv, int32_t k, int32_t n_seqs,
-                                const int32_t* cur_block, int32_t b_max, int32_t s,
-                                int32_t mode, const float* r_prev, float* r_out, void* stream) {
+sws_status sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                                       int32_t hkv, int32_t k, int32_t n_seqs,
+                                       const int32_t* cur_block, int32_t b_max, int32_t s,
+                                       int32_t mode, const float* r_prev, float* r_out, void* stream) {
   const char* fn = "sws_walk_update_row_variant";
   if (mode == SWS_WALK_DEFAULT)
     return sws_walk_update_row(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs, cur_block, b_max, s,
@@ -250,10 +250,10 @@ int sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache
                   fn);
 }
 
-static int select_topk_impl(const char* fn, const float* R, int32_t hq, int32_t hkv,
-                            const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
-                            int32_t max_blocks, int32_t rho_percent, int32_t flags,
-                            int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
+static sws_status select_topk_impl(const char* fn, const float* R, int32_t hq, int32_t hkv,
+                                   const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
+                                   int32_t max_blocks, int32_t rho_percent, int32_t flags,
+                                   int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
   const bool dense = (flags & SWS_SELECT_DENSE) != 0;
   if (!dense) REQUIRE_PTR(R);
   REQUIRE_PTR(cu_blocks);
@@ -277,27 +277,27 @@ static int select_topk_impl(const char* fn, const float* R, int32_t hq, int32_t 
                   fn);
 }
 
-int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
-                    int32_t total_blocks, int32_t max_blocks, int32_t rho_percent, int32_t dense,
-                    int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
+sws_status sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
+                           int32_t total_blocks, int32_t max_blocks, int32_t rho_percent, int32_t dense,
+                           int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
   return select_topk_impl("sws_select_topk", R, hq, hq, cu_blocks, n_seqs, total_blocks,
                           max_blocks, rho_percent, dense ? SWS_SELECT_DENSE : 0, width, idx, cnt,
                           stream);
 }
 
-int sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t* cu_blocks,
-                          int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
-                          int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
-                          int32_t* cnt, void* stream) {
+sws_status sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t* cu_blocks,
+                                 int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
+                                 int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
+                                 int32_t* cnt, void* stream) {
   return select_topk_impl("sws_select_topk_flags", R, hq, hkv, cu_blocks, n_seqs, total_blocks,
                           max_blocks, rho_percent, flags, width, idx, cnt, stream);
 }
 
-int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
-                        const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
-                        int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
-                        int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
-                        int32_t union_width, void* stream) {
+sws_status sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
+                               const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
+                               int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
+                               int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
+                               int32_t union_width, void* stream) {
   const char* fn = "sws_select_topk_row";
   const bool dense = (flags & SWS_SELECT_DENSE) != 0;
   if (flags & ~(SWS_SELECT_DENSE | SWS_SELECT_ROW_TAU | SWS_SELECT_GROUP))
@@ -328,12 +328,12 @@ int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
                   fn);
 }
 
-int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
-                            const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
-                            int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
-                            int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
-                            int32_t width, float scale, void* out, float* lse, void* ws,
-                            size_t ws_bytes, void* stream) {
+sws_status sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
+                                   const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
+                                   int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
+                                   int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
+                                   int32_t width, float scale, void* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream) {
   const char* fn = "sws_sparse_attn_prefill";
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
@@ -380,12 +380,12 @@ size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_
   return sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, union_width);
 }
 
-int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
-                           const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
-                           int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
-                           const int32_t* union_cnt, const uint32_t* union_mask,
-                           int32_t union_width, float scale, void* out, float* lse, void* ws,
-                           size_t ws_bytes, void* stream) {
+sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                                  const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
+                                  int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
+                                  const int32_t* union_cnt, const uint32_t* union_mask,
+                                  int32_t union_width, float scale, void* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream) {
   const char* fn = "sws_sparse_attn_decode";
   REQUIRE_PTR(q);
   REQUIRE_PTR(k_cache);
@@ -424,14 +424,14 @@ int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
                   fn);
 }
 
-int sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
-                                 int kv_dtype, float k_scale, float v_scale,
-                                 const int32_t* block_table, int32_t table_width,
-                                 int32_t num_pages, const int32_t* ctx_len, int32_t n_seqs,
-                                 int32_t hq, int32_t hkv, int32_t d, int32_t B,
-                                 const int32_t* union_idx, const int32_t* union_cnt,
-                                 const uint32_t* union_mask, int32_t union_width, float scale,
-                                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+sws_status sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                        int kv_dtype, float k_scale, float v_scale,
+                                        const int32_t* block_table, int32_t table_width,
+                                        int32_t num_pages, const int32_t* ctx_len, int32_t n_seqs,
+                                        int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                        const int32_t* union_idx, const int32_t* union_cnt,
+                                        const uint32_t* union_mask, int32_t union_width, float scale,
+                                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "sws_sparse_attn_decode_paged";
   REQUIRE_PTR(q);
   REQUIRE_PTR(k_pages);

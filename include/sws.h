@@ -104,7 +104,7 @@ enum {
 int sws_version(void);
 
 /* Static string naming a status code. */
-const char* sws_status_string(int status);
+const char* sws_status_string(sws_status status);
 
 /* Message describing the most recent failed call on this thread ("" if none). */
 const char* sws_last_error_detail(void);
@@ -130,10 +130,10 @@ const char* sws_last_error_detail(void);
  *   sum_out     optional (NULL to skip) fp32 [n_heads][total_blocks][d]: the
  *               block sums (not divided by the token count)
  */
-int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
-               int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
-               int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
-               int64_t ld_head, float* sum_out, void* stream);
+sws_status sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                      int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
+                      int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
+                      int64_t ld_head, float* sum_out, void* stream);
 
 /*
  * sws_sketch_append - decode form of sws_sketch (blog page, section 5: the
@@ -149,10 +149,10 @@ int sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_
  *   sketch_cache [n_seqs][n_heads][b_max][k] fp32: row c is rewritten;
  *                the caller guarantees pos / B < b_max
  */
-int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t n_seqs,
-                      int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
-                      const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
-                      void* stream);
+sws_status sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t n_seqs,
+                             int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
+                             const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
+                             void* stream);
 
 /*
  * sws_sketch_append_qk - sws_sketch_append of a decode step's query and key
@@ -164,11 +164,11 @@ int sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, int32_t 
  *   run_sum_k [n_seqs][hkv][d]; q_cache [n_seqs][hq][b_max][k], k_cache
  *   [n_seqs][hkv][b_max][k]; hq + hkv <= 65535
  */
-int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const int32_t* pos,
-                         int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
-                         int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
-                         float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
-                         void* stream);
+sws_status sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const int32_t* pos,
+                                int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
+                                float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
+                                void* stream);
 
 /*
  * sws_walk_update - the walk state of one layer (blog page, section 4:
@@ -192,10 +192,10 @@ int sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype, const 
  *         the same buffer as R_out (in-place update).
  *   max_blocks  host: max_s b_s; s >= 1; 1 <= k <= 64
  */
-int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv, int32_t k,
-                    const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
-                    int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
-                    void* stream);
+sws_status sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv, int32_t k,
+                           const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
+                           int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
+                           void* stream);
 
 /*
  * sws_walk_update_row - decode form of sws_walk_update: only the row of the
@@ -208,10 +208,10 @@ int sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int32_t hk
  *   r_prev     NULL (the unit row e_c) or [n_seqs][hq][b_max]; may equal r_out
  *   r_out      [n_seqs][hq][b_max]; entries above cur_block are written 0
  */
-int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
-                        int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
-                        int32_t b_max, int32_t s, const float* r_prev, float* r_out,
-                        void* stream);
+sws_status sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                               int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
+                               int32_t b_max, int32_t s, const float* r_prev, float* r_out,
+                               void* stream);
 
 /*
  * sws_walk_update_variant - sws_walk_update with a walk mode (SWS_WALK_*).
@@ -227,11 +227,11 @@ int sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache, int32_
  *               (T and two products, packed like R)
  *   max_blocks <= 4096; R_prev may equal R_out
  */
-int sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv,
-                            int32_t k, const int32_t* cu_blocks, int32_t n_seqs,
-                            int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
-                            const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
-                            size_t ws_bytes, void* stream);
+sws_status sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t hq, int32_t hkv,
+                                   int32_t k, const int32_t* cu_blocks, int32_t n_seqs,
+                                   int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
+                                   const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* Workspace bytes of sws_walk_update_variant for walk_numel = hq * sum b_s^2. */
 size_t sws_walk_variant_workspace_size(int64_t walk_numel);
@@ -242,10 +242,10 @@ size_t sws_walk_variant_workspace_size(int64_t walk_numel);
  * from the sketch caches.  Arguments and layouts as sws_walk_update_row, plus
  * mode (SWS_WALK_*; SWS_WALK_DEFAULT runs sws_walk_update_row).
  */
-int sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
-                                int32_t hkv, int32_t k, int32_t n_seqs,
-                                const int32_t* cur_block, int32_t b_max, int32_t s,
-                                int32_t mode, const float* r_prev, float* r_out, void* stream);
+sws_status sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache, int32_t hq,
+                                       int32_t hkv, int32_t k, int32_t n_seqs,
+                                       const int32_t* cur_block, int32_t b_max, int32_t s,
+                                       int32_t mode, const float* r_prev, float* r_out, void* stream);
 
 /*
  * sws_select_topk - top-tau key blocks per query block (blog page, section
@@ -261,9 +261,9 @@ int sws_walk_update_row_variant(const float* q_sk_cache, const float* k_sk_cache
  *          >= max_blocks when dense
  *   max_blocks <= 4096
  */
-int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
-                     int32_t total_blocks, int32_t max_blocks, int32_t rho_percent,
-                     int32_t dense, int32_t width, int32_t* idx, int32_t* cnt, void* stream);
+sws_status sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
+                           int32_t total_blocks, int32_t max_blocks, int32_t rho_percent,
+                           int32_t dense, int32_t width, int32_t* idx, int32_t* cnt, void* stream);
 
 /*
  * sws_select_topk_flags - sws_select_topk with the selection variants of the
@@ -272,17 +272,21 @@ int sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_
  * SWS_SELECT_ROW_TAU the width bound is the same (the last row has the
  * largest budget).
  */
-int sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t* cu_blocks,
-                          int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
-                          int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
-                          int32_t* cnt, void* stream);
+sws_status sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t* cu_blocks,
+                                 int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
+                                 int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
+                                 int32_t* cnt, void* stream);
 
 /*
  * sws_select_topk_row - decode form of sws_select_topk for the open block
- * c = cur_block[seq] (b = c + 1 blocks, tau = floor(rho_percent * b / 100)),
- * followed by the union over the query heads of each KV group: the ascending
- * list of blocks that any head of the group keeps, with a bit mask of the
- * heads (bit g = head hkv_group * (hq/hkv) + g) that keep it.
+ * c = cur_block[seq] (b = c + 1 blocks, tau = floor(rho_percent * b / 100)):
+ * each decode step keeps the top-tau blocks of the same block-level walk
+ * score as prefill (blog page, section 5, decode; section 4, top-tau
+ * selection).  It is followed by the union over the query heads of each KV
+ * group: the ascending list of blocks that any head of the group keeps, with
+ * a bit mask of the heads (bit g = head hkv_group * (hq/hkv) + g) that keep
+ * it, so one pass over the cache serves the group (the page lists GQA among
+ * the integration costs, section 11.4).
  *
  *   r          [n_seqs][hq][b_max] fp32 (sws_walk_update_row output)
  *   idx, cnt   optional (both NULL or both set): per-head lists
@@ -297,11 +301,11 @@ int sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const int32_t
  *              with SWS_SELECT_GROUP the union is the group's shared list,
  *              kept by every head)
  */
-int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
-                         const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
-                         int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
-                         int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
-                         int32_t union_width, void* stream);
+sws_status sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
+                               const int32_t* cur_block, int32_t b_max, int32_t rho_percent,
+                               int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
+                               int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
+                               int32_t union_width, void* stream);
 
 /*
  * sws_sparse_attn_prefill - block-sparse attention over the selected blocks
@@ -323,12 +327,12 @@ int sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t n_seqs,
  *        size is 0)
  *   d in {64, 128}; B in {64, 128}; q, k, v, out and ws 16-byte aligned
  */
-int sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
-                            const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
-                            int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
-                            int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
-                            int32_t width, float scale, void* out, float* lse, void* ws,
-                            size_t ws_bytes, void* stream);
+sws_status sws_sparse_attn_prefill(const void* q, const void* k, const void* v, int dtype,
+                                   const int32_t* cu_seqlens, const int32_t* cu_blocks, int32_t n_seqs,
+                                   int32_t total_blocks, int32_t max_blocks, int32_t hq, int32_t hkv,
+                                   int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
+                                   int32_t width, float scale, void* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* Workspace bytes sws_sparse_attn_prefill needs (hkv * total_blocks * d * B * 2
  * for SWS_BF16, 0 for SWS_F32). */
@@ -356,12 +360,12 @@ size_t sws_prefill_workspace_size(int dtype, int32_t total_blocks, int32_t hkv, 
  *   evenly across the workgroups, so the cost follows the total number of
  *   blocks, not the largest list.
  */
-int sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
-                           const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
-                           int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
-                           const int32_t* union_cnt, const uint32_t* union_mask,
-                           int32_t union_width, float scale, void* out, float* lse, void* ws,
-                           size_t ws_bytes, void* stream);
+sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                                  const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
+                                  int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
+                                  const int32_t* union_cnt, const uint32_t* union_mask,
+                                  int32_t union_width, float scale, void* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* Workspace bytes sws_sparse_attn_decode needs for these sizes (a work plan
  * and per-range partial softmax states; union_width does not change it). */
@@ -395,14 +399,14 @@ size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_
  *                B, union_width) bytes
  *   Same size limits as sws_sparse_attn_decode; pages 16-byte aligned.
  */
-int sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
-                                 int kv_dtype, float k_scale, float v_scale,
-                                 const int32_t* block_table, int32_t table_width,
-                                 int32_t num_pages, const int32_t* ctx_len, int32_t n_seqs,
-                                 int32_t hq, int32_t hkv, int32_t d, int32_t B,
-                                 const int32_t* union_idx, const int32_t* union_cnt,
-                                 const uint32_t* union_mask, int32_t union_width, float scale,
-                                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+sws_status sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                        int kv_dtype, float k_scale, float v_scale,
+                                        const int32_t* block_table, int32_t table_width,
+                                        int32_t num_pages, const int32_t* ctx_len, int32_t n_seqs,
+                                        int32_t hq, int32_t hkv, int32_t d, int32_t B,
+                                        const int32_t* union_idx, const int32_t* union_cnt,
+                                        const uint32_t* union_mask, int32_t union_width, float scale,
+                                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }
