@@ -21,7 +21,7 @@ __all__ = [
     "sketch", "sketch_append", "sketch_append_qk", "walk_update", "walk_update_row", "walk_update_variant",
     "walk_variant_workspace_size", "select_topk",
     "select_topk_row", "sparse_attn_prefill", "sparse_attn_decode", "decode_workspace_size",
-    "sparse_attn_decode_paged",
+    "sparse_attn_decode_paged", "sparse_attn_decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES",
     "prefill_layer", "EXPORTED_SYMBOLS", "version",
 ]
 
@@ -47,8 +47,11 @@ EXPORTED_SYMBOLS = (
     "sws_select_topk_row", "sws_sparse_attn_prefill", "sws_sparse_attn_decode",
     "sws_decode_workspace_size", "sws_prefill_workspace_size", "sws_select_topk_flags",
     "sws_walk_update_variant", "sws_walk_variant_workspace_size", "sws_walk_update_row_variant",
-    "sws_sparse_attn_decode_paged",
+    "sws_sparse_attn_decode_paged", "sws_sparse_attn_decode_noalloc",
 )
+
+# include/sws.h SWS_DECODE_NOALLOC_SCRATCH_BYTES
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class SwsError(RuntimeError):
@@ -94,6 +97,8 @@ _SIGS = {
     "sws_sparse_attn_decode": ([_P, _P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                 _P, _I, _F, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "sws_decode_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "sws_sparse_attn_decode_noalloc": ([_P, _P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I, _P,
+                                        _P, _P, _I, _F, _P, _P, _P], ctypes.c_int),
     "sws_sparse_attn_decode_paged": ([_P, _P, _P, ctypes.c_int, _F, _F, _P, _I, _I, _P, _I, _I,
                                       _I, _I, _I, _P, _P, _P, _I, _F, _P, _P, _P, _SZ, _P],
                                      ctypes.c_int),
@@ -403,6 +408,28 @@ def sparse_attn_decode(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cn
         _ptr(ctx_len), n_seqs, max_ctx, hq,
         hkv, d, B, _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def sparse_attn_decode_noalloc(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cnt,
+                               union_mask, scale: Optional[float] = None, out=None, lse=None,
+                               stream=None, head_major: bool = False):
+    """sparse_attn_decode with the split-KV records in the library's fixed
+    device array (no workspace argument; the C call allocates nothing)."""
+    n_seqs, hq, d = q.shape
+    if head_major:
+        _, hkv, max_ctx, _ = k_cache.shape
+    else:
+        _, max_ctx, hkv, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    uw = union_idx.shape[2] if union_idx is not None else -(-max_ctx // B)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("sws_sparse_attn_decode_noalloc", lib().sws_sparse_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q) | (KV_HEAD_MAJOR if head_major else 0),
+        _ptr(ctx_len), n_seqs, max_ctx, hq, hkv, d, B, _ptr(union_idx), _ptr(union_cnt),
+        _ptr(union_mask), uw, float(scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 

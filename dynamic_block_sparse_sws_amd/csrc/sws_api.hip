@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "sws_common.h"
@@ -380,13 +381,51 @@ size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_
   return sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, union_width);
 }
 
-sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
-                                  const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
-                                  int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
-                                  const int32_t* union_cnt, const uint32_t* union_mask,
-                                  int32_t union_width, float scale, void* out, float* lse, void* ws,
-                                  size_t ws_bytes, void* stream) {
-  const char* fn = "sws_sparse_attn_decode";
+}  // extern "C"
+
+namespace {
+
+// Split-KV records of sws_sparse_attn_decode_noalloc: a fixed device array
+// (each GPU holds its own copy while the library is loaded), used instead of
+// a caller workspace by callers that cannot allocate device memory.  Host
+// code must not pass `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SWS_DECODE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices] = {};
+
+sws_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SWS_ERR_LAUNCH, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SWS_ERR_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SWS_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SWS_OK;
+}
+
+// Validation and launch shared by the two contiguous-cache decode calls; with
+// use_scratch the split-KV records go to the device array above.
+sws_status decode_contiguous(const char* fn, const void* q, const void* k_cache,
+                             const void* v_cache, int dtype, const int32_t* ctx_len,
+                             int32_t n_seqs, int32_t max_ctx, int32_t hq, int32_t hkv, int32_t d,
+                             int32_t B, const int32_t* union_idx, const int32_t* union_cnt,
+                             const uint32_t* union_mask, int32_t union_width, float scale,
+                             void* out, float* lse, void* ws, size_t ws_bytes, bool use_scratch,
+                             void* stream) {
   REQUIRE_PTR(q);
   REQUIRE_PTR(k_cache);
   REQUIRE_PTR(v_cache);
@@ -415,13 +454,49 @@ sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(SWS_ERR_SHAPE, "%s: q/k_cache/v_cache must be 16-byte aligned", fn);
   const size_t need = sws::decode_workspace_bytes(n_seqs, hq, hkv, d, B, uw);
-  if (!ws || ws_bytes < need)
+  if (use_scratch) {
+    if (need > (size_t)SWS_DECODE_NOALLOC_SCRATCH_BYTES)
+      return fail(SWS_ERR_WORKSPACE,
+                  "%s: the call needs %zu bytes of split-KV records, more than the fixed %zu",
+                  fn, need, (size_t)SWS_DECODE_NOALLOC_SCRATCH_BYTES);
+    if (n_seqs == 0) return ok();
+    const sws_status st = scratch_address(fn, &ws);
+    if (st != SWS_OK) return st;
+  } else if (!ws || ws_bytes < need) {
     return fail(SWS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+  }
   return launched(sws::launch_attn_decode(q, k_cache, v_cache, dtype, head_major, ctx_len, n_seqs,
                                           max_ctx, hq, hkv, d, B, union_idx, union_cnt,
                                           union_mask, uw, scale, out, lse, ws,
                                           (hipStream_t)stream),
                   fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                                  const int32_t* ctx_len, int32_t n_seqs, int32_t max_ctx, int32_t hq,
+                                  int32_t hkv, int32_t d, int32_t B, const int32_t* union_idx,
+                                  const int32_t* union_cnt, const uint32_t* union_mask,
+                                  int32_t union_width, float scale, void* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return decode_contiguous("sws_sparse_attn_decode", q, k_cache, v_cache, dtype, ctx_len, n_seqs,
+                           max_ctx, hq, hkv, d, B, union_idx, union_cnt, union_mask, union_width,
+                           scale, out, lse, ws, ws_bytes, false, stream);
+}
+
+sws_status sws_sparse_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          int dtype, const int32_t* ctx_len, int32_t n_seqs,
+                                          int32_t max_ctx, int32_t hq, int32_t hkv, int32_t d,
+                                          int32_t B, const int32_t* union_idx,
+                                          const int32_t* union_cnt, const uint32_t* union_mask,
+                                          int32_t union_width, float scale, void* out, float* lse,
+                                          void* stream) {
+  return decode_contiguous("sws_sparse_attn_decode_noalloc", q, k_cache, v_cache, dtype, ctx_len,
+                           n_seqs, max_ctx, hq, hkv, d, B, union_idx, union_cnt, union_mask,
+                           union_width, scale, out, lse, nullptr, 0, true, stream);
 }
 
 sws_status sws_sparse_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -367,6 +367,40 @@ sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void
                                   int32_t union_width, float scale, void* out, float* lse, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* Size of the fixed device array holding the split-KV records of
+ * sws_sparse_attn_decode_noalloc (one copy per GPU the library runs on). */
+#define SWS_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * sws_sparse_attn_decode_noalloc - sws_sparse_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid allocation): the same computation and result, bit for bit, with
+ * the split-KV records kept in a fixed device array of
+ * SWS_DECODE_NOALLOC_SCRATCH_BYTES instead of a workspace argument.
+ *
+ *   arguments as sws_sparse_attn_decode without ws / ws_bytes; the caller
+ *   still passes q, the caches, the lists and out (and lse).
+ *   The array of the current device (hipGetDevice) is used: `stream` must
+ *   belong to that device.  Its address is looked up once per device, on
+ *   the first call there.
+ *   Returns SWS_ERR_WORKSPACE when the call needs more than
+ *   SWS_DECODE_NOALLOC_SCRATCH_BYTES (sws_decode_workspace_size gives the
+ *   need: 4.5 MB for 16 sequences x 8 KV heads x 4 query heads per group,
+ *   d = 128).
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind; nothing in it needs to start at any value.  Calls that may run
+ *   at the same time on one GPU (on different streams, or from different
+ *   threads without ordering) race on the array and give wrong results:
+ *   order them on one stream.
+ */
+sws_status sws_sparse_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          int dtype, const int32_t* ctx_len, int32_t n_seqs,
+                                          int32_t max_ctx, int32_t hq, int32_t hkv, int32_t d,
+                                          int32_t B, const int32_t* union_idx,
+                                          const int32_t* union_cnt, const uint32_t* union_mask,
+                                          int32_t union_width, float scale, void* out, float* lse,
+                                          void* stream);
+
 /* Workspace bytes sws_sparse_attn_decode needs for these sizes (a work plan
  * and per-range partial softmax states; union_width does not change it). */
 size_t sws_decode_workspace_size(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t B,

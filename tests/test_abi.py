@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     L = sws.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -149,3 +149,26 @@ def test_other_entry_points_validation():
     assert L.sws_sketch_append_qk(P, P, 1, P, 2, 32, 8, 128, 64, 65, P, P, P, P, P, P, 9, N) == 3
     assert L.sws_sketch_append_qk(P, P, 1, P, 2, 32, 8, 128, 64, 32, P, P, P,
                                   ctypes.c_void_p(4100), P, P, 9, N) == 2
+
+
+@cpu_only
+def test_decode_noalloc_validation():
+    """The no-allocation decode call validates like the workspace form and
+    rejects calls whose split-KV records exceed its fixed device array, all
+    on the host (no device symbol is looked up for a rejected call)."""
+    L = sws.lib()
+    f = ctypes.c_float
+    # 8192 (sequence, KV head) pairs x 16 heads per group x (d + 2) floats > 32 MiB
+    assert L.sws_decode_workspace_size(1024, 128, 8, 128, 64, 821) > sws.DECODE_NOALLOC_SCRATCH_BYTES
+    assert L.sws_sparse_attn_decode_noalloc(P, P, P, 1, P, 1024, 65792, 128, 8, 128, 64, P, P, P,
+                                            821, f(0.1), P, N, N) == 4
+    assert L.sws_last_error_detail().startswith(b"sws_sparse_attn_decode_noalloc")
+    # the bench's decode shape fits
+    assert L.sws_decode_workspace_size(16, 32, 8, 128, 64, 821) <= sws.DECODE_NOALLOC_SCRATCH_BYTES
+    # argument errors as in the workspace form: q NULL, bad d, group too large
+    assert L.sws_sparse_attn_decode_noalloc(N, P, P, 1, P, 16, 65792, 32, 8, 128, 64, P, P, P, 821,
+                                            f(0.1), P, N, N) == 1
+    assert L.sws_sparse_attn_decode_noalloc(P, P, P, 1, P, 16, 65792, 32, 8, 96, 64, P, P, P, 821,
+                                            f(0.1), P, N, N) == 3
+    assert L.sws_sparse_attn_decode_noalloc(P, P, P, 1, P, 16, 65792, 64, 2, 128, 64, P, P, P, 821,
+                                            f(0.1), P, N, N) == 3
