@@ -6,8 +6,11 @@ d=128, B=128, k=32, s=8, 20% density): sketch Q, sketch K, walk update, top-tau
 selection, block-sparse attention, on inputs already resident in HBM.  The
 JSON line reports dense-equivalent TFLOP/s (4 d Hq n(n+1)/2 per layer divided
 by the layer time), ms per layer, the per-stage split, the roofline of the
-attention kernel, the 16 x 64K decode step (32 layers, first two dense), and
-the CPU oracle timed on a bounded sample of the same workload.
+attention kernel against its target, the density sweep (10/30/100%) with the
+speed-up over our own 100% run, the 16 x 64K decode step (32 layers, first
+two dense, all 256 steps) with the decode attention's HBM roofline, the 32K
+and ragged prefill workloads, the tiny stack's latency, and the CPU oracle
+timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -29,6 +32,10 @@ sys.path.insert(0, ROOT)
 METRIC = "128K prefill ms/layer + dense-equiv TFLOP/s at 20% density; decode µs/step"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# the two roofline targets: prefill attention at >= 50% of the bf16 matrix
+# peak on executed FLOPs, sparse decode attention at >= 70% of HBM bandwidth
+TARGET_PREFILL_MFMA_FRAC = 0.50
+TARGET_DECODE_HBM_FRAC = 0.70
 
 
 def parse():
@@ -52,7 +59,10 @@ def parse():
                     help="skip the decode steps replayed as HIP graphs")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the paged / fp8 KV decode-attention timings")
-    ap.add_argument("--sweep", action="store_true", help="also time rho = 10, 30, 100")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 128K density sweep (rho = 10, 30, 100)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the 32K, ragged and tiny prefill workloads")
     ap.add_argument("--diag", action="store_true",
                     help="parameter sweep (s, k, B, rho) and selection-quality diagnostics")
     ap.add_argument("--seqlen", type=int, default=None, help="override n (testing only)")
@@ -186,7 +196,7 @@ def bench_prefill(args, torch, sws, gen, timer_cls):
         res["dense_attn_tflops"] = dense_flops / (dms * 1e-3) / 1e12
         res["speedup_attn_vs_dense"] = dms / attn_ms
         res["speedup_layer_vs_dense_attn"] = dms / ms_layer
-    if args.sweep:
+    if not args.no_sweep:
         sweep = {}
         for rho in (10, 30, 100):
             w2 = sws.select_width(rho, geo.max_blocks)
@@ -210,10 +220,110 @@ def bench_prefill(args, torch, sws, gen, timer_cls):
             p2 = int(cnt2.long().sum().item())
             sweep[str(rho)] = {"ms_per_layer": Ts.ms("layer"), "attn_ms": Ts.ms("attention"),
                                "attn_exec_tflops": 4.0 * B * B * d * p2 / (Ts.ms("attention") * 1e-3) / 1e12,
-                               "dense_equiv_tflops": dense_flops / (Ts.ms("layer") * 1e-3) / 1e12}
-        res["rho_sweep"] = sweep
+                               "dense_equiv_tflops": dense_flops / (Ts.ms("layer") * 1e-3) / 1e12,
+                               "executed_causal_density": p2 / causal_pairs}
+        sweep["20"] = {"ms_per_layer": ms_layer, "attn_ms": attn_ms,
+                       "attn_exec_tflops": res["attn_exec_tflops"],
+                       "dense_equiv_tflops": res["dense_equiv_tflops"],
+                       "executed_causal_density": pairs / causal_pairs}
+        full = sweep["100"]
+        for rho_, ent in sweep.items():
+            ent["speedup_layer_vs_rho100"] = full["ms_per_layer"] / ent["ms_per_layer"]
+            ent["speedup_attn_vs_rho100"] = full["attn_ms"] / ent["attn_ms"]
+        res["rho_sweep"] = {k_: sweep[k_] for k_ in ("10", "20", "30", "100")}
     ctx = {"cfg": cfg, "geo": geo, "layers": layers, "bufs": bufs, "signs": signs, "cols": cols}
     return res, ctx
+
+
+def bench_prefill_workload(torch, sws, gen, timer_cls, name, steps=8, warmup=2, distinct=4):
+    """ms per sparse layer (sketch Q and K, walk, select, attention) of the
+    32K ("C2") or ragged 8-sequence ("C5") prefill workload, cycling over
+    `distinct` generated layers with inputs resident in HBM, the walk state
+    carried from step to step, timed with HIP events after `warmup` steps."""
+    cfg = gen.CONFIGS[name]
+    geo = sws.Geometry(list(cfg.seqlens), cfg.B)
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    signs_d, cols_d = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    layers = [gen.layer_inputs(cfg, cfg.n_dense + l, device="cuda")[:3] for l in range(distinct)]
+    hq, hkv, d, B = cfg.hq, cfg.hkv, cfg.d, cfg.B
+    width = sws.select_width(cfg.rho, geo.max_blocks)
+    q_sk = torch.empty((hq, geo.total_blocks, cfg.k), dtype=torch.float32, device="cuda")
+    k_sk = torch.empty((hkv, geo.total_blocks, cfg.k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((hq, geo.total_blocks, width), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((hq, geo.total_blocks), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(layers[0][0])
+    ws = torch.empty(sws.prefill_workspace_size(sws.BF16, geo.total_blocks, hkv, d, B),
+                     dtype=torch.uint8, device="cuda")
+    R = torch.empty(geo.walk_numel(hq), dtype=torch.float32, device="cuda")
+    T = timer_cls(torch)
+
+    def step(i, first, timed):
+        q, k, v = layers[i % distinct]
+        ev = [T.ev()] if timed else None
+        sws.sketch(q, geo, cfg.k, signs_d, cols_d, out=q_sk)
+        sws.sketch(k, geo, cfg.k, signs_d, cols_d, out=k_sk)
+        sws.walk_update(q_sk, k_sk, geo, cfg.s, None if first else R, R_out=R)
+        sws.select_topk(R, hq, geo, cfg.rho, idx=idx, cnt=cnt)
+        if timed: ev.append(T.ev())
+        sws.sparse_attn_prefill(q, k, v, geo, idx, cnt, out=out, ws=ws)
+        if timed:
+            ev.append(T.ev())
+            T.add("layer", ev[0], ev[2])
+            T.add("select_chain", ev[0], ev[1])
+            T.add("attention", ev[1], ev[2])
+
+    for i in range(warmup):
+        step(i, i == 0, False)
+    for i in range(steps):
+        step(warmup + i, False, True)
+    torch.cuda.synchronize()
+    pairs = int(cnt.long().sum().item())
+    ms = T.ms("layer")
+    causal_pairs = hq * sum(b * (b + 1) // 2 for b in geo.blocks)
+    dense_flops = 4.0 * d * hq * sum(n * (n + 1) / 2.0 for n in geo.seqlens)
+    res = {"workload": cfg.name, "seqlens": list(geo.seqlens), "heads": f"{hq}q/{hkv}kv",
+           "B": B, "k": cfg.k, "rho": cfg.rho, "ms_per_layer": ms,
+           "ms_per_stack": ms * cfg.layers,
+           "select_chain_us": T.ms("select_chain") * 1e3, "attn_ms": T.ms("attention"),
+           "dense_equiv_tflops": dense_flops / (ms * 1e-3) / 1e12,
+           "attn_exec_tflops": 4.0 * B * B * d * pairs / (T.ms("attention") * 1e-3) / 1e12,
+           "executed_causal_density": pairs / causal_pairs,
+           "note": (f"one sparse layer per step, {steps} timed after {warmup} warm-up; "
+                    f"ms_per_stack = ms_per_layer x {cfg.layers} layers")}
+    del layers
+    return res
+
+
+def bench_tiny(torch, sws, gen, reps=50):
+    """Latency of the tiny fp32 stack (1 head, n = 1024, d = 64, B = 64,
+    k = 16, 4 layers, the first two dense): all four layers (sketch, walk,
+    select, attention each), timed with HIP events over `reps` runs."""
+    cfg = gen.CONFIGS["C1"]
+    geo = sws.Geometry(list(cfg.seqlens), cfg.B)
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    layers = [gen.layer_inputs(cfg, l, device="cuda")[:3] for l in range(cfg.layers)]
+    R = torch.empty(geo.walk_numel(cfg.hq), dtype=torch.float32, device="cuda")
+
+    def stack():
+        for l, (q, k, v) in enumerate(layers):
+            sws.prefill_layer(q, k, v, geo, cfg.k, sd, cd, cfg.s, cfg.rho, l < cfg.n_dense, R,
+                              first_layer=l == 0)
+
+    for _ in range(3):
+        stack()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        stack()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"workload": cfg.name, "us_per_stack": us, "us_per_layer": us / cfg.layers,
+            "layers": cfg.layers, "dtype": "f32",
+            "note": "eager launches (5 per layer, outputs allocated by the binding); launch-latency bound"}
 
 
 def bench_decode(args, torch, sws, gen, timer_cls):
@@ -298,21 +408,41 @@ def bench_decode(args, torch, sws, gen, timer_cls):
                 T.add("dense_attn" if dense else "sparse_attn", b_, c_)
                 T.add("dense_select_chain" if dense else "sparse_select_chain", a, b_)
 
-    # the decode steps run in order (the sketch caches and running sums are
-    # state); one step is warm-up
-    one_step(0)
+    def restore(sn):
+        for st_, x in zip(state, sn):
+            for k_, v_ in x.items():
+                st_[k_].copy_(v_)
+
+    # The decode steps run in order (the sketch caches and running sums are
+    # state).  An untimed pass over every step first (it warms up and
+    # records the union size of every sparse layer-step: the algorithmic
+    # bytes of the attention), then the state is restored and all steps are
+    # timed.
+    n_sparse = Lyr - min(Lyr, cfg.n_dense)
+    union_sum = torch.zeros((steps, max(1, n_sparse)), dtype=torch.int64, device="cuda")
+    for t in range(steps):
+        for l, st in enumerate(state):
+            dense = l < cfg.n_dense
+            sws.sketch_append_qk(st["qst"][t], st["knew"][t], pos[t], B, kd, signs_d, cols_d,
+                                 st["rq"], st["rk"], st["qsk"], st["ksk"])
+            sws.walk_update_row(st["qsk"], st["ksk"], cur[t], cfg.s, None if l == 0 else r, r)
+            u = sws.select_topk_row(r, hq, hkv, cur[t], b_max, cfg.rho, dense=dense,
+                                    out=dbufs if dense else ubufs)
+            sws.sparse_attn_decode(st["qst"][t], st["kc"], st["vc"], ctx_len[t], B, u[0], u[1],
+                                   u[2], out=st["out"], ws=ws, head_major=head_major)
+            if not dense:
+                union_sum[t, l - cfg.n_dense] = u[1].sum()
     torch.cuda.synchronize()
+    union_blocks = float(union_sum.double().mean()) if n_sparse else 0.0
+    restore(snap)
     T = timer_cls(torch)
     e0 = T.ev()
-    for t in range(1, steps):
+    for t in range(steps):
         one_step(t, T)
     e1 = T.ev()
     torch.cuda.synchronize()
-    timed = steps - 1
+    timed = steps
     us_step = e0.elapsed_time(e1) * 1e3 / timed
-    # union sizes at the last step (algorithmic bytes of the sparse attention)
-    ucnt = ubufs[1].long()
-    union_blocks = int(ucnt.sum().item())
     tok_read = union_blocks * B            # the open block is partial; counted whole
     attn_bytes = tok_read * d * 2 * 2 + ns * hq * d * 2 * 2
     sp_attn_us = T.ms("sparse_attn") * 1e3
@@ -328,6 +458,9 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         "sparse_attn_gbs": attn_bytes / (sp_attn_us * 1e-6) / 1e9,
         "dense_attn_gbs": (ns * (P + steps // 2) * hkv * d * 4) / (T.ms("dense_attn") * 1e-3) / 1e9,
         "union_blocks_per_group": union_blocks / (ns * hkv),
+        "union_note": ("algorithmic bytes per sparse layer-step: the mean over every "
+                       "sparse layer-step of the union blocks, K and V rows of whole blocks, "
+                       "plus q and out"),
         "per_head_blocks": cfg.rho * (b_max - 1) // 100 + 1,
         "setup_s": setup_s,
         "kv_layout": ("head-major [seq][kv head][ctx][d]" if head_major
@@ -337,9 +470,7 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         # The same steps again from the same starting state, each step one
         # HIP graph replay of all layers' kernels (captured once on static
         # buffers) after one copy of the step's q, k and positions into them.
-        for st_, sn in zip(state, snap):
-            for k_, v_ in sn.items():
-                st_[k_].copy_(v_)
+        restore(snap)
         del snap
         q_buf = torch.empty_like(q_all[:, 0])
         k_buf = torch.empty_like(k_all[:, 0])
@@ -406,10 +537,14 @@ def bench_decode(args, torch, sws, gen, timer_cls):
             stage(0)
             graph.replay()
             torch.cuda.synchronize()
+            for st_, sn in zip(state, snap2):
+                for k_, v_ in sn.items():
+                    st_[k_].copy_(v_)
+            torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            for t in range(1, steps):
+            for t in range(steps):
                 stage(t)
                 graph.replay()
             e1.record()
@@ -737,6 +872,23 @@ def cpu_baseline(ctx, torch, budget_s=12.0):
     }
 
 
+def cpu_tiny_single_thread(gen):
+    """The oracle on the whole tiny stack (4 layers, every block, attention of
+    every query block) with one BLAS thread."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    cfg = gen.CONFIGS["C1"]
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    layers = [tuple(x.double().numpy()[:, :, :] for x in gen.layer_inputs(cfg, l)[:3])
+              for l in range(cfg.layers)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.prefill(layers, signs, cols, cfg.B, cfg.s, cfg.rho, cfg.n_dense)
+        dt = time.perf_counter() - t0
+    return {"us_per_stack": dt * 1e6, "cores": 1, "kind": "oracle",
+            "sample": "fp64 NumPy oracle, tiny stack (1 head, n=1024, 4 layers), one thread, whole"}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     """A plain device copy of known size, for scaling the HBM counters."""
     x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -777,6 +929,19 @@ def main():
         print(f"[bench] cpu oracle sample {cpu['sample_seconds']:.1f}s", file=sys.stderr, flush=True)
     del ctx
     torch.cuda.empty_cache()
+    others = None
+    if not args.no_other_workloads:
+        others = {}
+        for name, key in (("C2", "prefill_32k"), ("C5", "prefill_ragged")):
+            others[key] = bench_prefill_workload(torch, sws, gen, Timer, name)
+            torch.cuda.empty_cache()
+            print(f"[bench] {key}: {others[key]['ms_per_layer']:.3f} ms/layer", file=sys.stderr,
+                  flush=True)
+        others["tiny_stack"] = bench_tiny(torch, sws, gen)
+        print(f"[bench] tiny stack: {others['tiny_stack']['us_per_stack']:.1f} us",
+              file=sys.stderr, flush=True)
+        if cpu is not None:
+            cpu["tiny_stack_single_thread"] = cpu_tiny_single_thread(gen)
     dec = None
     if not args.no_decode:
         dec = bench_decode(args, torch, sws, gen, Timer)
@@ -791,9 +956,11 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": ("long_128k_prefill: one sparse layer per step, 32 query / 8 KV "
-                                f"heads, d=128, n={pre['n']}, B=128, k=32, s=8, rho={args.rho}%; "
-                                "decode_64k_b16: 16 x 64K-token context, 32 layers (2 dense), "
-                                "B=64, k=32, rho=20%"),
+                                f"heads, d=128, n={pre['n']}, B=128, k=32, s=8, rho={args.rho}% "
+                                "(also rho = 10/30/100); decode_64k_b16: 16 x 64K-token context, "
+                                "32 layers (2 dense), B=64, k=32, rho=20%, 256 steps; "
+                                "other_workloads: 32K prefill (B=64), ragged 8-sequence prefill "
+                                "(40q/8kv), tiny fp32 stack"),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(pre["attn_exec_tflops"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -801,11 +968,26 @@ def main():
                      "traffic": attn_bytes,
                      "kernel": "attn_prefill_bf16_kernel<128,128>",
                      "flops_per_launch": pre["attn_flops_per_launch"],
-                     "avg_launch_ms": round(pre["attn_ms"], 4)},
+                     "avg_launch_ms": round(pre["attn_ms"], 4),
+                     "target_frac": TARGET_PREFILL_MFMA_FRAC,
+                     "target_met": pre["attn_exec_tflops"] / PEAK_BF16_TFLOPS >= TARGET_PREFILL_MFMA_FRAC},
         "cpu_baseline": cpu,
         "prefill": pre,
         "decode": dec,
     }
+    if others:
+        line["other_workloads"] = others
+    if dec:
+        gbs = dec["sparse_attn_gbs"]
+        line["roofline_decode"] = {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "kernel": "decode_mfma_kernel + decode_combine_kernel (sparse layer-step)",
+            "bytes_per_launch": dec["sparse_attn_bytes"],
+            "avg_launch_us": round(dec["sparse_attn_us"], 2),
+            "traffic": traffic_for("attn_decode.hip", "decode_sparse_64k_b16"),
+            "target_frac": TARGET_DECODE_HBM_FRAC,
+            "target_met": gbs / PEAK_HBM_GBS >= TARGET_DECODE_HBM_FRAC}
     if diag:
         line["diagnostics"] = diag
     if dec:
