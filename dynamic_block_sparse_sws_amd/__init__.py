@@ -126,9 +126,25 @@ def version() -> int:
 
 
 def _ptr(t: Optional[torch.Tensor]):
+    """Device pointer of a tensor for the C ABI, which takes dense row-major
+    arrays on the GPU: a strided view (e.g. a slice of a fused qkv tensor) or
+    a host tensor would be read with the wrong layout, so both are rejected."""
     if t is None:
         return None
+    if not t.is_contiguous():
+        raise SwsError("argument", 2, f"tensor of shape {tuple(t.shape)} is not contiguous "
+                                      f"(strides {t.stride()}); pass .contiguous()")
+    if not t.is_cuda:
+        raise SwsError("argument", 2, f"tensor of shape {tuple(t.shape)} is on {t.device}, "
+                                      "not on a GPU")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _typed(t: Optional[torch.Tensor], dtype, what: str):
+    """_ptr of an index / table tensor that must have the given dtype."""
+    if t is not None and t.dtype != dtype:
+        raise SwsError("argument", 3, f"{what} must be {dtype}, not {t.dtype}")
+    return _ptr(t)
 
 
 def _stream(stream=None):
@@ -206,8 +222,8 @@ def sketch(x: torch.Tensor, geo: Geometry, k: int, signs: torch.Tensor, cols: to
         out = torch.empty((H, geo.total_blocks, k), dtype=torch.float32, device=x.device)
     _check("sws_sketch", lib().sws_sketch(
         _ptr(x), _dtype_code(x), _ptr(geo.cu_seqlens), _ptr(geo.cu_blocks), geo.n_seqs,
-        geo.total_blocks, H, d, geo.B, k, _ptr(signs), _ptr(cols), _ptr(out), ld_head,
-        _ptr(sum_out), _stream(stream)))
+        geo.total_blocks, H, d, geo.B, k, _typed(signs, torch.int8, "signs"),
+        _typed(cols, torch.int32, "cols"), _ptr(out), ld_head, _ptr(sum_out), _stream(stream)))
     return out
 
 
@@ -216,8 +232,9 @@ def sketch_append(x_new: torch.Tensor, pos: torch.Tensor, B: int, k: int, signs,
     n_seqs, H, d = x_new.shape
     b_max = sketch_cache.shape[2]
     _check("sws_sketch_append", lib().sws_sketch_append(
-        _ptr(x_new), _dtype_code(x_new), _ptr(pos), n_seqs, H, d, B, k, _ptr(signs), _ptr(cols),
-        _ptr(run_sum), _ptr(sketch_cache), b_max, _stream(stream)))
+        _ptr(x_new), _dtype_code(x_new), _typed(pos, torch.int32, "pos"), n_seqs, H, d, B, k,
+        _typed(signs, torch.int8, "signs"), _typed(cols, torch.int32, "cols"), _ptr(run_sum),
+        _ptr(sketch_cache), b_max, _stream(stream)))
 
 
 def sketch_append_qk(q_new: torch.Tensor, k_new: torch.Tensor, pos: torch.Tensor, B: int, k: int,
@@ -232,9 +249,9 @@ def sketch_append_qk(q_new: torch.Tensor, k_new: torch.Tensor, pos: torch.Tensor
     if k_cache.shape[2] != b_max:
         raise ValueError("q_cache and k_cache differ in b_max")
     _check("sws_sketch_append_qk", lib().sws_sketch_append_qk(
-        _ptr(q_new), _ptr(k_new), _dtype_code(q_new), _ptr(pos), n_seqs, hq, hkv, d, B, k,
-        _ptr(signs), _ptr(cols), _ptr(run_q), _ptr(run_k), _ptr(q_cache), _ptr(k_cache), b_max,
-        _stream(stream)))
+        _ptr(q_new), _ptr(k_new), _dtype_code(q_new), _typed(pos, torch.int32, "pos"), n_seqs,
+        hq, hkv, d, B, k, _typed(signs, torch.int8, "signs"), _typed(cols, torch.int32, "cols"),
+        _ptr(run_q), _ptr(run_k), _ptr(q_cache), _ptr(k_cache), b_max, _stream(stream)))
 
 
 def walk_update(q_sk: torch.Tensor, k_sk: torch.Tensor, geo: Geometry, s: int,
@@ -257,12 +274,14 @@ def walk_update_row(q_cache: torch.Tensor, k_cache: torch.Tensor, cur_block: tor
     hkv = k_cache.shape[1]
     if mode == WALK_DEFAULT:
         _check("sws_walk_update_row", lib().sws_walk_update_row(
-            _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs, _ptr(cur_block), b_max, s,
-            _ptr(r_prev), _ptr(r_out), _stream(stream)))
+            _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs,
+            _typed(cur_block, torch.int32, "cur_block"), b_max, s, _ptr(r_prev), _ptr(r_out),
+            _stream(stream)))
     else:
         _check("sws_walk_update_row_variant", lib().sws_walk_update_row_variant(
-            _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs, _ptr(cur_block), b_max, s, mode,
-            _ptr(r_prev), _ptr(r_out), _stream(stream)))
+            _ptr(q_cache), _ptr(k_cache), hq, hkv, k, n_seqs,
+            _typed(cur_block, torch.int32, "cur_block"), b_max, s, mode, _ptr(r_prev),
+            _ptr(r_out), _stream(stream)))
     return r_out
 
 
@@ -311,13 +330,15 @@ def select_topk(R: Optional[torch.Tensor], hq: int, geo: Geometry, rho: int, den
     if not row_tau and group_hkv is None:
         _check("sws_select_topk", lib().sws_select_topk(
             _ptr(R), hq, _ptr(geo.cu_blocks), geo.n_seqs, geo.total_blocks, geo.max_blocks, rho,
-            int(dense), width, _ptr(idx), _ptr(cnt), _stream(stream)))
+            int(dense), width, _typed(idx, torch.int32, "idx"), _typed(cnt, torch.int32, "cnt"),
+            _stream(stream)))
         return idx, cnt
     flags = ((SELECT_DENSE if dense else 0) | (SELECT_ROW_TAU if row_tau else 0)
              | (SELECT_GROUP if group_hkv is not None else 0))
     _check("sws_select_topk_flags", lib().sws_select_topk_flags(
         _ptr(R), hq, group_hkv or hq, _ptr(geo.cu_blocks), geo.n_seqs, geo.total_blocks,
-        geo.max_blocks, rho, flags, width, _ptr(idx), _ptr(cnt), _stream(stream)))
+        geo.max_blocks, rho, flags, width, _typed(idx, torch.int32, "idx"),
+        _typed(cnt, torch.int32, "cnt"), _stream(stream)))
     return idx, cnt
 
 
@@ -349,9 +370,11 @@ def select_topk_row(r: Optional[torch.Tensor], hq: int, hkv: int, cur_block: tor
         if idx is not None:
             w = idx.shape[2]
     _check("sws_select_topk_row", lib().sws_select_topk_row(
-        _ptr(r), hq, hkv, n_seqs, _ptr(cur_block), b_max, rho,
-        (SELECT_DENSE if dense else 0) | (SELECT_GROUP if group else 0), w, _ptr(idx),
-        _ptr(cnt), _ptr(uidx), _ptr(ucnt), _ptr(umask), uw, _stream(stream)))
+        _ptr(r), hq, hkv, n_seqs, _typed(cur_block, torch.int32, "cur_block"), b_max, rho,
+        (SELECT_DENSE if dense else 0) | (SELECT_GROUP if group else 0), w,
+        _typed(idx, torch.int32, "idx"), _typed(cnt, torch.int32, "cnt"),
+        _typed(uidx, torch.int32, "union_idx"), _typed(ucnt, torch.int32, "union_cnt"),
+        _typed(umask, torch.int32, "union_mask"), uw, _stream(stream)))
     return uidx, ucnt, umask, idx, cnt
 
 
@@ -376,8 +399,9 @@ def sparse_attn_prefill(q, k, v, geo: Geometry, idx: Optional[torch.Tensor],
     width = idx.shape[-1] if idx is not None else 0
     _check("sws_sparse_attn_prefill", lib().sws_sparse_attn_prefill(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(geo.cu_seqlens), _ptr(geo.cu_blocks),
-        geo.n_seqs, geo.total_blocks, geo.max_blocks, hq, hkv, d, geo.B, _ptr(idx), _ptr(cnt),
-        width, float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+        geo.n_seqs, geo.total_blocks, geo.max_blocks, hq, hkv, d, geo.B,
+        _typed(idx, torch.int32, "idx"), _typed(cnt, torch.int32, "cnt"), width, float(scale),
+        _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
     return out
 
 
@@ -405,8 +429,10 @@ def sparse_attn_decode(q, k_cache, v_cache, ctx_len, B: int, union_idx, union_cn
         out = torch.empty_like(q)
     _check("sws_sparse_attn_decode", lib().sws_sparse_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q) | (KV_HEAD_MAJOR if head_major else 0),
-        _ptr(ctx_len), n_seqs, max_ctx, hq,
-        hkv, d, B, _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
+        _typed(ctx_len, torch.int32, "ctx_len"), n_seqs, max_ctx, hq,
+        hkv, d, B, _typed(union_idx, torch.int32, "union_idx"),
+        _typed(union_cnt, torch.int32, "union_cnt"), _typed(union_mask, torch.int32, "union_mask"),
+        uw, float(scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
 
@@ -428,8 +454,10 @@ def sparse_attn_decode_noalloc(q, k_cache, v_cache, ctx_len, B: int, union_idx, 
         out = torch.empty_like(q)
     _check("sws_sparse_attn_decode_noalloc", lib().sws_sparse_attn_decode_noalloc(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q) | (KV_HEAD_MAJOR if head_major else 0),
-        _ptr(ctx_len), n_seqs, max_ctx, hq, hkv, d, B, _ptr(union_idx), _ptr(union_cnt),
-        _ptr(union_mask), uw, float(scale), _ptr(out), _ptr(lse), _stream(stream)))
+        _typed(ctx_len, torch.int32, "ctx_len"), n_seqs, max_ctx, hq, hkv, d, B,
+        _typed(union_idx, torch.int32, "union_idx"), _typed(union_cnt, torch.int32, "union_cnt"),
+        _typed(union_mask, torch.int32, "union_mask"), uw, float(scale), _ptr(out), _ptr(lse),
+        _stream(stream)))
     return out
 
 
@@ -468,8 +496,10 @@ def sparse_attn_decode_paged(q, k_pages, v_pages, block_table, ctx_len, union_id
     _check("sws_sparse_attn_decode_paged", lib().sws_sparse_attn_decode_paged(
         _ptr(q), _ptr(k_pages), _ptr(v_pages), kv | (KV_HEAD_MAJOR if head_major else 0),
         float(k_scale), float(v_scale),
-        _ptr(block_table), width, num_pages, _ptr(ctx_len), n_seqs, hq, hkv, d, B,
-        _ptr(union_idx), _ptr(union_cnt), _ptr(union_mask), uw, float(scale), _ptr(out),
+        _typed(block_table, torch.int32, "block_table"), width, num_pages,
+        _typed(ctx_len, torch.int32, "ctx_len"), n_seqs, hq, hkv, d, B,
+        _typed(union_idx, torch.int32, "union_idx"), _typed(union_cnt, torch.int32, "union_cnt"),
+        _typed(union_mask, torch.int32, "union_mask"), uw, float(scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
 

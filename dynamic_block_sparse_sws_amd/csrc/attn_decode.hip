@@ -142,7 +142,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int& total
 template <int BLK, int NT>
 __device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
                                           const int32_t* __restrict__ ucnt, int P, int hkv,
-                                          int32_t* spre, int* wtot) {
+                                          int rows, int uwidth, int32_t* spre, int* wtot) {
   constexpr int LB = 8;                       // loads in flight per thread
   const int t = threadIdx.x;
   for (int p0 = 0; p0 < P; p0 += LB * NT) {
@@ -150,7 +150,9 @@ __device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int p = min(p0 + u * NT + t, P - 1);
-      v[u] = ucnt ? ucnt[p] : (ctx_len[p / hkv] + BLK - 1) / BLK;
+      // union sizes clamped to the list width, context lengths to the cache
+      v[u] = ucnt ? min(max(ucnt[p], 0), uwidth)
+                  : (min(max(ctx_len[p / hkv], 1), rows) + BLK - 1) / BLK;
     }
 #pragma unroll
     for (int u = 0; u < LB; ++u)
@@ -185,8 +187,12 @@ __device__ __forceinline__ int build_plan(const int32_t* __restrict__ ctx_len,
 // (hkv max_ctx d, max_ctx d, d).  For pages `seq` is the page stride and rows
 // count from the page's first token: [BLK][hkv][d] pages have (BLK hkv d, d,
 // hkv d), [hkv][BLK][d] pages (hkv BLK d, BLK d, d).
+// `rows` is a sequence's row capacity (max_ctx, or table_width * BLK for
+// pages): context lengths are clamped to it, so a length past the cache
+// reads inside the sequence's own rows.
 struct KvLayout {
   int64_t seq, head, row;
+  int rows;
 };
 
 // Partial state of blocks [a, b) of pair p's list for every query head of the
@@ -221,7 +227,7 @@ __device__ __forceinline__ void decode_range(
   const int seq = p / hkv;
   const int g = p % hkv;
   const int G = hq / hkv;
-  const int ctx = max(ctx_len[seq], 1);   // at least the new token
+  const int ctx = min(max(ctx_len[seq], 1), L.rows);   // the new token .. the cache
   const float sl2 = scale_log2 * kscale;
   const int last_blk = (ctx - 1) / BLK;
   const int ntok = (b - a) * BLK;
@@ -375,8 +381,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ int32_t spre[kDecMaxPairs + 1];
   __shared__ int wtot[kDecThreads / 64];
   const int P = n_seqs * hkv;
-  const int64_t W = build_plan<BLK, kDecThreads>(ctx_len, uidx ? ucnt : nullptr, P, hkv, spre,
-                                                 wtot);
+  const int64_t W = build_plan<BLK, kDecThreads>(ctx_len, uidx ? ucnt : nullptr, P, hkv, L.rows,
+                                                 uwidth, spre, wtot);
   // with fewer blocks than workgroups, only the first W get a (one-block) range
   const int nwg = (int)std::min<int64_t>(nwg_launched, std::max<int64_t>(W, 1));
   const int w = blockIdx.x;
@@ -480,7 +486,7 @@ __device__ __forceinline__ void mfma_range(
   const int seq = p / hkv;
   const int g = p % hkv;
   const int G = hq / hkv;
-  const int ctx = max(ctx_len[seq], 1);
+  const int ctx = min(max(ctx_len[seq], 1), L.rows);
   const int last_blk = (ctx - 1) / BLK;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -697,8 +703,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ float mw[NWV * 16], lw[NWV * 16];
   static_assert(NWV * D * kVtStride * 2 >= NWV * 16 * D * 4, "merge area fits in V^T area");
   const int P = n_seqs * hkv;
-  const int64_t W = build_plan<BLK, kDecThreads>(ctx_len, uidx ? ucnt : nullptr, P, hkv, spre,
-                                                 wtot);
+  const int64_t W = build_plan<BLK, kDecThreads>(ctx_len, uidx ? ucnt : nullptr, P, hkv, L.rows,
+                                                 uwidth, spre, wtot);
   const int nwg = (int)std::min<int64_t>(nwg_launched, std::max<int64_t>(W, 1));
   const int w = blockIdx.x;
   if (w == 0) {
@@ -904,8 +910,9 @@ hipError_t launch_attn_decode(const void* q, const void* k_cache, const void* v_
                               int union_width, float scale, void* out, float* lse, void* ws,
                               hipStream_t st) {
   if (n_seqs == 0) return hipSuccess;
-  const KvLayout L = head_major ? KvLayout{(int64_t)hkv * max_ctx * d, (int64_t)max_ctx * d, d}
-                                : KvLayout{(int64_t)max_ctx * hkv * d, d, (int64_t)hkv * d};
+  const KvLayout L = head_major
+                         ? KvLayout{(int64_t)hkv * max_ctx * d, (int64_t)max_ctx * d, d, max_ctx}
+                         : KvLayout{(int64_t)max_ctx * hkv * d, d, (int64_t)hkv * d, max_ctx};
 #define SWS_DEC(T, D, BLK)                                                                     \
   return pick_g<T, D, BLK>(q, k_cache, v_cache, ctx_len, n_seqs, L, hq, hkv, union_idx,       \
                            union_cnt, union_mask, union_width, scale, out, lse, ws, st)
@@ -931,8 +938,9 @@ hipError_t launch_attn_decode_paged(const void* q, const void* k_pages, const vo
                                     void* out, float* lse, void* ws, hipStream_t st) {
   if (n_seqs == 0) return hipSuccess;
   // a page holds B rows of every KV head: [B][hkv][d] or, head-major, [hkv][B][d]
-  const KvLayout L = head_major ? KvLayout{(int64_t)hkv * B * d, (int64_t)B * d, d}
-                                : KvLayout{(int64_t)B * hkv * d, d, (int64_t)hkv * d};
+  const int rows = (int)std::min<int64_t>((int64_t)table_width * B, 0x7fffffff);
+  const KvLayout L = head_major ? KvLayout{(int64_t)hkv * B * d, (int64_t)B * d, d, rows}
+                                : KvLayout{(int64_t)B * hkv * d, d, (int64_t)hkv * d, rows};
 #define SWS_DEC(TK, D, BLK)                                                                    \
   return pick_g<uint16_t, D, BLK, TK>(q, k_pages, v_pages, ctx_len, n_seqs, L, hq, hkv,       \
                                       union_idx, union_cnt, union_mask, union_width, scale,   \

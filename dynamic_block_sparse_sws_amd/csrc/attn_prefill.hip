@@ -385,18 +385,23 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int nb = idx ? cnt[(int64_t)h * total_blocks + gb] : i + 1;
+  // List entries are clamped to the causal blocks [0, i] and the count to
+  // [0, min(width, i + 1)], so a malformed list gives a wrong answer, never a
+  // stray access (a valid list is unchanged by the clamps).
+  const int nb = idx ? min(max(cnt[(int64_t)h * total_blocks + gb], 0), min(width, i + 1))
+                     : i + 1;
   const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
+  auto entry = [&](int nn) { return lst ? min(max(lst[nn], 0), i) : nn; };
 
   // Step sub of a block uses LDS buffer pair sub % 2; while it computes, the
   // next step (the block's next sub-step, or the first of the next block)
   // streams into the other pair.
-  int j = lst ? lst[0] : 0;
+  int j = entry(0);
   load_step(j, 0, Ks0, Vs0);
   step_barrier();
   for (int nn = 0; nn < nb; ++nn) {
     const bool has_next = nn + 1 < nb;
-    const int j_next = has_next ? (lst ? lst[nn + 1] : nn + 1) : j;
+    const int j_next = has_next ? entry(nn + 1) : j;
 #pragma unroll
     for (int sub = 0; sub < TL::NSUB; ++sub) {
       const bool odd = sub & 1;
@@ -464,10 +469,12 @@ __global__ __launch_bounds__(BLK) void attn_prefill_f32_kernel(
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int nb = idx ? cnt[(int64_t)h * total_blocks + gb] : i + 1;
+  // list entries clamped to [0, i] and the count to [0, min(width, i + 1)]
+  const int nb = idx ? min(max(cnt[(int64_t)h * total_blocks + gb], 0), min(width, i + 1))
+                     : i + 1;
   const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
   for (int nn = 0; nn < nb; ++nn) {
-    const int j = lst ? lst[nn] : nn;
+    const int j = lst ? min(max(lst[nn], 0), i) : nn;
     for (int k0 = 0; k0 < BLK; k0 += KT) {
       __syncthreads();
       for (int e = t; e < KT * D; e += BLK) {

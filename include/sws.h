@@ -16,9 +16,12 @@
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work on it and never synchronises.
  * - Arguments are validated on the host before any launch; on error nothing
- *   is launched and the outputs are untouched.  Device-side array contents
- *   (offsets, positions, index lists) are trusted: they must be consistent
- *   with the host sizes passed alongside them.
+ *   is launched and the outputs are untouched.  Device-side offsets and
+ *   positions (cu_seqlens, cu_blocks, pos, cur_block) are trusted: they must
+ *   be consistent with the host sizes passed alongside them.  Index lists,
+ *   their counts, context lengths and page tables are clamped by the kernels
+ *   to the ranges the sizes allow, so a malformed one gives a wrong result,
+ *   never an access outside the caller's buffers.
  * - Return value: SWS_OK (0) or an sws_status error code.  sws_status_string
  *   names a code; sws_last_error_detail gives a per-thread message for the
  *   most recent failed call.

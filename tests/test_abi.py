@@ -172,3 +172,26 @@ def test_decode_noalloc_validation():
                                             f(0.1), P, N, N) == 3
     assert L.sws_sparse_attn_decode_noalloc(P, P, P, 1, P, 16, 65792, 64, 2, 128, 64, P, P, P, 821,
                                             f(0.1), P, N, N) == 3
+
+
+def test_binding_rejects_strided_host_and_mistyped_tensors():
+    """The binding passes dense row-major GPU arrays only: a strided view, a
+    host tensor or an index tensor of the wrong dtype raises SwsError before
+    any call reaches the library."""
+    x = torch.zeros((4, 6, 8))
+    with pytest.raises(sws.SwsError, match="not contiguous"):
+        sws._ptr(x.transpose(0, 1))
+    with pytest.raises(sws.SwsError, match="not on a GPU"):
+        sws._ptr(x)
+    with pytest.raises(sws.SwsError, match="must be torch.int32"):
+        sws._typed(torch.zeros(3, dtype=torch.int64), torch.int32, "ctx_len")
+    with pytest.raises(sws.SwsError, match="must be torch.int8"):
+        sws._typed(torch.zeros(3, dtype=torch.int32), torch.int8, "signs")
+    assert sws._ptr(None) is None and sws._typed(None, torch.int32, "idx") is None
+    # a whole call: host tensors never reach the C ABI
+    q = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((2, 64, 2, 128), dtype=torch.bfloat16)
+    ctx = torch.full((2,), 64, dtype=torch.int32)
+    with pytest.raises(sws.SwsError, match="not on a GPU"):
+        sws.sparse_attn_decode(q, kc, kc, ctx, 64, None, None, None,
+                               ws=torch.zeros(1 << 20, dtype=torch.uint8))

@@ -192,3 +192,85 @@ def test_prefill_attention_offsets_past_2_31():
             assert err <= TOL_ATTN_BF16, (h, i, err)
             assert lerr <= TOL_ATTN_BF16, (h, i, lerr)
         _print("head", h, "ok")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_malformed_lists_are_clamped(dtype):
+    """Index lists with entries above the query block, past the sequence or
+    negative, and counts above the list width: the kernels clamp each entry to
+    [0, i] and the count to [0, min(width, i + 1)], so the result is the
+    attention over the clamped list (the oracle on that list), never a stray
+    access."""
+    B, d, hq, hkv = 64, 128, 4, 2
+    lens = [700, 300]
+    geo = sws.Geometry(lens, B)
+    q = _rand((geo.total_tokens, hq, d), 1).to(dtype)
+    k = _rand((geo.total_tokens, hkv, d), 2).to(dtype)
+    v = _rand((geo.total_tokens, hkv, d), 3).to(dtype)
+    width = 4
+    rng = np.random.default_rng(7)
+    idx = np.zeros((hq, geo.total_blocks, width), np.int32)
+    cnt = np.zeros((hq, geo.total_blocks), np.int32)
+    for h in range(hq):
+        for gb in range(geo.total_blocks):
+            idx[h, gb] = rng.integers(-3, 20, size=width)
+            cnt[h, gb] = rng.integers(1, width + 4)
+    lse = torch.empty((hq, geo.total_tokens), dtype=torch.float32, device="cuda")
+    out = sws.sparse_attn_prefill(q, k, v, geo, torch.from_numpy(idx).cuda(),
+                                  torch.from_numpy(cnt).cuda(), lse=lse)
+    torch.cuda.synchronize()
+    Q, K, V, O_, L_ = (f64(t) for t in (q, k, v, out, lse))
+    tol = TOL_ATTN_BF16 if dtype == torch.bfloat16 else 1e-5
+    grp = hq // hkv
+    for s, n in enumerate(lens):
+        t0, b0, b = int(geo.cu_seqlens_host[s]), int(geo.cu_blocks_host[s]), geo.blocks[s]
+        for h in range(hq):
+            g = h // grp
+            lists = []
+            for i in range(b):
+                nb = min(max(int(cnt[h, b0 + i]), 0), min(width, i + 1))
+                lists.append(np.clip(idx[h, b0 + i, :nb].astype(np.int64), 0, i))
+            res = O.sparse_attention_rows(Q[t0:t0 + n, h], K[t0:t0 + n, g], V[t0:t0 + n, g],
+                                          lists, B, 1 / np.sqrt(d), range(b))
+            for i in range(b):
+                o_w, lse_w = res[i]
+                a = t0 + i * B
+                assert np.abs(O_[a:a + o_w.shape[0], h] - o_w).max() <= tol, (s, h, i)
+                assert np.abs(L_[h, a:a + o_w.shape[0]] - lse_w).max() <= max(tol, 1e-4)
+
+
+def test_decode_context_past_the_cache_and_long_union_counts_are_clamped():
+    """A context length past the cache's rows is read as the whole cache, and
+    a union count above the list width as the width: the result is the
+    oracle's attention of the cache's last row over the clamped list."""
+    B, d, hq, hkv, max_ctx = 64, 128, 8, 2, 1000
+    ns = 2
+    q = _rand((ns, hq, d), 4).to(torch.bfloat16)
+    kc = _rand((ns, max_ctx, hkv, d), 5).to(torch.bfloat16)
+    vc = _rand((ns, max_ctx, hkv, d), 6).to(torch.bfloat16)
+    last = (max_ctx - 1) // B
+    uw = 6
+    rng = np.random.default_rng(8)
+    uidx = rng.integers(-2, last + 5, size=(ns, hkv, uw)).astype(np.int32)
+    ucnt = np.full((ns, hkv), uw + 3, np.int32)
+    umask = rng.integers(1, 1 << (hq // hkv), size=(ns, hkv, uw)).astype(np.int32)
+    ctx = torch.tensor([max_ctx + 100, max_ctx + 1], dtype=torch.int32, device="cuda")
+    lse = torch.empty((ns, hq), dtype=torch.float32, device="cuda")
+    out = sws.sparse_attn_decode(q, kc, vc, ctx, B, torch.from_numpy(uidx).cuda(),
+                                 torch.from_numpy(ucnt).cuda(), torch.from_numpy(umask).cuda(),
+                                 lse=lse)
+    torch.cuda.synchronize()
+    Qh, Kh, Vh, Oh, Lh = (f64(t) for t in (q, kc, vc, out, lse))
+    grp = hq // hkv
+    for s in range(ns):
+        for h in range(hq):
+            g, bit = h // grp, h % grp
+            lst = np.array([min(max(int(e), 0), last)
+                            for e, m in zip(uidx[s, g], umask[s, g]) if (m >> bit) & 1],
+                           np.int64)
+            if len(lst) == 0:
+                continue
+            o_w, lse_w = O.query_attention(Qh[s, h], Kh[s, :, g], Vh[s, :, g], lst, B,
+                                           max_ctx - 1, 1 / np.sqrt(d))
+            assert np.abs(Oh[s, h] - o_w).max() <= TOL_ATTN_BF16, (s, h)
+            assert abs(Lh[s, h] - lse_w) <= TOL_ATTN_BF16, (s, h)
