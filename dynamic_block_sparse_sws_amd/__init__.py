@@ -39,7 +39,9 @@ SELECT_ROW_TAU = 2
 SELECT_GROUP = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsws.so")
+# SWS_LIBRARY selects another build of the same library (the host-sanitizer
+# build, libsws_asan.so); by default the in-tree libsws.so
+LIB_PATH = os.environ.get("SWS_LIBRARY") or os.path.join(_HERE, "libsws.so")
 
 EXPORTED_SYMBOLS = (
     "sws_version", "sws_status_string", "sws_last_error_detail", "sws_sketch",

@@ -6,6 +6,8 @@
 #include <mutex>
 #include <string>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "sws_common.h"
 
 namespace {
@@ -32,6 +34,16 @@ sws_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// A roctx range around each call of the C ABI, named after the call, so a
+// profiler trace (rocprofv3 --marker-trace) shows the host-side validation
+// and launches of every call next to its kernels.
+struct RocRange {
+  explicit RocRange(const char* name) { roctxRangePushA(name); }
+  ~RocRange() { roctxRangePop(); }
+  RocRange(const RocRange&) = delete;
+  RocRange& operator=(const RocRange&) = delete;
+};
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool dtype_ok(int dt) { return dt == SWS_F32 || dt == SWS_BF16; }
@@ -46,8 +58,8 @@ int tau_of(int rho, int b) { return (int)(((int64_t)rho * b) / 100); }
 extern "C" {
 
 int sws_version(void) { return 100; }
-                
-                const char* sws_status_string(sws_status status) {
+
+const char* sws_status_string(sws_status status) {
   switch (status) {
     case SWS_OK: return "SWS_OK";
     case SWS_ERR_NULL: return "SWS_ERR_NULL";
@@ -60,11 +72,12 @@ int sws_version(void) { return 100; }
 }
 
 const char* sws_last_error_detail(void) { return g_detail.c_str(); }
-                                  
-                                  sws_status sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
-                                  int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
-                                  int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
-                                  int64_t ld_head, float* sum_out, void* stream) {
+
+sws_status sws_sketch(const void* x, int dtype, const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                      int32_t n_seqs, int32_t total_blocks, int32_t n_heads, int32_t d, int32_t B,
+                      int32_t k, const int8_t* signs, const int32_t* cols, float* sketch_out,
+                      int64_t ld_head, float* sum_out, void* stream) {
+  const RocRange roctx_range("sws_sketch");
   const char* fn = "sws_sketch";
   REQUIRE_PTR(x);
   REQUIRE_PTR(cu_seqlens);
@@ -91,6 +104,7 @@ sws_status sws_sketch_append(const void* x_new, int dtype, const int32_t* pos, i
                              int32_t n_heads, int32_t d, int32_t B, int32_t k, const int8_t* signs,
                              const int32_t* cols, float* run_sum, float* sketch_cache, int32_t b_max,
                              void* stream) {
+  const RocRange roctx_range("sws_sketch_append");
   const char* fn = "sws_sketch_append";
   REQUIRE_PTR(x_new);
   REQUIRE_PTR(pos);
@@ -117,6 +131,7 @@ sws_status sws_sketch_append_qk(const void* q_new, const void* k_new, int dtype,
                                 int32_t k, const int8_t* signs, const int32_t* cols, float* run_sum_q,
                                 float* run_sum_k, float* q_cache, float* k_cache, int32_t b_max,
                                 void* stream) {
+  const RocRange roctx_range("sws_sketch_append_qk");
   const char* fn = "sws_sketch_append_qk";
   REQUIRE_PTR(q_new);
   REQUIRE_PTR(k_new);
@@ -147,6 +162,7 @@ sws_status sws_walk_update(const float* q_sk, const float* k_sk, int32_t hq, int
                            const int32_t* cu_blocks, int32_t n_seqs, int32_t total_blocks,
                            int32_t max_blocks, int32_t s, const float* R_prev, float* R_out,
                            void* stream) {
+  const RocRange roctx_range("sws_walk_update");
   const char* fn = "sws_walk_update";
   REQUIRE_PTR(q_sk);
   REQUIRE_PTR(k_sk);
@@ -168,6 +184,7 @@ sws_status sws_walk_update_row(const float* q_sk_cache, const float* k_sk_cache,
                                int32_t hkv, int32_t k, int32_t n_seqs, const int32_t* cur_block,
                                int32_t b_max, int32_t s, const float* r_prev, float* r_out,
                                void* stream) {
+  const RocRange roctx_range("sws_walk_update_row");
   const char* fn = "sws_walk_update_row";
   REQUIRE_PTR(q_sk_cache);
   REQUIRE_PTR(k_sk_cache);
@@ -191,6 +208,7 @@ sws_status sws_walk_update_variant(const float* q_sk, const float* k_sk, int32_t
                                    int32_t total_blocks, int32_t max_blocks, int32_t s, int32_t mode,
                                    const float* R_prev, float* R_out, int64_t walk_numel, void* ws,
                                    size_t ws_bytes, void* stream) {
+  const RocRange roctx_range("sws_walk_update_variant");
   const char* fn = "sws_walk_update_variant";
   if (mode == SWS_WALK_DEFAULT)
     return sws_walk_update(q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs, total_blocks, max_blocks,
@@ -229,6 +247,7 @@ sws_status sws_walk_update_row_variant(const float* q_sk_cache, const float* k_s
                                        int32_t hkv, int32_t k, int32_t n_seqs,
                                        const int32_t* cur_block, int32_t b_max, int32_t s,
                                        int32_t mode, const float* r_prev, float* r_out, void* stream) {
+  const RocRange roctx_range("sws_walk_update_row_variant");
   const char* fn = "sws_walk_update_row_variant";
   if (mode == SWS_WALK_DEFAULT)
     return sws_walk_update_row(q_sk_cache, k_sk_cache, hq, hkv, k, n_seqs, cur_block, b_max, s,
@@ -281,6 +300,7 @@ static sws_status select_topk_impl(const char* fn, const float* R, int32_t hq, i
 sws_status sws_select_topk(const float* R, int32_t hq, const int32_t* cu_blocks, int32_t n_seqs,
                            int32_t total_blocks, int32_t max_blocks, int32_t rho_percent, int32_t dense,
                            int32_t width, int32_t* idx, int32_t* cnt, void* stream) {
+  const RocRange roctx_range("sws_select_topk");
   return select_topk_impl("sws_select_topk", R, hq, hq, cu_blocks, n_seqs, total_blocks,
                           max_blocks, rho_percent, dense ? SWS_SELECT_DENSE : 0, width, idx, cnt,
                           stream);
@@ -290,6 +310,7 @@ sws_status sws_select_topk_flags(const float* R, int32_t hq, int32_t hkv, const 
                                  int32_t n_seqs, int32_t total_blocks, int32_t max_blocks,
                                  int32_t rho_percent, int32_t flags, int32_t width, int32_t* idx,
                                  int32_t* cnt, void* stream) {
+  const RocRange roctx_range("sws_select_topk_flags");
   return select_topk_impl("sws_select_topk_flags", R, hq, hkv, cu_blocks, n_seqs, total_blocks,
                           max_blocks, rho_percent, flags, width, idx, cnt, stream);
 }
@@ -299,6 +320,7 @@ sws_status sws_select_topk_row(const float* r, int32_t hq, int32_t hkv, int32_t 
                                int32_t flags, int32_t width, int32_t* idx, int32_t* cnt,
                                int32_t* union_idx, int32_t* union_cnt, uint32_t* union_mask,
                                int32_t union_width, void* stream) {
+  const RocRange roctx_range("sws_select_topk_row");
   const char* fn = "sws_select_topk_row";
   const bool dense = (flags & SWS_SELECT_DENSE) != 0;
   if (flags & ~(SWS_SELECT_DENSE | SWS_SELECT_ROW_TAU | SWS_SELECT_GROUP))
@@ -335,6 +357,7 @@ sws_status sws_sparse_attn_prefill(const void* q, const void* k, const void* v, 
                                    int32_t d, int32_t B, const int32_t* idx, const int32_t* cnt,
                                    int32_t width, float scale, void* out, float* lse, void* ws,
                                    size_t ws_bytes, void* stream) {
+  const RocRange roctx_range("sws_sparse_attn_prefill");
   const char* fn = "sws_sparse_attn_prefill";
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
@@ -482,6 +505,7 @@ sws_status sws_sparse_attn_decode(const void* q, const void* k_cache, const void
                                   const int32_t* union_cnt, const uint32_t* union_mask,
                                   int32_t union_width, float scale, void* out, float* lse, void* ws,
                                   size_t ws_bytes, void* stream) {
+  const RocRange roctx_range("sws_sparse_attn_decode");
   return decode_contiguous("sws_sparse_attn_decode", q, k_cache, v_cache, dtype, ctx_len, n_seqs,
                            max_ctx, hq, hkv, d, B, union_idx, union_cnt, union_mask, union_width,
                            scale, out, lse, ws, ws_bytes, false, stream);
@@ -494,6 +518,7 @@ sws_status sws_sparse_attn_decode_noalloc(const void* q, const void* k_cache, co
                                           const int32_t* union_cnt, const uint32_t* union_mask,
                                           int32_t union_width, float scale, void* out, float* lse,
                                           void* stream) {
+  const RocRange roctx_range("sws_sparse_attn_decode_noalloc");
   return decode_contiguous("sws_sparse_attn_decode_noalloc", q, k_cache, v_cache, dtype, ctx_len,
                            n_seqs, max_ctx, hq, hkv, d, B, union_idx, union_cnt, union_mask,
                            union_width, scale, out, lse, nullptr, 0, true, stream);
@@ -507,6 +532,7 @@ sws_status sws_sparse_attn_decode_paged(const void* q, const void* k_pages, cons
                                         const int32_t* union_idx, const int32_t* union_cnt,
                                         const uint32_t* union_mask, int32_t union_width, float scale,
                                         void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const RocRange roctx_range("sws_sparse_attn_decode_paged");
   const char* fn = "sws_sparse_attn_decode_paged";
   REQUIRE_PTR(q);
   REQUIRE_PTR(k_pages);
