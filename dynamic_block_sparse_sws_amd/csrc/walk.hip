@@ -898,6 +898,181 @@ __global__ __launch_bounds__(kRowThreads) void walk_row_kernel(
   for (int j = b + tid; j < b_max; j += kRowThreads) rout[j] = 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// decode, rows of up to 64 * LaneRows<KP> blocks: four waves per row
+// ---------------------------------------------------------------------------
+// Wave p of the workgroup owns sketch components [p KP/4, (p+1) KP/4) of every
+// row j; lane g owns the segment of L = ceil(b / 64) consecutive rows
+// j0 = (63 - g) L .. j0 + L - 1 (descending j over the lanes, so the suffix sum
+// over j is a prefix scan over the lanes of one wave).  The segment's q and k
+// sketch components stay in registers for all s hops.  Each wave therefore
+// holds the whole row's x and takes its maximum alone; a hop is
+//   B  T = sum over the segment of x q (this wave's components), an in-wave
+//      exclusive scan of T over the lanes;
+//   C  running down the segment, S += x q and the row's partial product
+//      k . S to LDS (one buffer per hop parity), barrier;
+//   A  (next hop) x of the segment's rows from the four waves' partials, the
+//      row maximum (wave reduction), x scaled by the power of two nearest
+//      below 1 / max and cut to the walk floor.
+// One barrier per hop: a wave writes the other parity's buffer only after
+// every wave has passed the barrier that follows its last read of it.
+template <int KP> struct LaneRows;
+template <> struct LaneRows<16> { static constexpr int value = 16; };
+template <> struct LaneRows<32> { static constexpr int value = 12; };
+template <> struct LaneRows<64> { static constexpr int value = 6; };
+constexpr int kLaneThreads = 256;
+
+template <int KP>
+__global__ __launch_bounds__(kLaneThreads) void walk_row_lane_kernel(
+    const float* __restrict__ q_cache, const float* __restrict__ k_cache, int hq, int hkv,
+    const int32_t* __restrict__ cur_block, int n_seqs, int b_max, int s,
+    const float* r_prev, float* r_out, float inv_sqrt_k) {
+  constexpr int CQ = KP / 4;                   // components per wave
+  constexpr int LR = LaneRows<KP>::value;      // rows per lane (capacity)
+  constexpr int CAP = 64 * LR;                 // rows per partial buffer
+  static_assert(CQ % 4 == 0, "whole 16-byte slots per wave");
+  __shared__ __attribute__((aligned(16))) float ypart[2][4][CAP];
+
+  // workgroup -> (sequence, head), query heads of one KV head on one XCD
+  const int grp = hq / hkv;
+  int pair, hi;
+  {
+    const int id = blockIdx.x;
+    const int np8 = (n_seqs * hkv) / 8 * 8;
+    if (id < np8 * grp) {
+      pair = id / (8 * grp) * 8 + id % 8;
+      hi = id / 8 % grp;
+    } else {
+      const int t = id - np8 * grp;
+      pair = np8 + t / grp;
+      hi = t % grp;
+    }
+  }
+  const int seq = pair / hkv;
+  const int h = pair % hkv * grp + hi;
+  const int c = cur_block[seq];
+  const int b = c + 1;
+  const int lane = threadIdx.x & 63;
+  const int p = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = (b + 63) / 64;                 // <= LR (b <= b_max, checked on the host)
+  const int j0 = min(b, (63 - lane) * L);
+  const int nv = min(b, j0 + L) - j0;          // rows of this lane's segment
+
+  const float* qrow = q_cache + ((int64_t)seq * hq + h) * b_max * KP + p * CQ;
+  const float* krow = k_cache + ((int64_t)seq * hkv + h / grp) * b_max * KP + p * CQ;
+  const float* rin = r_prev ? r_prev + ((int64_t)seq * hq + h) * b_max : nullptr;
+  float* rout = r_out + ((int64_t)seq * hq + h) * b_max;
+
+  // the segment's sketch components (zero past the segment) and its x
+  float qv[LR][CQ], kv[LR][CQ], xr[LR];
+#pragma unroll
+  for (int l = 0; l < LR; ++l) {
+    const bool in = l < nv;
+    const int j = j0 + l;
+#pragma unroll
+    for (int e = 0; e < CQ; e += 4) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a;
+      if (in) {
+        a = *reinterpret_cast<const float4*>(qrow + (int64_t)j * KP + e);
+        bb = *reinterpret_cast<const float4*>(krow + (int64_t)j * KP + e);
+      }
+      qv[l][e] = a.x; qv[l][e + 1] = a.y; qv[l][e + 2] = a.z; qv[l][e + 3] = a.w;
+      kv[l][e] = bb.x; kv[l][e + 1] = bb.y; kv[l][e + 2] = bb.z; kv[l][e + 3] = bb.w;
+    }
+    xr[l] = in ? (rin ? rin[j] : (j == c ? 1.0f : 0.0f)) : 0.f;
+  }
+
+  // x of the segment's rows from the partials of a hop's buffer, and the row's
+  // largest |x| (every lane of the wave gets it)
+  auto gather = [&](const float (*yp)[CAP]) -> float {
+    float lmax = 0.f;
+#pragma unroll
+    for (int l = 0; l < LR; ++l) {
+      if (l < L) {
+        const int j = j0 + l;
+        const float y = ((yp[0][j] + yp[1][j]) + (yp[2][j] + yp[3][j])) * inv_sqrt_k;
+        xr[l] = l < nv ? y : 0.f;
+        lmax = fmaxf(lmax, fabsf(xr[l]));
+      }
+    }
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_max_nonneg(lmax)), 63));
+  };
+
+  for (int hop = 0; hop < s; ++hop) {
+    // ---- A ----
+    float gmax;
+    if (hop > 0) {
+      gmax = gather(ypart[(hop - 1) & 1]);
+    } else {
+      float lmax = 0.f;
+#pragma unroll
+      for (int l = 0; l < LR; ++l) lmax = fmaxf(lmax, fabsf(xr[l]));
+      gmax = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_max_nonneg(lmax)), 63));
+    }
+    {
+      const float sc =
+          gmax > 0.f ? __builtin_amdgcn_ldexpf(1.0f, min(-__builtin_amdgcn_frexp_expf(gmax), 126))
+                     : 1.0f;
+      const float thr = hop > 0 ? (gmax * sc) * kWalkFloor : 0.f;
+#pragma unroll
+      for (int l = 0; l < LR; ++l) {
+        const float x = xr[l] * sc;
+        xr[l] = fabsf(x) < thr ? 0.f : x;
+      }
+    }
+    // ---- B ----
+    float S[CQ];
+#pragma unroll
+    for (int e = 0; e < CQ; ++e) S[e] = 0.f;
+#pragma unroll
+    for (int l = 0; l < LR; ++l) {
+      if (l < L) {
+#pragma unroll
+        for (int e = 0; e < CQ; ++e) S[e] += xr[l] * qv[l][e];
+      }
+    }
+    wave_prefix_sum_n<CQ>(S);
+    // exclusive: shifted up one lane (wave_shr:1, lane 0 gets 0)
+#pragma unroll
+    for (int e = 0; e < CQ; ++e)
+      S[e] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, S[e]), 0x138, 0xF, 0xF, true));
+    // ---- C ----
+    // (rows l in [nv, L) exist only in the truncated or empty segments at the
+    // end of the row; their x and sketches are zero and their products land on
+    // rows >= b, below CAP, which are never read as part of the row)
+    float (*yo)[CAP] = ypart[hop & 1];
+#pragma unroll
+    for (int l = LR - 1; l >= 0; --l) {
+      if (l < L) {
+        const float x = xr[l];
+        float y = 0.f;
+#pragma unroll
+        for (int e = 0; e < CQ; ++e) {
+          S[e] += x * qv[l][e];
+          y += kv[l][e] * S[e];
+        }
+        yo[p][j0 + l] = y;
+      }
+    }
+    __syncthreads();
+  }
+  // ---- final row, divided by its largest magnitude ----
+  const float gmax = gather(ypart[(s - 1) & 1]);
+  if (p == 0) {
+#pragma unroll
+    for (int l = 0; l < LR; ++l) {
+      if (l < nv) {
+        const float x = xr[l] / gmax;
+        rout[j0 + l] = gmax > 0.f && fabsf(x) >= kWalkFloor ? x : 0.f;
+      }
+    }
+  }
+  for (int j = b + (int)threadIdx.x; j < b_max; j += kLaneThreads) rout[j] = 0.f;
+}
+
 template <int KP>
 hipError_t run_walk(const float* q_sk, const float* k_sk, int hq, int hkv, int k,
                     const int32_t* cu_blocks, int n_seqs, int total_blocks, int max_blocks, int s,
@@ -916,6 +1091,12 @@ hipError_t run_walk_row(const float* q_sk, const float* k_sk, int hq, int hkv, i
                         const int32_t* cur_block, int b_max, int s, const float* r_prev,
                         float* r_out, hipStream_t st) {
   const dim3 grid(hq * n_seqs);
+  if (k == KP && b_max <= 64 * LaneRows<KP>::value) {
+    hipLaunchKernelGGL((walk_row_lane_kernel<KP>), grid, dim3(kLaneThreads), 0, st, q_sk, k_sk,
+                       hq, hkv, cur_block, n_seqs, b_max, s, r_prev, r_out,
+                       1.0f / sqrtf((float)k));
+    return hipGetLastError();
+  }
   // every row has b <= b_max blocks, so ceil(b_max / 256) bounds the segment length
   const int l_max = (b_max + kRowSeg - 1) / kRowSeg;
   if (k == KP && l_max <= 40 / (KP / 4))

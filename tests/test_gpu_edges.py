@@ -69,6 +69,10 @@ def test_empty_batches_launch_nothing():
     (2600, 24, 4, 4, 1),     # k not a power of two (padded to 32)
     (700, 64, 2, 2, 2),      # k = 64 past 512 blocks
     (1280, 32, 8, 4, 2),     # the largest rows held in registers (5 per segment)
+    (768, 32, 8, 4, 2),      # four-wave form: its largest rows at k = 32 (12 per lane)
+    (384, 64, 5, 4, 4),      # four-wave form at k = 64 (6 per lane)
+    (1024, 16, 8, 8, 2),     # four-wave form at k = 16 (16 per lane)
+    (37, 32, 8, 2, 1),       # short rows: most lanes hold no row
 ])
 def test_walk_row_long_and_odd_rows(b, k, s, hq, hkv):
     _print("walk row", b, k, s, hq, hkv)
