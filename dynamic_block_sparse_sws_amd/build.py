@@ -3,6 +3,10 @@
     python -m dynamic_block_sparse_sws_amd.build          # or build() from Python
     python -m dynamic_block_sparse_sws_amd.build --asan   # + libsws_asan.so
 
+build() also builds ceiling_probe, a standalone program (csrc/ceiling_probe.hip,
+not part of the library) that measures the MFMA, exp2 and LDS ceilings the
+attention kernels' roofline fractions are read against.
+
 The --asan variant compiles the host side of the C ABI layer (sws_api.hip:
 argument validation, error reporting, the scratch address lookup) with
 AddressSanitizer; the GPU code is built as usual.  Load it with the ASan
@@ -23,6 +27,7 @@ ROOT = os.path.dirname(PKG)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsws.so")
 LIB_ASAN = os.path.join(PKG, "libsws_asan.so")
+PROBE = os.path.join(PKG, "ceiling_probe")
 SOURCES = ["sws_api.hip", "sketch.hip", "walk.hip", "walk_variant.hip", "select.hip",
            "attn_prefill.hip", "attn_decode.hip"]
 ARCH = os.environ.get("SWS_OFFLOAD_ARCH", "gfx950")
@@ -98,14 +103,32 @@ def build_asan(verbose: bool = False) -> str:
     return LIB_ASAN
 
 
+def build_probe(verbose: bool = False) -> str:
+    """The ceiling-probe program, next to this file."""
+    tmp = PROBE + ".tmp"
+    cmd = [hipcc()] + [f for f in COMMON_FLAGS if f != "-fPIC"] + [
+        os.path.join(CSRC, "ceiling_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on ceiling_probe.hip:\n{r.stderr}")
+    os.replace(tmp, PROBE)
+    if verbose:
+        print(f"built {PROBE}")
+    return PROBE
+
+
 def build(verbose: bool = False, jobs: int = 6) -> str:
-    """Compile every source and link libsws.so next to this file."""
+    """Compile every source and link libsws.so next to this file; build the
+    ceiling-probe program."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES) + 1))) as ex:
+        probe = ex.submit(build_probe)
         objs = list(ex.map(_compile, SOURCES))
+        probe.result()
     _link(objs, LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE}")
     return LIB
 
 

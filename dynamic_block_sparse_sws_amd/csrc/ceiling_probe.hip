@@ -1,0 +1,190 @@
+// Ceiling probes for the roofline figures of the attention kernels (gfx950).
+//
+// A standalone program, not part of libsws.so: each probe is a register- or
+// LDS-only loop that measures what one instruction mix can reach on this chip
+// (with the clock it runs at, read from GRBM_GUI_ACTIVE when the program runs
+// under a counter pass), so that a kernel's fraction of the published peak can
+// be split into "what the mix allows" and "what the kernel loses".
+//
+//   mfma32      v_mfma_f32_32x32x16_bf16, 4 independent accumulators
+//   mfma16      v_mfma_f32_16x16x32_bf16, 8 independent accumulators
+//   mix<N>      4 x 32x32x16 MFMA plus N independent exp2 per loop trip
+//               (the prefill attention step issues 16 MFMA and 16 exp2 per
+//               32 x 32 score tile: 4 exp2 per 4 MFMA)
+//   lds         ds_read_b128 bandwidth, conflict-free addresses
+//   one<M,N>    one wave per SIMD (96 KB of LDS per block keeps one block per
+//               CU): M MFMA and N exp2 per trip in the same wave, to see how
+//               far one wave overlaps its own MFMA and transcendental work
+//
+// Every access stays inside the probe's own buffers; the loops have fixed
+// trip counts.  Output: one line per probe with the time and the rate.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void operands(bf16x8_t& a, bf16x8_t& b) {
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(threadIdx.x * 1e-3f + e);
+    b[e] = (__bf16)(e * 1e-3f);
+  }
+}
+
+__global__ __launch_bounds__(256) void mfma32_probe(float* out, int iters) {
+  bf16x8_t a, b;
+  operands(a, b);
+  floatx16_t acc[4];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void mfma16_probe(float* out, int iters) {
+  bf16x8_t a, b;
+  operands(a, b);
+  floatx4_t acc[8];
+  for (int i = 0; i < 8; ++i)
+    for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i)
+    for (int r = 0; r < 4; ++r) s += acc[i][r];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+template <int NEXP>
+__global__ __launch_bounds__(256) void mix_probe(float* out, int iters) {
+  bf16x8_t a, b;
+  operands(a, b);
+  floatx16_t acc[4];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float x[16];
+  for (int e = 0; e < 16; ++e) x[e] = -(float)(threadIdx.x % 7) * 0.01f - e * 0.001f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < NEXP; ++e) x[e % 16] = __builtin_amdgcn_exp2f(x[e % 16]) - 1.0f;
+  }
+  float s = 0.f;
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  for (int e = 0; e < 16; ++e) s += x[e];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void lds_probe(float* out, int iters) {
+  constexpr int N = 8192;                     // 32 KB
+  __shared__ __attribute__((aligned(16))) float sm[N];
+  for (int i = threadIdx.x; i < N; i += 256) sm[i] = i * 1e-3f;
+  __syncthreads();
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int base = (threadIdx.x * 4) & (N - 1);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // consecutive lanes read consecutive 16-byte slots; index < N - 3
+      const float4 v =
+          *reinterpret_cast<const float4*>(&sm[(base + u * 1024 + (it & 1) * 4) & (N - 4)]);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc.x + acc.y + acc.z + acc.w;
+}
+
+template <int NMFMA, int NEXP>
+__global__ __launch_bounds__(256) void one_wave_probe(float* out, int iters) {
+  __shared__ float pad[24576];                // 96 KB: one block per CU
+  pad[threadIdx.x] = 1.f;
+  __syncthreads();
+  bf16x8_t a, b;
+  operands(a, b);
+  floatx16_t acc[4];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float x[16];
+  for (int e = 0; e < 16; ++e) x[e] = -(float)(threadIdx.x % 7) * 0.01f - e * 0.001f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i)
+      acc[i % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i % 4], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < NEXP; ++e) x[e % 16] = __builtin_amdgcn_exp2f(x[e % 16]) - 1.0f;
+  }
+  float s = pad[(threadIdx.x + 1) % 256];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  for (int e = 0; e < 16; ++e) s += x[e];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+#define CHECK(x)                                                                     \
+  do {                                                                               \
+    const hipError_t e_ = (x);                                                       \
+    if (e_ != hipSuccess) {                                                          \
+      std::fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));            \
+      std::exit(1);                                                                  \
+    }                                                                                \
+  } while (0)
+
+}  // namespace
+
+int main() {
+  constexpr int kBlocks = 256 * 12;           // 12 blocks of 4 waves per CU
+  constexpr int kIters = 20000;
+  float* out = nullptr;
+  CHECK(hipMalloc(&out, (size_t)kBlocks * 256 * sizeof(float)));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  // rate = blocks x 4 waves x iterations x work per wave-iteration / time
+  auto run = [&](const char* name, void (*kern)(float*, int), int blocks, double work,
+                 const char* unit) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, 0, out, 100);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, 0, out, kIters);
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    const double rate = blocks * 4.0 * kIters * work / (ms * 1e-3);
+    std::printf("%-36s %9.3f ms  %9.1f %-8s %8.1f ns/trip\n", name, ms, rate / 1e12, unit,
+                ms * 1e6 / kIters);
+  };
+  const double f32x32 = 2.0 * 32 * 32 * 16, f16x16 = 2.0 * 16 * 16 * 32;
+  run("mfma 32x32x16 bf16, 4 chains", mfma32_probe, kBlocks, 4 * f32x32, "TFLOP/s");
+  run("mfma 16x16x32 bf16, 8 chains", mfma16_probe, kBlocks, 8 * f16x16, "TFLOP/s");
+  run("mfma 32x32x16 x4 + 0 exp2", mix_probe<0>, kBlocks, 4 * f32x32, "TFLOP/s");
+  run("mfma 32x32x16 x4 + 4 exp2", mix_probe<4>, kBlocks, 4 * f32x32, "TFLOP/s");
+  run("mfma 32x32x16 x4 + 8 exp2", mix_probe<8>, kBlocks, 4 * f32x32, "TFLOP/s");
+  run("mfma 32x32x16 x4 + 16 exp2", mix_probe<16>, kBlocks, 4 * f32x32, "TFLOP/s");
+  run("mfma 32x32x16 x4 + 32 exp2", mix_probe<32>, kBlocks, 4 * f32x32, "TFLOP/s");
+  run("lds ds_read_b128", lds_probe, kBlocks, 8 * 16.0 * 64, "TB/s");
+  run("1 wave/SIMD: 8 mfma", one_wave_probe<8, 0>, 256, 8 * f32x32, "TFLOP/s");
+  run("1 wave/SIMD: 16 exp2", one_wave_probe<0, 16>, 256, 0.0, "-");
+  run("1 wave/SIMD: 8 mfma + 16 exp2", one_wave_probe<8, 16>, 256, 8 * f32x32, "TFLOP/s");
+  run("1 wave/SIMD: 8 mfma + 32 exp2", one_wave_probe<8, 32>, 256, 8 * f32x32, "TFLOP/s");
+  run("1 wave/SIMD: 32 exp2", one_wave_probe<0, 32>, 256, 0.0, "-");
+  CHECK(hipFree(out));
+  return 0;
+}
