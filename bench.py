@@ -645,6 +645,88 @@ def serving_layouts(torch, sws, gen, st, ubufs, ctx, B, t, head_major, reps=20):
     return res
 
 
+# ---------------------------------------------------------------------------
+# Exact-score references of the selection diagnostics (torch on the device;
+# tests/test_bench_reference.py checks each against the oracle on small
+# inputs on the CPU)
+# ---------------------------------------------------------------------------
+
+def ref_block_means(torch, x, B):
+    """Mean of each block's token rows of x [n, d] in fp64, the last block over
+    the tokens it holds."""
+    n, d = x.shape
+    b = -(-n // B)
+    xx = torch.nn.functional.pad(x.double(), (0, 0, 0, b * B - n)).view(b, B, d).sum(1)
+    cnt = torch.full((b, 1), float(B), dtype=torch.float64, device=x.device)
+    cnt[-1, 0] = n - (b - 1) * B
+    return xx / cnt
+
+
+def ref_walk_sets(torch, qm, km, s, rho, floor=2.0 ** -64):
+    """Selected sets of the walk on exact block scores: M = tril(qm km^T) /
+    sqrt(d) (a sketch of dimension d is exact), s hops from the identity with
+    each hop's rows cut below floor times their largest magnitude, then per
+    query block i the tau = floor(rho b / 100) earlier blocks of largest score
+    (ties by index) plus block i (all of 0..i when i <= tau)."""
+    b, d = qm.shape
+    M = torch.tril(qm.double() @ km.double().T) / math.sqrt(d)
+    X = torch.eye(b, dtype=torch.float64, device=qm.device)
+    for _ in range(s):
+        X = X @ M
+        mx = X.abs().amax(dim=1, keepdim=True)
+        X = torch.where(X.abs() < floor * mx, torch.zeros_like(X), X)
+    X = X / X.abs().amax(dim=1, keepdim=True).clamp_min(1e-300)
+    tau = (rho * b) // 100
+    Xc = X.cpu().numpy() + 0.0
+    sets = []
+    for i in range(b):
+        if i <= tau:
+            sets.append(set(range(i + 1)))
+            continue
+        order = np.lexsort((np.arange(i), -Xc[i, :i]))[:tau]
+        sets.append(set(order.tolist()) | {i})
+    return sets
+
+
+def ref_captured_mass(torch, q, k, B, selections, rhos=(), chunk=8):
+    """Exact attention mass that block selections capture, per query row, for
+    one head: q, k [n, d] (computed in fp32, scale 1/sqrt(d), token-causal).
+    selections: name -> list over query blocks of key-block collections.  For
+    each rho in rhos also the best block selection of that density: for query
+    block i, the tau = floor(rho b / 100) earlier key blocks of largest total
+    exact mass over the block's queries, plus block i.  Returns name (or
+    'best rho=..') -> numpy array of the per-row captured mass."""
+    n, d = q.shape
+    b = -(-n // B)
+    qf, kf = q.float(), k.float()
+    res = {nm: [] for nm in selections}
+    res.update({f"best rho={r}": [] for r in rhos})
+    for c0 in range(0, b, chunk):
+        c1 = min(b, c0 + chunk)
+        r0, r1 = c0 * B, min(n, c1 * B)
+        S = (qf[r0:r1] @ kf[:r1].T.contiguous()) / math.sqrt(d)
+        keys = torch.arange(r1, device=q.device)
+        rows = torch.arange(r0, r1, device=q.device)
+        S = S.masked_fill(keys[None, :] > rows[:, None], float("-inf"))
+        P = torch.softmax(S, dim=1)
+        P = torch.nn.functional.pad(P, (0, c1 * B - r1))
+        Mrow = P.view(r1 - r0, c1, B).sum(2).double().cpu().numpy()
+        for i in range(c0, c1):
+            a, e = i * B - r0, min(n, (i + 1) * B) - r0
+            Mi = Mrow[a:e, :i + 1]
+            for nm, sel in selections.items():
+                res[nm].append(Mi[:, np.asarray(sorted(sel[i]), dtype=np.int64)].sum(1))
+            tot = Mi[:, :i].sum(0)
+            for r in rhos:
+                tau = (r * b) // 100
+                if i <= tau:
+                    keep = np.arange(i + 1)
+                else:
+                    keep = np.concatenate([np.lexsort((np.arange(i), -tot))[:tau], [i]])
+                res[f"best rho={r}"].append(Mi[:, keep].sum(1))
+    return {nm: np.concatenate(v) for nm, v in res.items()}
+
+
 def diagnostics(args, torch, sws, gen, ctx):
     """Sweeps over the walk degree s, the sketch dimension k, the block size B
     and the density rho on one 128K layer (walk started from the identity), with
@@ -707,34 +789,9 @@ def diagnostics(args, torch, sws, gen, ctx):
     b = geo.max_blocks
     tau = (20 * b) // 100
     ref_heads = [0, 13, 26]
-
-    def block_means(x):
-        pad = b * B - n
-        xx = torch.nn.functional.pad(x.double(), (0, 0, 0, pad)).view(b, B, d).sum(1)
-        cnt_ = torch.full((b, 1), float(B), dtype=torch.float64, device=dev)
-        cnt_[-1, 0] = n - (b - 1) * B
-        return xx / cnt_
-
-    def exact_sets(h, s=8, rho=20):
-        g = h // grp
-        M = torch.tril(block_means(q[:, h]) @ block_means(k[:, g]).T) / math.sqrt(d)
-        X = torch.eye(b, dtype=torch.float64, device=dev)
-        for _ in range(s):
-            X = X @ M
-            X = X / X.abs().amax(dim=1, keepdim=True).clamp_min(1e-300)
-        t_ = (rho * b) // 100
-        sets = []
-        Xc = X.cpu().numpy()
-        for i in range(b):
-            if i <= t_:
-                sets.append(set(range(i + 1)))
-                continue
-            row = Xc[i, :i]
-            order = np.lexsort((np.arange(i), -row))[:t_]
-            sets.append(set(order.tolist()) | {i})
-        return sets
-
-    ref = {h: exact_sets(h) for h in ref_heads}
+    ref = {h: ref_walk_sets(torch, ref_block_means(torch, q[:, h], B),
+                            ref_block_means(torch, k[:, h // grp], B), 8, 20)
+           for h in ref_heads}
 
     def jaccard(idx, cnt, heads=ref_heads):
         idx_h = idx.cpu().numpy()
@@ -787,7 +844,34 @@ def diagnostics(args, torch, sws, gen, ctx):
         run(geo, 32, 8, rho, lse=lse_s)
         frac = torch.exp((lse_s - lse_d).double())
         captured[str(rho)] = {"mean": float(frac.mean()), "p5": float(frac.quantile(0.05)),
-                              "min": float(frac.min())}
+                              "min": float(frac.min()),
+                              "mean_sampled_heads": float(frac[ref_heads].mean())}
+
+    # The same mass from exact fp32 attention on the sampled heads, for the
+    # kernels' selections and for the best block selection of each density
+    # (the ceiling of any block-sparse selection at that density).
+    sel_runs = {"s=8 rho=10": (8, 0, 10), "s=8 rho=20": (8, 0, 20), "s=8 rho=30": (8, 0, 30),
+                "s=1 rho=20": (1, 0, 20), "power s=8 rho=20": (8, sws.WALK_POWER, 20),
+                "softmax s=8 rho=20": (8, sws.WALK_SOFTMAX, 20)}
+    sel_lists = {}
+    for nm, (s_, mode, rho) in sel_runs.items():
+        idx, cnt, _ = run(geo, 32, s_, rho, attn=False, mode=mode)
+        sel_lists[nm] = (idx[ref_heads].cpu().numpy(), cnt[ref_heads].cpu().numpy())
+        del idx, cnt
+    per_name = {}
+    for hi, h in enumerate(ref_heads):
+        sels = {nm: [ix[hi, i, :ct[hi, i]] for i in range(b)] for nm, (ix, ct) in sel_lists.items()}
+        got = ref_captured_mass(torch, q[:, h], k[:, h // grp], B, sels, rhos=(10, 20, 30))
+        for nm, a in got.items():
+            per_name.setdefault(nm, []).append(a)
+    exact_mass = {}
+    for nm, vs in per_name.items():
+        a = np.concatenate(vs)
+        exact_mass[nm] = {"mean": float(a.mean()), "p5": float(np.quantile(a, 0.05)),
+                          "min": float(a.min())}
+    print(f"[diag] exact captured mass: " + ", ".join(f"{nm} {v_['mean']:.3f}"
+                                                      for nm, v_ in exact_mass.items()),
+          file=sys.stderr, flush=True)
 
     # planted chain recall: multi-hop walk against a one-hop walk
     recall = {}
@@ -809,7 +893,8 @@ def diagnostics(args, torch, sws, gen, ctx):
         recall[key] = {"near_block_j": hit_j / tot, "far_block_m": hit_m / tot,
                        "chains_x_heads": tot}
     return {"layer": "128K prefill layer (generator layer 2), walk from the identity",
-            "sweep": sweep, "captured_attention_mass": captured, "planted_chain_recall": recall,
+            "sweep": sweep, "captured_attention_mass": captured,
+            "exact_captured_mass_sampled_heads": exact_mass, "planted_chain_recall": recall,
             "exact_reference_heads": ref_heads}
 
 
