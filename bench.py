@@ -432,6 +432,10 @@ def bench_decode(args, torch, sws, gen, timer_cls):
                                    u[2], out=st["out"], ws=ws, head_major=head_major)
             if not dense:
                 union_sum[t, l - cfg.n_dense] = u[1].sum()
+        if (t + 1) % 64 == 0 or t + 1 == steps:
+            torch.cuda.synchronize()
+            print(f"[bench] decode recording pass: step {t + 1}/{steps}", file=sys.stderr,
+                  flush=True)
     torch.cuda.synchronize()
     union_blocks = float(union_sum.double().mean()) if n_sparse else 0.0
     restore(snap)
@@ -441,6 +445,7 @@ def bench_decode(args, torch, sws, gen, timer_cls):
         one_step(t, T)
     e1 = T.ev()
     torch.cuda.synchronize()
+    print(f"[bench] decode eager pass: {steps} steps", file=sys.stderr, flush=True)
     timed = steps
     us_step = e0.elapsed_time(e1) * 1e3 / timed
     tok_read = union_blocks * B            # the open block is partial; counted whole
