@@ -348,14 +348,21 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
 
   float4 xv[4], qv[2], kv[2];
   // Tiles strictly below the diagonal tile, with all 64 rows inside the
-  // sequence and 16-byte aligned rows, take plain 16-byte loads and stores;
-  // the others (the diagonal tile, a sequence's last rows, odd b) go through
-  // clamped, always valid addresses with the out-of-range values replaced.
+  // sequence and 16-byte aligned rows, take plain 16-byte loads and stores
+  // (thread (sr, sp): 16 consecutive entries of row sr).  The others (the
+  // diagonal tile, a sequence's last rows, b not a multiple of 4) are read and
+  // written row by row instead (xrow): entry e of wave w's lane l is row
+  // 16 w + e, column l, so each access of a wave covers 64 consecutive floats
+  // of one row whatever the row's alignment, through clamped, always valid
+  // addresses with the out-of-range values replaced.
   const bool plain_rows = i0 + kWmRows <= b && (b & 3) == 0;
+  const int row0 = i0 + 16 * __builtin_amdgcn_readfirstlane(w);   // a wave's first row (xrow)
+  bool xrow = false;
   auto fetch = [&](int hop, int jt) {
     const int ig = i0 + sr;
     const int jg0 = jt * kWmRows + sp * 16;
     const float* src = hop == 0 ? Rp : Rh;
+    xrow = src && !(plain_rows && jt < I);        // uniform
     if (!src) {                                   // the identity (uniform)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -364,23 +371,26 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
         for (int x = 0; x < 4; ++x) v[x] = (ig < b && jg0 + 4 * e + x == ig) ? 1.f : 0.f;
         xv[e] = make_float4(v[0], v[1], v[2], v[3]);
       }
-    } else if (plain_rows && jt < I) {           // uniform
+    } else if (!xrow) {
       const float4* p4 = reinterpret_cast<const float4*>(src + (int64_t)ig * b + jg0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) xv[e] = p4[e];
     } else {
-      const float* row = src + (int64_t)min(ig, b - 1) * b;
+      // 32-bit offsets within the head's b x b block (b <= 4096).  A row past
+      // the sequence reads the block's last entry (a finite walk value of
+      // magnitude <= 1): such rows only ever feed their own output rows, which
+      // are zeroed before the write-back, so they need no test here.
+      const int jg = jt * kWmRows + lane;
+      const int off0 = row0 * b + min(jg, b - 1);
+      const int last = b * b - 1;
+      float v[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int jg = jg0 + 4 * e + x;
-          const float t = row[min(jg, b - 1)];
-          v[x] = (ig < b && jg <= ig) ? t : 0.f;
-        }
-        xv[e] = make_float4(v[0], v[1], v[2], v[3]);
+      for (int e = 0; e < 16; ++e) {
+        const float t = src[min(off0 + e * b, last)];
+        v[e] = jg <= row0 + e ? t : 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[e] = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
     }
     // sketch rows: rows past the sequence (and, for k < 32, components
     // past k) are zero, read from clamped addresses and then replaced
@@ -409,13 +419,27 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   };
   auto stash = [&]() {
     // the previous hop's output, scaled and cut to the walk floor
-    const float sc = rsc[sr], th = rthr[sr];
-    auto cut = [&](float x) { x *= sc; return fabsf(x) < th ? 0.f : x; };
+    if (xrow) {
+      float v[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float4 v = xv[e];
-      v.x = cut(v.x); v.y = cut(v.y); v.z = cut(v.z); v.w = cut(v.w);
-      *reinterpret_cast<float4*>(&Xs[sr][sp * 16 + 4 * e]) = v;
+      for (int e = 0; e < 4; ++e) {
+        v[4 * e] = xv[e].x; v[4 * e + 1] = xv[e].y; v[4 * e + 2] = xv[e].z; v[4 * e + 3] = xv[e].w;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = row0 - i0 + e;              // uniform
+        const float x = v[e] * rsc[r];
+        Xs[r][lane] = fabsf(x) < rthr[r] ? 0.f : x;
+      }
+    } else {
+      const float sc = rsc[sr], th = rthr[sr];
+      auto cut = [&](float x) { x *= sc; return fabsf(x) < th ? 0.f : x; };
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float4 v = xv[e];
+        v.x = cut(v.x); v.y = cut(v.y); v.z = cut(v.z); v.w = cut(v.w);
+        *reinterpret_cast<float4*>(&Xs[sr][sp * 16 + 4 * e]) = v;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -526,20 +550,18 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)),
                              fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
       }
-      float* dst = Rh + (int64_t)ig * b + jg0;
       if (plain_rows && jt < I) {                 // uniform
+        float* dst = Rh + (int64_t)ig * b + jg0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) reinterpret_cast<float4*>(dst)[e] = v[e];
-      } else if (ig < b) {
-        // diagonal tile or last rows: only entries on or below the diagonal
-        // (so never past the row's end)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jg = jg0 + 4 * e;
-          if (jg <= ig) dst[4 * e] = v[e].x;
-          if (jg + 1 <= ig) dst[4 * e + 1] = v[e].y;
-          if (jg + 2 <= ig) dst[4 * e + 2] = v[e].z;
-          if (jg + 3 <= ig) dst[4 * e + 3] = v[e].w;
+      } else {
+        // row by row (as xrow reads it back): only entries on or below the
+        // diagonal of rows inside the sequence, so never past a row's end
+        const int jg = jt * kWmRows + lane;
+        const int nr = min(16, b - row0);         // rows of this wave inside the sequence
+#pragma unroll 4
+        for (int e = 0; e < nr; ++e) {
+          if (jg <= row0 + e) Rh[(row0 + e) * b + jg] = Xs[row0 - i0 + e][lane];
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 1));

@@ -278,3 +278,19 @@ def test_decode_context_past_the_cache_and_long_union_counts_are_clamped():
                                            max_ctx - 1, 1 / np.sqrt(d))
             assert np.abs(Oh[s, h] - o_w).max() <= TOL_ATTN_BF16, (s, h)
             assert abs(Lh[s, h] - lse_w) <= TOL_ATTN_BF16, (s, h)
+
+
+def test_prefill_walk_at_every_row_alignment():
+    """The prefill walk on sequences of 200, 201, 202 and 131 blocks (walk-state
+    rows of every length modulo 4, so rows that are and are not 16-byte
+    aligned; partial last row tiles) plus a one-tile sequence of 40 blocks,
+    two layers (the second carries the walk state), every stage against the
+    oracle."""
+    from gpu_util import PrefillRun, check_prefill_run
+    cfg = gen.CONFIGS["C2"].with_(d=128, B=64, hq=4, hkv=2, k=32, s=8)
+    seqlens = (200 * 64 - 5, 201 * 64, 202 * 64 - 63, 130 * 64 + 3, 40 * 64)
+    _print("walk alignment", seqlens)
+    run = PrefillRun(cfg, seqlens, 2, 20, n_dense=0)
+    assert [b % 4 for b in run.geo.blocks] == [0, 1, 2, 3, 0]
+    w = check_prefill_run(run, attn_rows_per_head=2, attn_heads=[0])
+    _print("worst", w)
