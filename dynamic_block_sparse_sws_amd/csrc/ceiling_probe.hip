@@ -15,6 +15,10 @@
 //   one<M,N>    one wave per SIMD (96 KB of LDS per block keeps one block per
 //               CU): M MFMA and N exp2 per trip in the same wave, to see how
 //               far one wave overlaps its own MFMA and transcendental work
+//   hbm read    a 4 GiB buffer streamed once with 16-byte loads (grid-stride,
+//               4 or 8 loads in flight per thread, 2048 or 8192 blocks), an xor
+//               of the words kept per thread
+//   hbm copy    a 2 GiB buffer copied to another with 16-byte accesses
 //
 // Every access stays inside the probe's own buffers; the loops have fixed
 // trip counts.  Output: one line per probe with the time and the rate.
@@ -135,6 +139,38 @@ __global__ __launch_bounds__(256) void one_wave_probe(float* out, int iters) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Streams n16 16-byte words: each thread keeps U loads in flight per trip.
+template <int U>
+__global__ __launch_bounds__(256) void hbm_read_probe(const uint4* __restrict__ src, size_t n16,
+                                                      unsigned* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void hbm_copy_probe(const uint4* __restrict__ src, size_t n16,
+                                                      uint4* __restrict__ dst) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a; dst[i + stride] = b; dst[i + 2 * stride] = c; dst[i + 3 * stride] = d;
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
 #define CHECK(x)                                                                     \
   do {                                                                               \
     const hipError_t e_ = (x);                                                       \
@@ -186,5 +222,47 @@ int main() {
   run("1 wave/SIMD: 8 mfma + 32 exp2", one_wave_probe<8, 32>, 256, 8 * f32x32, "TFLOP/s");
   run("1 wave/SIMD: 32 exp2", one_wave_probe<0, 32>, 256, 0.0, "-");
   CHECK(hipFree(out));
+
+  // HBM: 4 GiB read once, 2 GiB copied; 8 launches each after one untimed
+  const size_t read_bytes = (size_t)4 << 30, copy_bytes = (size_t)2 << 30;
+  uint4 *a = nullptr, *b = nullptr;
+  unsigned* sink = nullptr;
+  constexpr int kStreamBlocks = 256 * 32;   // largest grid of the stream probes
+  CHECK(hipMalloc(&a, read_bytes));
+  CHECK(hipMalloc(&b, copy_bytes));
+  CHECK(hipMalloc(&sink, (size_t)kStreamBlocks * 256 * sizeof(unsigned)));
+  CHECK(hipMemset(a, 1, read_bytes));
+  CHECK(hipDeviceSynchronize());
+  // mode 0: copy; otherwise a read with that many loads in flight per thread
+  auto stream = [&](const char* name, int mode, int blocks) {
+    const size_t n16 = (mode == 0 ? copy_bytes : read_bytes) / 16;
+    auto launch = [&]() {
+      if (mode == 0)
+        hipLaunchKernelGGL(hbm_copy_probe, dim3(blocks), dim3(256), 0, 0, a, n16, b);
+      else if (mode == 4)
+        hipLaunchKernelGGL(hbm_read_probe<4>, dim3(blocks), dim3(256), 0, 0, a, n16, sink);
+      else
+        hipLaunchKernelGGL(hbm_read_probe<8>, dim3(blocks), dim3(256), 0, 0, a, n16, sink);
+      CHECK(hipGetLastError());
+    };
+    launch();
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 8; ++r) launch();
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    const double bytes = 8.0 * (mode == 0 ? 2.0 * copy_bytes : (double)read_bytes);
+    std::printf("%-36s %9.3f ms  %9.1f %-8s\n", name, ms / 8, bytes / (ms * 1e-3) / 1e9, "GB/s");
+  };
+  stream("hbm read, 4 in flight, 2048 blocks", 4, 2048);
+  stream("hbm read, 4 in flight, 8192 blocks", 4, kStreamBlocks);
+  stream("hbm read, 8 in flight, 2048 blocks", 8, 2048);
+  stream("hbm read, 8 in flight, 8192 blocks", 8, kStreamBlocks);
+  stream("hbm copy, 2 GiB (read + write)", 0, kStreamBlocks);
+  CHECK(hipFree(a));
+  CHECK(hipFree(b));
+  CHECK(hipFree(sink));
   return 0;
 }
