@@ -443,6 +443,9 @@ def bench_decode(args, torch, sws, gen, timer_cls):
     e0 = T.ev()
     for t in range(steps):
         one_step(t, T)
+        if (t + 1) % 64 == 0 and t + 1 < steps:
+            print(f"[bench] decode eager pass: step {t + 1}/{steps} launched", file=sys.stderr,
+                  flush=True)
     e1 = T.ev()
     torch.cuda.synchronize()
     print(f"[bench] decode eager pass: {steps} steps", file=sys.stderr, flush=True)
