@@ -92,9 +92,9 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(
   }
 }
 
-template <int D, int BLK>
+template <int D, int BLK, int HP = 1>
 struct PrefillTile {
-  static constexpr int NW = BLK / 32;               // waves (32 query rows each)
+  static constexpr int NW = BLK / 32 * HP;          // waves (32 query rows each)
   static constexpr int NT = NW * 64;
   static constexpr int KT = 32;                     // keys per pipeline step
   static constexpr int NSUB = BLK / KT;             // steps per selected block
@@ -253,8 +253,9 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
   }
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 128 ? 3 : 2)))
+template <int D, int BLK, int HP>
+__global__ __launch_bounds__(BLK * 2 * HP)
+__attribute__((amdgpu_waves_per_eu(BLK == 128 || HP == 2 ? 3 : 2)))
 void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                               const uint16_t* __restrict__ vt,
                               const int32_t* __restrict__ cu_seqlens,
@@ -263,8 +264,9 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
                               const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
                               int width, float scale_log2, uint16_t* __restrict__ out,
                               float* __restrict__ lse) {
-  using TL = PrefillTile<D, BLK>;
+  using TL = PrefillTile<D, BLK, HP>;
   constexpr int NT = TL::NT, KT = TL::KT;
+  constexpr int WH = BLK / 32;                        // waves per query head
   static_assert(TL::NSUB % 2 == 0, "an even number of pipeline steps per block");
   // Two buffers per operand as separate LDS objects, so the compiler can tell
   // that the reads of one buffer do not wait on the direct-to-LDS loads
@@ -274,18 +276,25 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   __shared__ __attribute__((aligned(16))) char Vs0[TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs1[TL::TILE];
 
+  // Workgroup -> (query head(s), query block).  HP = 2 pairs query heads
+  // 2p and 2p + 1 of one KV group (the last pair of an odd group holds one
+  // head): the pair walks the merge of its two lists, so a block both heads
+  // selected is loaded once for both.
   const int G = hq / hkv;
   const int id = blockIdx.x;
-  const int slot = id % hq;
-  const int h = (slot % hkv) * G + slot / hkv;
-  const int gb = total_blocks - 1 - id / hq;
+  const int PPG = (G + HP - 1) / HP;                  // head slots per KV group
+  const int nslot = hkv * PPG;
+  const int slot = id % nslot;
+  const int hfirst = (slot % hkv) * G + slot / hkv * HP;
+  const int nheads = min(HP, (slot % hkv) * G + G - hfirst);   // 1 or HP
+  const int gb = total_blocks - 1 - id / nslot;
   const int seq = seq_of_block(cu_blocks, n_seqs, gb);
   const int i = gb - cu_blocks[seq];
   const int blk0 = cu_blocks[seq];
   const int tok0 = cu_seqlens[seq];
   const int n = cu_seqlens[seq + 1] - tok0;
   const int T = cu_seqlens[n_seqs];
-  const int kvh = h / G;
+  const int kvh = hfirst / G;
   const int64_t qstride = (int64_t)hq * D;
   const int64_t kstride = (int64_t)hkv * D;
 
@@ -294,7 +303,11 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int qi = w * 32 + l32;
+  // this wave's head in the workgroup (a lone head's partner waves idle)
+  const int hs = HP == 1 ? 0 : __builtin_amdgcn_readfirstlane(w) / WH;
+  const bool head_ok = HP == 1 || hs < nheads;
+  const int h = HP == 1 ? hfirst : hfirst + min(hs, nheads - 1);
+  const int qi = (HP == 1 ? w : w % WH) * 32 + l32;
   const int qrow = i * BLK + qi;
 
   // ---- this wave's Q rows as MFMA B operands ----
@@ -304,7 +317,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
       u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (qrow < n) raw = *reinterpret_cast<const u32x4_t*>(qp + dc * 16);
+      if (qrow < n && head_ok) raw = *reinterpret_cast<const u32x4_t*>(qp + dc * 16);
       // scaled once by scale * log2(e) (rounded to bf16), so the scores come
       // out of the matrix cores in log2 units
       qf[dc] = __builtin_bit_cast(bf16x8_t, raw);
@@ -388,37 +401,90 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   // List entries are clamped to the causal blocks [0, i] and the count to
   // [0, min(width, i + 1)], so a malformed list gives a wrong answer, never a
   // stray access (a valid list is unchanged by the clamps).
-  const int nb = idx ? min(max(cnt[(int64_t)h * total_blocks + gb], 0), min(width, i + 1))
-                     : i + 1;
-  const int32_t* lst = idx ? idx + ((int64_t)h * total_blocks + gb) * width : nullptr;
-  auto entry = [&](int nn) { return lst ? min(max(lst[nn], 0), i) : nn; };
+  auto list_len = [&](int hh) {
+    return idx ? min(max(cnt[(int64_t)hh * total_blocks + gb], 0), min(width, i + 1)) : i + 1;
+  };
+  auto list_of = [&](int hh) {
+    return idx ? idx + ((int64_t)hh * total_blocks + gb) * width : nullptr;
+  };
 
-  // Step sub of a block uses LDS buffer pair sub % 2; while it computes, the
-  // next step (the block's next sub-step, or the first of the next block)
-  // streams into the other pair.
-  int j = entry(0);
-  load_step(j, 0, Ks0, Vs0);
-  step_barrier();
-  for (int nn = 0; nn < nb; ++nn) {
-    const bool has_next = nn + 1 < nb;
-    const int j_next = has_next ? entry(nn + 1) : j;
+  if constexpr (HP == 1) {
+    const int nb = list_len(h);
+    const int32_t* lst = list_of(h);
+    auto entry = [&](int nn) { return lst ? min(max(lst[nn], 0), i) : nn; };
+
+    // Step sub of a block uses LDS buffer pair sub % 2; while it computes, the
+    // next step (the block's next sub-step, or the first of the next block)
+    // streams into the other pair.
+    int j = entry(0);
+    load_step(j, 0, Ks0, Vs0);
+    step_barrier();
+    for (int nn = 0; nn < nb; ++nn) {
+      const bool has_next = nn + 1 < nb;
+      const int j_next = has_next ? entry(nn + 1) : j;
 #pragma unroll
-    for (int sub = 0; sub < TL::NSUB; ++sub) {
-      const bool odd = sub & 1;
-      const bool last_sub = sub + 1 == TL::NSUB;
-      if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
-      else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
-      attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd, o,
-                        m_run, l_run, qi, hl);
+      for (int sub = 0; sub < TL::NSUB; ++sub) {
+        const bool odd = sub & 1;
+        const bool last_sub = sub + 1 == TL::NSUB;
+        if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
+        else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
+        attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd, o,
+                          m_run, l_run, qi, hl);
+        step_barrier();
+      }
+      j = j_next;
+    }
+  } else {
+    // The merge of the heads' ascending lists: each merged block carries a
+    // mask of the heads that selected it; a wave computes a step only if its
+    // head's bit is set, and every wave takes part in the loads and barriers.
+    // Each merge step consumes at least one entry, so the walk ends after at
+    // most nbA + nbB blocks whatever the lists hold.
+    const int nbA = list_len(hfirst);
+    const int nbB = nheads > 1 ? list_len(hfirst + 1) : 0;
+    const int32_t* lA = list_of(hfirst);
+    const int32_t* lB = nheads > 1 ? list_of(hfirst + 1) : nullptr;
+    constexpr int kEnd = 0x7fffffff;
+    auto peek = [&](int pa, int pb, int& j, int& mask) {
+      const int a = pa < nbA ? (lA ? min(max(lA[pa], 0), i) : pa) : kEnd;
+      const int b = pb < nbB ? (lB ? min(max(lB[pb], 0), i) : pb) : kEnd;
+      j = min(a, b);
+      mask = (a == j ? 1 : 0) | (b == j ? 2 : 0);
+    };
+    const int my_bit = 1 << hs;
+    int pa = 0, pb = 0, j, mask;
+    peek(pa, pb, j, mask);
+    if (j != kEnd) {
+      load_step(j, 0, Ks0, Vs0);
       step_barrier();
     }
-    j = j_next;
+    while (j != kEnd) {
+      pa += mask & 1;
+      pb += mask >> 1;
+      int j_next, mask_next;
+      peek(pa, pb, j_next, mask_next);
+      const bool has_next = j_next != kEnd;
+      const bool mine = (mask & my_bit) != 0;        // uniform over the wave
+#pragma unroll
+      for (int sub = 0; sub < TL::NSUB; ++sub) {
+        const bool odd = sub & 1;
+        const bool last_sub = sub + 1 == TL::NSUB;
+        if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
+        else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
+        if (mine)
+          attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd,
+                            o, m_run, l_run, qi, hl);
+        step_barrier();
+      }
+      j = j_next;
+      mask = mask_next;
+    }
   }
 
   // ---- finalise ----
   l_run += __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_run;
-  if (qrow < n) {
+  if (qrow < n && head_ok) {
     uint16_t* op = out + (int64_t)(tok0 + qrow) * qstride + (int64_t)h * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -526,12 +592,23 @@ hipError_t run_bf16(const void* q, const void* k, const void* v, const int32_t* 
                      total_blocks, hkv, vt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)total_blocks * hq);
-  hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, BLK>), grid, dim3(BLK * 2), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt,
-                     cu_seqlens, cu_blocks, n_seqs, total_blocks, hq, hkv, idx, cnt, width,
-                     scale * kLog2e, static_cast<uint16_t*>(out), lse);
-  return hipGetLastError();
+  // B = 64 with query-head groups of two or more: two query heads per
+  // workgroup (their 2 x 2 waves share the tiles of the blocks both
+  // selected); otherwise one head per workgroup (B / 32 waves)
+  const int G = hq / hkv;
+  auto launch = [&](auto hp) {
+    constexpr int HP = decltype(hp)::value;
+    dim3 grid((unsigned)total_blocks * hkv * ((G + HP - 1) / HP));
+    hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, BLK, HP>), grid, dim3(BLK * 2 * HP), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt,
+                       cu_seqlens, cu_blocks, n_seqs, total_blocks, hq, hkv, idx, cnt, width,
+                       scale * kLog2e, static_cast<uint16_t*>(out), lse);
+    return hipGetLastError();
+  };
+  if constexpr (BLK == 64) {
+    if (G >= 2) return launch(std::integral_constant<int, 2>{});
+  }
+  return launch(std::integral_constant<int, 1>{});
 }
 
 template <int D, int BLK>

@@ -34,6 +34,8 @@ def test_tiny_stack_fp32_all_layers():
     (128, 128, (700, 129, 1), 4, 1, 30),
     (64, 64, (257, 64, 1500), 6, 3, 20),
     (64, 128, (1024,), 2, 2, 10),
+    (128, 64, (900, 64, 3), 4, 4, 20),       # B = 64, one query head per KV head
+    (128, 64, (1000, 300), 6, 2, 20),       # B = 64, groups of three: a lone head per group
 ])
 def test_bf16_gqa_ragged(d, B, seqlens, hq, hkv, rho):
     cfg = gen.CONFIGS["C2"].with_(d=d, B=B, hq=hq, hkv=hkv, k=min(32, d))
