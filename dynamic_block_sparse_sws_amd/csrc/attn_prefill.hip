@@ -3,7 +3,10 @@
 // the key blocks selected for each query block).
 //
 // bf16 path: one workgroup per (query head, query block of B tokens), B/32
-// wavefronts, each owning 32 query rows.  A pre-pass writes V transposed per
+// wavefronts, each owning 32 query rows; at B = 64 (groups of two or more
+// query heads per KV head) one workgroup per pair of query heads of a group,
+// walking the merge of the two heads' lists so a block both selected is
+// loaded once.  A pre-pass writes V transposed per
 // block (keys in accumulator-row order) to a workspace.  The selected key
 // blocks are walked in steps of 32 keys: the K and V^T tiles of the next step
 // stream from memory straight into the other half of a double-buffered,
