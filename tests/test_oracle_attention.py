@@ -111,3 +111,26 @@ def test_query_attention_equals_masked_sdpa_row(seed):
     rows = O.sparse_attention_rows(Q[:p + 1], K[:p + 1], V[:p + 1], {c: lst}, B,
                                    1 / math.sqrt(d), [c])
     np.testing.assert_allclose(o, rows[c][0][-1], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (6, 3), (8, 1)])
+def test_gqa_head_map_equals_sdpa_enable_gqa(hq, hkv):
+    """The oracle's grouped-query map (query head h reads KV head h // (hq /
+    hkv), reading R14) against torch's grouped-query attention, which fixes
+    the same convention independently: one dense layer (every block kept),
+    all heads, fp64."""
+    n, d, B = 45, 8, 8
+    rng = np.random.default_rng(hq * 10 + hkv)
+    Q = rng.normal(size=(n, hq, d))
+    K = rng.normal(size=(n, hkv, d))
+    V = rng.normal(size=(n, hkv, d))
+    signs = np.ones(d, np.int8)
+    cols = np.arange(4, dtype=np.int32)
+    st = O.SeqPrefill(hq)
+    recs = O.prefill_layer(Q, K, V, st, signs, cols, B, 1, 20, dense=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q).permute(1, 0, 2)[None], torch.from_numpy(K).permute(1, 0, 2)[None],
+        torch.from_numpy(V).permute(1, 0, 2)[None], is_causal=True, enable_gqa=True)[0]
+    for h in range(hq):
+        got = np.concatenate([recs[h]["attn"][i][0] for i in sorted(recs[h]["attn"])])
+        np.testing.assert_allclose(got, ref[h].numpy(), rtol=1e-12, atol=1e-12)
