@@ -982,6 +982,31 @@ def cpu_tiny_single_thread(gen):
             "sample": "fp64 NumPy oracle, tiny stack (1 head, n=1024, 4 layers), one thread, whole"}
 
 
+def cpu_decode_sample(torch, gen):
+    """The oracle's decode of one sequence of the 16 x 64K decode workload at
+    its first step (row p of the prefill of the first p + 1 tokens, every
+    query head), one sparse layer with the walk row started from the open
+    block; the time is scaled to the whole batch and all layers of a step."""
+    import oracle as O
+    cfg = gen.CONFIGS["C4"]
+    qpre, qst, kc, vc = gen.decode_layer_inputs(cfg, cfg.n_dense, device="cpu", n_seqs=1,
+                                                prefix=cfg.decode_prefix, steps=1)
+    Q = torch.cat([qpre[0], qst[:, 0]], 0).double().numpy()
+    K = kc[0].double().numpy()
+    V = vc[0].double().numpy()
+    del qpre, qst, kc, vc
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    t0 = time.perf_counter()
+    O.decode_step([(Q, K, V)], signs, cols, cfg.B, cfg.s, cfg.rho, n_dense=0)
+    dt = time.perf_counter() - t0
+    return {"us_per_step_extrapolated": dt * 1e6 * cfg.decode_batch * cfg.layers,
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle decode of 1 of {cfg.decode_batch} sequences at its "
+                       f"first step ({cfg.decode_prefix + 1} tokens, {cfg.hq} query heads), one "
+                       f"sparse layer; scaled x{cfg.decode_batch} sequences x{cfg.layers} layers"),
+            "sample_seconds": dt}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     """A plain device copy of known size, for scaling the HBM counters."""
     x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -1039,6 +1064,10 @@ def main():
     if not args.no_decode:
         dec = bench_decode(args, torch, sws, gen, Timer)
         print(f"[bench] decode: {dec['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+        if cpu is not None:
+            cpu["decode_step"] = cpu_decode_sample(torch, gen)
+            print(f"[bench] cpu oracle decode sample {cpu['decode_step']['sample_seconds']:.1f}s",
+                  file=sys.stderr, flush=True)
     attn_bytes = traffic_for("attn_prefill.hip", "attn_prefill_bf16_128k_rho20")
     line = {
         "metric": METRIC,
