@@ -294,3 +294,42 @@ def test_prefill_walk_at_every_row_alignment():
     assert [b % 4 for b in run.geo.blocks] == [0, 1, 2, 3, 0]
     w = check_prefill_run(run, attn_rows_per_head=2, attn_heads=[0])
     _print("worst", w)
+
+
+@pytest.mark.parametrize("hq", [2, 3])
+def test_head_pairing_equals_one_head_form(hq):
+    """At B = 64 a KV group of two or more query heads runs two heads per
+    workgroup over the merge of their lists (three heads: a pair and a lone
+    head).  Each head's output and log-sum-exp equal, bit for bit, what the
+    one-head form computes for that head alone (one query head on the KV
+    head), on random ascending lists that differ between the heads."""
+    B, d = 64, 128
+    lens = [900, 333]
+    geo = sws.Geometry(lens, B)
+    T = geo.total_tokens
+    q = _rand((T, hq, d), 41).to(torch.bfloat16)
+    k = _rand((T, 1, d), 42).to(torch.bfloat16)
+    v = _rand((T, 1, d), 43).to(torch.bfloat16)
+    rng = np.random.default_rng(44)
+    width = 6
+    idx = np.zeros((hq, geo.total_blocks, width), np.int32)
+    cnt = np.zeros((hq, geo.total_blocks), np.int32)
+    for h in range(hq):
+        for s, b in enumerate(geo.blocks):
+            for i in range(b):
+                gb = int(geo.cu_blocks_host[s]) + i
+                pick = np.sort(rng.choice(i, size=min(i, width - 1), replace=False)) if i else []
+                lst = list(pick) + [i]
+                idx[h, gb, :len(lst)] = lst
+                cnt[h, gb] = len(lst)
+    idx_d, cnt_d = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    lse = torch.empty((hq, T), dtype=torch.float32, device="cuda")
+    out = sws.sparse_attn_prefill(q, k, v, geo, idx_d, cnt_d, lse=lse)
+    for h in range(hq):
+        lse1 = torch.empty((1, T), dtype=torch.float32, device="cuda")
+        out1 = sws.sparse_attn_prefill(q[:, h:h + 1].contiguous(), k, v, geo,
+                                       idx_d[h:h + 1].contiguous(), cnt_d[h:h + 1].contiguous(),
+                                       lse=lse1)
+        torch.cuda.synchronize()
+        assert torch.equal(out1[:, 0], out[:, h]), h
+        assert torch.equal(lse1[0], lse[h]), h
