@@ -15,6 +15,14 @@
 //   one<M,N>    one wave per SIMD (96 KB of LDS per block keeps one block per
 //               CU): M MFMA and N exp2 per trip in the same wave, to see how
 //               far one wave overlaps its own MFMA and transcendental work
+//   mfma+lds<E> 16 MFMA per trip, each with its A operand read from LDS
+//               (ds_read_b128, 1 KB per wave, the prefill step's ratio), plus E
+//               exp2 per MFMA: the attention step's mix without its global
+//               (L2 -> LDS) traffic
+//   + fill      the same plus, per trip, 4 KB per wave copied from a 2 MB
+//               (L2-resident) or a 64 MB (MALL-resident) buffer straight into
+//               LDS (global_load_lds), the step's tile fill: 16 KB per
+//               workgroup of 4 waves and 64 MFMA
 //   hbm read    a 4 GiB buffer streamed once with 16-byte loads (grid-stride,
 //               4 or 8 loads in flight per thread, 2048 or 8192 blocks), an xor
 //               of the words kept per thread
@@ -139,6 +147,90 @@ __global__ __launch_bounds__(256) void one_wave_probe(float* out, int iters) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+template <int EXP>
+__global__ __launch_bounds__(256) void mfma_lds_probe(float* out, int iters) {
+  constexpr int N = 512;                      // 16-byte operand chunks (8 KB)
+  __shared__ __attribute__((aligned(16))) bf16x8_t tile[N];
+  for (int i = threadIdx.x; i < N; i += 256) {
+    bf16x8_t t;
+    for (int e = 0; e < 8; ++e) t[e] = (__bf16)(i * 1e-3f + e);
+    tile[i] = t;
+  }
+  __syncthreads();
+  bf16x8_t a0, b;
+  operands(a0, b);
+  floatx16_t acc[4];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float x[16];
+  for (int e = 0; e < 16; ++e) x[e] = -(float)(threadIdx.x % 7) * 0.01f - e * 0.001f;
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // consecutive lanes, consecutive 16-byte chunks: conflict-free; index < N
+      const bf16x8_t a = tile[(lane + i * 64 + (it & 7) * 8) & (N - 1)];
+      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i & 3], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EXP; ++e) x[(i + e) % 16] = __builtin_amdgcn_exp2f(x[(i + e) % 16]) - 1.0f;
+    }
+  }
+  float s = (float)a0[0];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  for (int e = 0; e < 16; ++e) s += x[e];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__global__ __launch_bounds__(256) void mfma_lds_fill_probe(float* out, const uint4* src,
+                                                           int src16, int iters) {
+  constexpr int N = 512;                      // operand chunks (8 KB), read by the MFMAs
+  __shared__ __attribute__((aligned(16))) bf16x8_t tile[N];
+  __shared__ __attribute__((aligned(16))) char fill[4 * 1024];   // 1 KB per wave, rewritten
+  for (int i = threadIdx.x; i < N; i += 256) {
+    bf16x8_t t;
+    for (int e = 0; e < 8; ++e) t[e] = (__bf16)(i * 1e-3f + e);
+    tile[i] = t;
+  }
+  __syncthreads();
+  bf16x8_t a0, b;
+  operands(a0, b);
+  floatx16_t acc[4];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float x[16];
+  for (int e = 0; e < 16; ++e) x[e] = -(float)(threadIdx.x % 7) * 0.01f - e * 0.001f;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // src16 is a power of two; every index below is masked to it
+  int pos = ((blockIdx.x * 4 + w) * 256) & (src16 - 1);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ci = (pos + u * 64 + lane) & (src16 - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + ci), (lds_void_t*)(fill + w * 1024),
+                                       16, 0, 0);
+    }
+    pos = (pos + 256) & (src16 - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8_t a = tile[(lane + i * 64 + (it & 7) * 8) & (N - 1)];
+      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i & 3], 0, 0, 0);
+      x[i] = __builtin_amdgcn_exp2f(x[i]) - 1.0f;
+    }
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float s = (float)a0[0];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  for (int e = 0; e < 16; ++e) s += x[e];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // Streams n16 16-byte words: each thread keeps U loads in flight per trip.
 template <int U>
 __global__ __launch_bounds__(256) void hbm_read_probe(const uint4* __restrict__ src, size_t n16,
@@ -216,6 +308,32 @@ int main() {
   run("mfma 32x32x16 x4 + 16 exp2", mix_probe<16>, kBlocks, 4 * f32x32, "TFLOP/s");
   run("mfma 32x32x16 x4 + 32 exp2", mix_probe<32>, kBlocks, 4 * f32x32, "TFLOP/s");
   run("lds ds_read_b128", lds_probe, kBlocks, 8 * 16.0 * 64, "TB/s");
+  run("mfma + lds operand (1 KB per mfma)", mfma_lds_probe<0>, kBlocks, 16 * f32x32, "TFLOP/s");
+  run("mfma + lds operand + 1 exp2 per mfma", mfma_lds_probe<1>, kBlocks, 16 * f32x32, "TFLOP/s");
+  // the same mix plus the tile fill, from a 2 MB buffer (one XCD's L2 holds
+  // it) and from a 64 MB one (past the L2s, inside the 256 MB MALL)
+  for (const int mb : {2, 64}) {
+    const int src16 = (mb << 20) / 16;
+    uint4* src = nullptr;
+    CHECK(hipMalloc(&src, (size_t)src16 * 16));
+    CHECK(hipMemset(src, 0, (size_t)src16 * 16));
+    hipLaunchKernelGGL(mfma_lds_fill_probe, dim3(kBlocks), dim3(256), 0, 0, out, src, src16, 100);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(mfma_lds_fill_probe, dim3(kBlocks), dim3(256), 0, 0, out, src, src16,
+                       kIters);
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    const double flops = kBlocks * 4.0 * kIters * 16 * f32x32;
+    const double fill_bytes = kBlocks * 4.0 * kIters * 4096;
+    std::printf("mfma + lds + exp2 + fill from %2d MB %9.3f ms  %9.1f %-8s %8.1f TB/s fill\n", mb,
+                ms, flops / (ms * 1e-3) / 1e12, "TFLOP/s", fill_bytes / (ms * 1e-3) / 1e12);
+    CHECK(hipFree(src));
+  }
   run("1 wave/SIMD: 8 mfma", one_wave_probe<8, 0>, 256, 8 * f32x32, "TFLOP/s");
   run("1 wave/SIMD: 16 exp2", one_wave_probe<0, 16>, 256, 0.0, "-");
   run("1 wave/SIMD: 8 mfma + 16 exp2", one_wave_probe<8, 16>, 256, 8 * f32x32, "TFLOP/s");
