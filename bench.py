@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -72,8 +73,15 @@ def parse():
 
 
 def src_hash(name):
-    with open(os.path.join(ROOT, "dynamic_block_sparse_sws_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of a kernel source's code: comments and whitespace are
+    removed first, so a comment edit does not invalidate counters taken on
+    the same code."""
+    with open(os.path.join(ROOT, "dynamic_block_sparse_sws_amd", "csrc", name)) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_for(kernel_src, launch_bytes_key):

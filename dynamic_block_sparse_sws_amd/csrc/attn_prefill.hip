@@ -27,9 +27,10 @@
 // every list); a partial last block is zero-padded.  Workgroups are ordered
 // longest list first, and the query heads of one KV head are mapped to the same
 // XCD (workgroup id modulo 8) so their shared K/V blocks meet in one L2.  For
-// B = 128 the register budget is capped so three waves share each SIMD (the
-// short 32-key steps keep the score registers small); the extra wave hides
-// more of the softmax and load latency behind other waves' MFMAs.
+// B = 128 and for the paired B = 64 form the register budget is capped so
+// three waves share each SIMD (the short 32-key steps keep the score registers
+// small); the extra wave hides more of the softmax and load latency behind
+// other waves' MFMAs.
 //
 // fp32 path: a plain kernel, one thread per query row, key-by-key online
 // softmax with K/V tiles staged in LDS; it exists for tight-tolerance checks.
