@@ -23,6 +23,11 @@
 //               (L2-resident) or a 64 MB (MALL-resident) buffer straight into
 //               LDS (global_load_lds), the step's tile fill: 16 KB per
 //               workgroup of 4 waves and 64 MFMA
+//   rand<E>     mfma+lds<E> with random operands: the LDS tile and eight
+//               per-lane B fragments (the step's Q fragments) hold hashed
+//               bf16 values of random sign and mantissa, so the multipliers
+//               toggle as they do on real data (the probes above repeat the
+//               same operands, which draws less power)
 //   hbm read    a 4 GiB buffer streamed once with 16-byte loads (grid-stride,
 //               4 or 8 loads in flight per thread, 2048 or 8192 blocks), an xor
 //               of the words kept per thread
@@ -182,6 +187,55 @@ __global__ __launch_bounds__(256) void mfma_lds_probe(float* out, int iters) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// A bf16 of random sign and mantissa and magnitude in [0.25, 4) from a
+// 32-bit integer hash of i (the "lowbias32" mixer).
+__device__ __forceinline__ __bf16 random_bf16(uint32_t i) {
+  i ^= i >> 16;
+  i *= 0x7feb352du;
+  i ^= i >> 15;
+  i *= 0x846ca68bu;
+  i ^= i >> 16;
+  const uint16_t bits = (uint16_t)(((i >> 31) << 15) | ((125u + ((i >> 20) & 3u)) << 7) | (i & 0x7fu));
+  return __builtin_bit_cast(__bf16, bits);
+}
+
+template <int EXP>
+__global__ __launch_bounds__(256) void mfma_rand_probe(float* out, int iters) {
+  constexpr int N = 512;                      // 16-byte operand chunks (8 KB)
+  __shared__ __attribute__((aligned(16))) bf16x8_t tile[N];
+  for (int i = threadIdx.x; i < N; i += 256) {
+    bf16x8_t t;
+    for (int e = 0; e < 8; ++e) t[e] = random_bf16((blockIdx.x * N + i) * 8 + e);
+    tile[i] = t;
+  }
+  __syncthreads();
+  bf16x8_t b[8];
+  for (int f = 0; f < 8; ++f)
+    for (int e = 0; e < 8; ++e)
+      b[f][e] = random_bf16(0x9e3779b9u ^ (((blockIdx.x * 256 + threadIdx.x) * 8 + f) * 8 + e));
+  floatx16_t acc[4];
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float x[16];
+  for (int e = 0; e < 16; ++e) x[e] = -(float)(threadIdx.x % 7) * 0.01f - e * 0.001f;
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // consecutive lanes, consecutive 16-byte chunks: conflict-free; index < N
+      const bf16x8_t a = tile[(lane + i * 64 + (it & 7) * 8) & (N - 1)];
+      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[i & 7], acc[i & 3], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EXP; ++e) x[(i + e) % 16] = __builtin_amdgcn_exp2f(x[(i + e) % 16]) - 1.0f;
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) s += acc[i][r];
+  for (int e = 0; e < 16; ++e) s += x[e];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
@@ -310,6 +364,8 @@ int main() {
   run("lds ds_read_b128", lds_probe, kBlocks, 8 * 16.0 * 64, "TB/s");
   run("mfma + lds operand (1 KB per mfma)", mfma_lds_probe<0>, kBlocks, 16 * f32x32, "TFLOP/s");
   run("mfma + lds operand + 1 exp2 per mfma", mfma_lds_probe<1>, kBlocks, 16 * f32x32, "TFLOP/s");
+  run("random operands: mfma + lds", mfma_rand_probe<0>, kBlocks, 16 * f32x32, "TFLOP/s");
+  run("random operands: + 1 exp2 per mfma", mfma_rand_probe<1>, kBlocks, 16 * f32x32, "TFLOP/s");
   // the same mix plus the tile fill, from a 2 MB buffer (one XCD's L2 holds
   // it) and from a 64 MB one (past the L2s, inside the 256 MB MALL)
   for (const int mb : {2, 64}) {
