@@ -119,6 +119,7 @@ __device__ __forceinline__ int row_swizzle(int row) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 // max(v, v of the lane 32 away): v_permlane32_swap exchanges the two halves
 // of the wave in registers (no LDS round trip); the larger of the swapped pair
@@ -151,7 +152,7 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
                                           const int (&k_rd)[D / 16],
                                           const int (&v_rd)[PrefillTile<D, BLK>::KT / 16],
                                           floatx16_t (&o)[D / 32], float& m_run, float& l_run,
-                                          int qi, int hl) {
+                                          int& ref_mode, int qi, int hl) {
   constexpr int KT = PrefillTile<D, BLK>::KT;
   // ---- S^T = K Q^T ----
   floatx16_t st[KT / 32];
@@ -187,9 +188,11 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
       }
   }
   // ---- P = exp2(S * scale - m), bf16; row sum from the same bf16 values ----
-  // (the first step of a query block takes the column maximum)
+  // (the first step of a query block takes the column maximum).  ref_mode is
+  // wave-uniform: 0 before the first step, 1 when every column of the wave has
+  // reference 0, 2 otherwise.
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8_t pb[KT / 16];
+  u32x4_t pw[KT / 16];
   auto exp_step = [&](float& l_acc, auto zero_ref) {
 #pragma unroll
     for (int kc = 0; kc < KT / 16; ++kc) {
@@ -197,28 +200,23 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
       const int r0 = (kc & 1) * 8;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        bf16x2_t pr;
-        if constexpr (decltype(zero_ref)::value) {
-          pr[0] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e]);
-          pr[1] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e + 1]);
-        } else {
-          pr[0] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e] - m_run);
-          pr[1] = (__bf16)__builtin_amdgcn_exp2f(st[kt][r0 + e + 1] - m_run);
+        float x0 = st[kt][r0 + e], x1 = st[kt][r0 + e + 1];
+        if constexpr (!decltype(zero_ref)::value) {
+          x0 -= m_run;
+          x1 -= m_run;
         }
+        const float2_t ex = {__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1)};
+        const bf16x2_t pr = __builtin_convertvector(ex, bf16x2_t);
         l_acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_acc, false);
-        pb[kc][e] = pr[0];
-        pb[kc][e + 1] = pr[1];
+        pw[kc][e >> 1] = __builtin_bit_cast(uint32_t, pr);
       }
     }
   };
-  auto exp_any = [&](float& l_acc) {
-    if (__all(m_run == 0.f)) exp_step(l_acc, std::true_type{});
-    else exp_step(l_acc, std::false_type{});
-  };
   float l_new = l_run;
-  bool redo = m_run == -INFINITY;
+  bool redo = ref_mode == 0;
   if (!redo) {
-    exp_any(l_new);
+    if (ref_mode == 1) exp_step(l_new, std::true_type{});
+    else exp_step(l_new, std::false_type{});
     redo = __any(!(l_new < kSumLimit));
   }
   if (redo) {
@@ -231,17 +229,19 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
     // a query block's first step takes the reference 0 when its maximum is
     // within +-64 (no subtraction in the later steps' exponentials), else the
     // maximum itself
-    const float m_new = m_run == -INFINITY ? (fabsf(mx) <= kZeroRefRange ? 0.f : mx)
-                                           : fmaxf(m_run, mx);
-    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = ref_mode == 0 ? (fabsf(mx) <= kZeroRefRange ? 0.f : mx)
+                                      : fmaxf(m_run, mx);
+    const float alpha = ref_mode == 0 ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     m_run = m_new;
+    ref_mode = __all(m_run == 0.f) ? 1 : 2;
     l_new = l_run;
-    exp_any(l_new);
+    if (ref_mode == 1) exp_step(l_new, std::true_type{});
+    else exp_step(l_new, std::false_type{});
   }
   l_run = l_new;
   // ---- O^T += V^T P^T ----
@@ -253,7 +253,8 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
       a[dt] = *reinterpret_cast<const bf16x8_t*>(vsb + v_rd[kc] + dt * 32 * KT * 2);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], pb[kc], o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], __builtin_bit_cast(bf16x8_t, pw[kc]),
+                                                      o[dt], 0, 0, 0);
   }
 }
 
@@ -335,7 +336,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   // wave w writes the 16 bytes at chunk u * NT + 64 w + l, so the XOR swizzle
   // of the LDS layout is applied to the global source column instead.
   int k_roff[TL::LOADS], k_col[TL::LOADS];
-  uint32_t v_off[TL::LOADS];
+  uint32_t k_off[TL::LOADS], v_off[TL::LOADS];
 #pragma unroll
   for (int u = 0; u < TL::LOADS; ++u) {
     const int qc = u * NT + tid;
@@ -343,9 +344,10 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     const int kp = qc % TL::KCH;
     k_roff[u] = kr * (int)kstride;
     k_col[u] = (kp ^ row_swizzle<TL::KCH>(kr)) * 8;
+    k_off[u] = (uint32_t)(k_roff[u] + k_col[u]) * 2u;
     const int vr = qc / TL::VCH;
     const int vp = qc % TL::VCH;
-    v_off[u] = (uint32_t)(vr * BLK + (vp ^ row_swizzle<TL::VCH>(vr)) * 8);
+    v_off[u] = (uint32_t)(vr * BLK + (vp ^ row_swizzle<TL::VCH>(vr)) * 8) * 2u;
   }
   const uint16_t* kbase = k + (int64_t)tok0 * kstride + (int64_t)kvh * D;
   const uint16_t* vtbase = vt + ((int64_t)kvh * total_blocks + blk0) * D * BLK;
@@ -357,26 +359,46 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   // Rows past the end of the sequence (only in the last, partial block, which
   // only its own query block selects, as its diagonal) re-read the last row:
   // the causal mask removes those keys and their V^T is zero.
+  // Full blocks and every V^T tile load through raw buffer resources (stride
+  // 0, the last word selecting 32-bit data as untyped loads require): a
+  // scalar base per step plus a 32-bit per-lane offset fixed for the whole
+  // kernel, so a step's loads cost no vector address arithmetic.  (The
+  // offsets are passed as converted values: given the captured array element
+  // itself, the host pass of this compiler silently drops the kernel's
+  // launch stub.)
   auto load_step = [&](int j, int sub, char* kd, char* vd) {
-    // offsets from the block's first row: block j holds at least one token,
-    // so the clamp row n - 1 - j * BLK is >= 0 and every offset is
-    // non-negative (a sub-step of a partial block may start past the end)
-    const uint16_t* ks = kbase + (int64_t)j * BLK * kstride;
     const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
-    // (the row distance is clamped to the block first: every offset below is
-    // under BLK rows anyway, and the product stays in 32 bits at any length)
-    const int last_off = min(n - 1 - j * BLK, BLK - 1) * (int)kstride;
-    const int sub_off = sub * KT * (int)kstride;
+    if ((j + 1) * BLK <= n) {
+      const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(kbase + ((int64_t)j * BLK + sub * KT) * kstride), (short)0,
+          (int)(KT * kstride * 2), 0x00020000);
 #pragma unroll
-    for (int u = 0; u < TL::LOADS; ++u) {
-      // 32-bit byte offsets from a uniform base (scalar base + vector offset)
-      const uint32_t kb = (uint32_t)(min(sub_off + k_roff[u], last_off) + k_col[u]) * 2u;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const char*>(ks) + kb),
-                                       (lds_void_t*)(kd + u * NT * 16 + wave_chunk), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (glb_void_t*)(reinterpret_cast<const char*>(vs) + v_off[u] * 2u),
-          (lds_void_t*)(vd + u * NT * 16 + wave_chunk), 16, 0, 0);
+      for (int u = 0; u < TL::LOADS; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(kd + u * NT * 16 + wave_chunk),
+                                                 16, (int)k_off[u], 0, 0, 0);
+    } else {
+      // partial block: offsets from the block's first row, clamped to the
+      // last row of the sequence.  Block j holds at least one token, so the
+      // clamp row n - 1 - j * BLK is >= 0 and every offset is non-negative
+      // (a sub-step may start past the end); the row distance is clamped to
+      // the block first, so the product stays in 32 bits at any length.
+      const char* kblk = reinterpret_cast<const char*>(kbase + (int64_t)j * BLK * kstride);
+      const int last_off = min(n - 1 - j * BLK, BLK - 1) * (int)kstride;
+      const int sub_off = sub * KT * (int)kstride;
+#pragma unroll
+      for (int u = 0; u < TL::LOADS; ++u) {
+        const uint32_t kb = (uint32_t)(min(sub_off + k_roff[u], last_off) + k_col[u]) * 2u;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kblk + kb),
+                                         (lds_void_t*)(kd + u * NT * 16 + wave_chunk), 16, 0, 0);
+      }
     }
+    // the step's V^T tile: D rows of KT keys inside the block's D x BLK tile
+    const auto vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vs), (short)0,
+                                                      D * BLK * 2, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < TL::LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vd + u * NT * 16 + wave_chunk), 16,
+                                               (int)v_off[u], 0, 0, 0);
   };
   // A step's tiles are complete for the workgroup once every wave has waited
   // for its own loads and passed the barrier.
@@ -401,6 +423,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY;
   float l_run = 0.f;
+  int ref_mode = 0;
 
   // List entries are clamped to the causal blocks [0, i] and the count to
   // [0, min(width, i + 1)], so a malformed list gives a wrong answer, never a
@@ -433,7 +456,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
         if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
         else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
         attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd, o,
-                          m_run, l_run, qi, hl);
+                          m_run, l_run, ref_mode, qi, hl);
         step_barrier();
       }
       j = j_next;
@@ -477,7 +500,7 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
         else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
         if (mine)
           attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd,
-                            o, m_run, l_run, qi, hl);
+                            o, m_run, l_run, ref_mode, qi, hl);
         step_barrier();
       }
       j = j_next;
