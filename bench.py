@@ -1096,7 +1096,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre["attn_exec_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": attn_bytes,
-                     "kernel": "attn_prefill_bf16_kernel<128,128>",
+                     "kernel": "attn_prefill_bf16_kernel<128, 128, 1>",
                      "flops_per_launch": pre["attn_flops_per_launch"],
                      "avg_launch_ms": round(pre["attn_ms"], 4),
                      "target_frac": TARGET_PREFILL_MFMA_FRAC,

@@ -121,13 +121,13 @@ __device__ __forceinline__ int row_swizzle(int row) {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-// max(v, v of the lane 32 away): v_permlane32_swap exchanges the two halves
-// of the wave in registers (no LDS round trip); the larger of the swapped pair
-// is the answer in either half.
+// max(v, v of the lane 32 away): a lane's 16 scores and its partner's are the
+// two halves of one query column.  (A lane shuffle, not v_permlane32_swap:
+// given the same register as both operands this compiler folds the swap's
+// two results into one, which drops the other half.)  Only a query block's
+// first step and the rare rescale take it.
 __device__ __forceinline__ float max_halves(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
-                                                  __builtin_bit_cast(unsigned, v), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  return fmaxf(v, __shfl_xor(v, 32));
 }
 
 // Softmax reference: after the first step of a query block the reference m
@@ -169,13 +169,14 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
       st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dc], qf[dc], st[0], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // three operand reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-    for (int dc = 0; dc < D / 16 - 2; ++dc) {
+    for (int dc = 0; dc < D / 16 - 3; ++dc) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   }
   // ---- causal mask (diagonal block only) ----
   if (diag) {
@@ -245,16 +246,27 @@ __device__ __forceinline__ void attn_step(bool diag, const char* ksb, const char
   }
   l_run = l_new;
   // ---- O^T += V^T P^T ----
+  {
+    bf16x8_t a[KT / 16][D / 32];
 #pragma unroll
-  for (int kc = 0; kc < KT / 16; ++kc) {
-    bf16x8_t a[D / 32];
+    for (int kc = 0; kc < KT / 16; ++kc)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      a[dt] = *reinterpret_cast<const bf16x8_t*>(vsb + v_rd[kc] + dt * 32 * KT * 2);
+      for (int dt = 0; dt < D / 32; ++dt)
+        a[kc][dt] = *reinterpret_cast<const bf16x8_t*>(vsb + v_rd[kc] + dt * 32 * KT * 2);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], __builtin_bit_cast(bf16x8_t, pw[kc]),
-                                                      o[dt], 0, 0, 0);
+    for (int kc = 0; kc < KT / 16; ++kc)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a[kc][dt], __builtin_bit_cast(bf16x8_t, pw[kc]), o[dt], 0, 0, 0);
+    // three operand reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int i = 0; i < 8 - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   }
 }
 

@@ -333,3 +333,60 @@ def test_head_pairing_equals_one_head_form(hq):
         torch.cuda.synchronize()
         assert torch.equal(out1[:, 0], out[:, h]), h
         assert torch.equal(lse1[0], lse[h]), h
+
+
+@pytest.mark.parametrize("B,hq,hkv,jump", [(128, 4, 2, 1), (128, 4, 2, 0), (64, 4, 2, 1),
+                                           (64, 2, 2, 0)])
+def test_prefill_softmax_reference_and_rescale(B, hq, hkv, jump):
+    """The bf16 prefill fixes each query's softmax reference after its first
+    32-key step (0 when that step's maximum is within +-64 in log2 units, else
+    the maximum) and rescales the running state only when the running sum
+    nears 2^100.  Here scale * log2(e) = 1/8, so the kernel's bf16 pre-scaled Q
+    is exactly Q / 8 and the scores are exact up to fp32 accumulation.  KV
+    head 0's key magnitudes start small (reference 0) and grow along the
+    sequence until single scores pass 100 (repeated rescales); KV head 1's
+    scores pass 64 in the first step (a nonzero reference) and grow past it by
+    far more than 2^128 (an overflowing step).  Inside every 32-key step one
+    16-key half is 1.5x larger (`jump` picks which), so the first overflow of a
+    step can come in either half.  Dense lists on one ragged sequence; every
+    query block against the oracle's exact softmax."""
+    d = 128
+    n = 5 * B + 17
+    geo = sws.Geometry([n], B)
+    scale = 0.125 * np.log(2.0)                     # scale * log2(e) = 1/8
+    pos = torch.arange(n, dtype=torch.float32, device="cuda")
+    half = ((pos.long() % 32) // 16) == jump
+    mag0 = (0.5 + 30.0 * (pos / n) ** 2) * torch.where(half, 1.5, 1.0)
+    mag1 = (60.0 + 60.0 * pos / n) * torch.where(half, 1.5, 1.0)
+    mags = torch.stack([mag0, mag1], 1)[:, :hkv]
+    q = _rand((n, hq, d), 51).to(torch.bfloat16)
+    k = (_rand((n, hkv, d), 52) * mags[:, :, None]).to(torch.bfloat16)
+    v = _rand((n, hkv, d), 53).to(torch.bfloat16)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    out = sws.sparse_attn_prefill(q, k, v, geo, None, None, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    Q, K, V, Og, Lg = f64(q), f64(k), f64(v), f64(out), f64(lse)
+    G = hq // hkv
+    b = geo.blocks[0]
+    lists = [np.arange(i + 1) for i in range(b)]
+    worst = 0.0
+    for h in range(hq):
+        g = h // G
+        # the inputs reach the paths named above (scores in log2 units)
+        s2 = (Q[:, h] / 8.0) @ K[:, g].T
+        first = s2[32:, :32].max(axis=1)           # first-step maxima of queries 32..
+        late = np.tril(s2).max()
+        if g == 0:
+            assert np.abs(first).max() < 64 and late > 110, (first, late)
+        else:
+            assert first.min() > 64 and late - first.max() > 128, (first.min(), late)
+        res = O.sparse_attention_rows(Q[:, h], K[:, g], V[:, g], lists, B, scale, range(b))
+        for i in range(b):
+            o_want, lse_want = res[i]
+            a = i * B
+            e = float(np.abs(Og[a:a + o_want.shape[0], h] - o_want).max())
+            e2 = float(np.abs(Lg[h, a:a + o_want.shape[0]] - lse_want).max())
+            worst = max(worst, e)
+            assert e <= TOL_ATTN_BF16, (h, i, "attn", e)
+            assert e2 <= TOL_ATTN_BF16, (h, i, "lse", e2)
+    _print("softmax paths", B, hq, hkv, jump, "worst", worst)
