@@ -682,3 +682,63 @@ def test_decode_snapshot_resume_bit_identical():
         for a_l, b_l in zip(a_t, b_t):
             for x, y in zip(a_l, b_l):
                 assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype,d,B,hq,hkv,lens", [
+    ("bf16", 128, 64, 8, 2, (1000, 2049, 64)),
+    ("bf16", 128, 128, 4, 4, (700, 1, 1280)),
+    ("f32", 64, 64, 4, 2, (1000, 333)),
+])
+def test_decode_large_scores_across_splits(dtype, d, B, hq, hkv, lens):
+    """Decode attention when the scores are far outside the usual range: key
+    magnitudes grow along the context so single scores pass 2^128 above the
+    first keys' (in log2 units), with a 1.5x jump in one 16-key half of every
+    32 keys, for KV head 0; KV head 1 starts above 64 and grows.  The split
+    workgroups' partial states and the combine's rescaling must still give
+    the exact softmax: every (sequence, head) against the oracle, dense
+    lists.  scale * log2(e) = 1/8, so the scores are exact up to fp32
+    accumulation."""
+    ns = len(lens)
+    max_ctx = max(lens)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(gen.seed_for(16, d, B, hq))
+    pos = torch.arange(max_ctx, dtype=torch.float32, device="cuda")
+    half = ((pos.long() % 32) // 16) == 1
+    mag0 = (0.5 + 45.0 * (pos / max_ctx) ** 2) * torch.where(half, 1.5, 1.0)
+    mag1 = (60.0 + 60.0 * pos / max_ctx) * torch.where(half, 1.5, 1.0)
+    # (scaled by 128 / d so the score range does not shrink with d)
+    mags = torch.stack([mag0, mag1] + [mag0] * max(0, hkv - 2), 1)[:, :hkv] * (128.0 / d)
+    kc = (torch.randn((ns, max_ctx, hkv, d), generator=g, device="cuda") * mags[None, :, :, None]).to(tdt)
+    vc = torch.randn((ns, max_ctx, hkv, d), generator=g, device="cuda").to(tdt)
+    q = torch.randn((ns, hq, d), generator=g, device="cuda").to(tdt)
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scale = 0.125 * math.log(2.0)
+    lse = torch.empty((ns, hq), dtype=torch.float32, device="cuda")
+    out = sws.sparse_attn_decode(q, kc, vc, ctx, B, None, None, None, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    Q, K, V, Og, Lg = f64(q), f64(kc), f64(vc), f64(out), f64(lse)
+    # fp32: scores in the hundreds carry fp32 rounding of about 1e-5 (natural
+    # units), a relative error of that size in every weight; 1e-3 still
+    # rejects any wrong rescale (an O(1) error)
+    tol = TOL_ATTN_BF16 if dtype == "bf16" else 1e-3
+    grp = hq // hkv
+    worst = 0.0
+    for s, n in enumerate(lens):
+        for h in range(hq):
+            gg = h // grp
+            nb = -(-n // B)
+            o_want, lse_want = O.query_attention(Q[s, h], K[s, :, gg], V[s, :, gg],
+                                                 np.arange(nb), B, n - 1, scale)
+            assert np.isfinite(Og[s, h]).all(), (s, h)
+            e = float(np.abs(Og[s, h] - o_want).max())
+            # the log-sum-exp is large here (hundreds); fp32 keeps it to ~1e-5 relative
+            e2 = abs(Lg[s, h] - lse_want)
+            worst = max(worst, e)
+            assert e <= tol, (s, h, e)
+            assert e2 <= max(tol, 1e-5 * abs(lse_want)), (s, h, e2, lse_want)
+    # the inputs do reach scores far apart within one context (log2 units)
+    sl = int(np.argmax(lens))
+    s2 = (Q[sl, 0] / 8.0) @ K[sl, :lens[sl], 0].T
+    assert s2.max() - np.abs(s2[:32]).max() > 128
+    _print("decode large scores", dtype, d, B, hq, hkv, lens, "worst", worst)
