@@ -8,10 +8,11 @@
 // walking the merge of the two heads' lists so a block both selected is
 // loaded once.  A pre-pass writes V transposed per
 // block (keys in accumulator-row order) to a workspace.  The selected key
-// blocks are walked in steps of 32 keys: the K and V^T tiles of the next step
-// stream from memory straight into the other half of a double-buffered,
-// XOR-swizzled LDS tile pair while the current step computes (one barrier per
-// step).  Each wave runs a FlashAttention-style
+// blocks are walked in steps of 32 keys: the K and V^T tiles stream from
+// memory straight into XOR-swizzled LDS tiles while earlier steps compute
+// (one barrier per step), two steps ahead through a ring of three tile pairs
+// in the one-head form, one step ahead through two pairs in the paired form.
+// Each wave runs a FlashAttention-style
 // step on the matrix cores with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T          (A = K rows from LDS, B = this wave's Q in registers)
 //   online softmax       (Q is pre-scaled by scale * log2(e), so scores are
@@ -292,6 +293,10 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   __shared__ __attribute__((aligned(16))) char Ks1[TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs0[TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs1[TL::TILE];
+  // the one-head form keeps a ring of three buffer pairs (tiles two steps
+  // ahead); the paired form alternates two
+  __shared__ __attribute__((aligned(16))) char Ks2[HP == 1 ? TL::TILE : 16];
+  __shared__ __attribute__((aligned(16))) char Vs2[HP == 1 ? TL::TILE : 16];
 
   // Workgroup -> (query head(s), query block).  HP = 2 pairs query heads
   // 2p and 2p + 1 of one KV group (the last pair of an odd group holds one
@@ -347,16 +352,13 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   // The tiles go global -> LDS directly (global_load_lds_dwordx4): lane l of
   // wave w writes the 16 bytes at chunk u * NT + 64 w + l, so the XOR swizzle
   // of the LDS layout is applied to the global source column instead.
-  int k_roff[TL::LOADS], k_col[TL::LOADS];
   uint32_t k_off[TL::LOADS], v_off[TL::LOADS];
 #pragma unroll
   for (int u = 0; u < TL::LOADS; ++u) {
     const int qc = u * NT + tid;
     const int kr = qc / TL::KCH;
     const int kp = qc % TL::KCH;
-    k_roff[u] = kr * (int)kstride;
-    k_col[u] = (kp ^ row_swizzle<TL::KCH>(kr)) * 8;
-    k_off[u] = (uint32_t)(k_roff[u] + k_col[u]) * 2u;
+    k_off[u] = (uint32_t)(kr * (int)kstride + (kp ^ row_swizzle<TL::KCH>(kr)) * 8) * 2u;
     const int vr = qc / TL::VCH;
     const int vp = qc % TL::VCH;
     v_off[u] = (uint32_t)(vr * BLK + (vp ^ row_swizzle<TL::VCH>(vr)) * 8) * 2u;
@@ -366,45 +368,30 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   const int wave_chunk = __builtin_amdgcn_readfirstlane(w) * 64 * 16;
 
   typedef __attribute__((address_space(3))) void lds_void_t;
-  typedef __attribute__((address_space(1))) void glb_void_t;
-  // Issue the loads of step `sub` of block j into LDS buffer pair (kd, vd).
-  // Rows past the end of the sequence (only in the last, partial block, which
-  // only its own query block selects, as its diagonal) re-read the last row:
-  // the causal mask removes those keys and their V^T is zero.
-  // Full blocks and every V^T tile load through raw buffer resources (stride
-  // 0, the last word selecting 32-bit data as untyped loads require): a
-  // scalar base per step plus a 32-bit per-lane offset fixed for the whole
-  // kernel, so a step's loads cost no vector address arithmetic.  (The
-  // offsets are passed as converted values: given the captured array element
-  // itself, the host pass of this compiler silently drops the kernel's
-  // launch stub.)
+  // Issue the loads of step `sub` of block j into LDS buffer pair (kd, vd),
+  // through raw buffer resources (stride 0, the last word selecting 32-bit
+  // data as untyped loads require): a scalar base per step plus a 32-bit
+  // per-lane offset fixed for the whole kernel, so a step's loads cost no
+  // vector address arithmetic.  The K resource covers only the step's rows
+  // inside the sequence: rows past its end (only in the last, partial block,
+  // which only its own query block selects, as its diagonal) read as zero,
+  // and the causal mask removes those keys (their V^T is zero too).  (The
+  // offsets are passed as converted values: given the captured array
+  // element itself, the host pass of this compiler silently drops the
+  // kernel's launch stub.)
   auto load_step = [&](int j, int sub, char* kd, char* vd) {
-    const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
-    if ((j + 1) * BLK <= n) {
-      const auto kr = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(kbase + ((int64_t)j * BLK + sub * KT) * kstride), (short)0,
-          (int)(KT * kstride * 2), 0x00020000);
+    const int row0 = j * BLK + sub * KT;
+    // (uniform: said explicitly, or the resource is built per lane in a loop)
+    const int valid = __builtin_amdgcn_readfirstlane(min(max(n - row0, 0), KT));
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbase + (int64_t)row0 * kstride), (short)0,
+        (int)(valid * kstride * 2), 0x00020000);
 #pragma unroll
-      for (int u = 0; u < TL::LOADS; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(kd + u * NT * 16 + wave_chunk),
-                                                 16, (int)k_off[u], 0, 0, 0);
-    } else {
-      // partial block: offsets from the block's first row, clamped to the
-      // last row of the sequence.  Block j holds at least one token, so the
-      // clamp row n - 1 - j * BLK is >= 0 and every offset is non-negative
-      // (a sub-step may start past the end); the row distance is clamped to
-      // the block first, so the product stays in 32 bits at any length.
-      const char* kblk = reinterpret_cast<const char*>(kbase + (int64_t)j * BLK * kstride);
-      const int last_off = min(n - 1 - j * BLK, BLK - 1) * (int)kstride;
-      const int sub_off = sub * KT * (int)kstride;
-#pragma unroll
-      for (int u = 0; u < TL::LOADS; ++u) {
-        const uint32_t kb = (uint32_t)(min(sub_off + k_roff[u], last_off) + k_col[u]) * 2u;
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(kblk + kb),
-                                         (lds_void_t*)(kd + u * NT * 16 + wave_chunk), 16, 0, 0);
-      }
-    }
+    for (int u = 0; u < TL::LOADS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(kd + u * NT * 16 + wave_chunk), 16,
+                                               (int)k_off[u], 0, 0, 0);
     // the step's V^T tile: D rows of KT keys inside the block's D x BLK tile
+    const uint16_t* vs = vtbase + (int64_t)j * D * BLK + sub * KT;
     const auto vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vs), (short)0,
                                                       D * BLK * 2, 0x00020000);
 #pragma unroll
@@ -450,29 +437,50 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   if constexpr (HP == 1) {
     const int nb = list_len(h);
     const int32_t* lst = list_of(h);
-    auto entry = [&](int nn) { return lst ? min(max(lst[nn], 0), i) : nn; };
-
-    // Step sub of a block uses LDS buffer pair sub % 2; while it computes, the
-    // next step (the block's next sub-step, or the first of the next block)
-    // streams into the other pair.
-    int j = entry(0);
-    load_step(j, 0, Ks0, Vs0);
-    step_barrier();
-    for (int nn = 0; nn < nb; ++nn) {
-      const bool has_next = nn + 1 < nb;
-      const int j_next = has_next ? entry(nn + 1) : j;
-#pragma unroll
-      for (int sub = 0; sub < TL::NSUB; ++sub) {
-        const bool odd = sub & 1;
-        const bool last_sub = sub + 1 == TL::NSUB;
-        if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
-        else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
-        attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd, o,
-                          m_run, l_run, ref_mode, qi, hl);
-        step_barrier();
-      }
-      j = j_next;
+    // list entries through the scalar cache: a vector-memory read here would
+    // wait for every tile load in flight
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    auto entry = [&](int nn) {
+      return lst ? min(max(((const_i32*)lst)[nn], 0), i) : nn;
+    };
+    constexpr int NS = TL::NSUB;
+    constexpr int LPS = 2 * TL::LOADS;           // vector-memory loads per step per thread
+    const int nsteps = nb * NS;                  // step t: block entry(t / NS), keys (t % NS) KT..
+    auto issue = [&](int t, char* kd, char* vd) { load_step(entry(t / NS), t % NS, kd, vd); };
+    // Step t + 1's tiles are complete for the workgroup once every wave has
+    // waited for its own loads of them (leaving step t + 2's in flight) and
+    // passed the barrier.
+    // (s_waitcnt through the builtin, so the compiler's own wait placement
+    // knows which tile loads have completed; the immediate is vmcnt(n) with
+    // the other counters left open: expcnt 7, lgkmcnt 15)
+    auto wait_next = [&](bool ahead) {
+      static_assert(LPS < 16, "vmcnt in the low bits");
+      if (ahead) __builtin_amdgcn_s_waitcnt(0xF70 | LPS);
+      else __builtin_amdgcn_s_waitcnt(0xF70);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // Step t computes from buffer pair t % 3 while the tiles of step t + 2
+    // stream into pair (t + 2) % 3, the one step t - 1 used.
+    // (the last two steps issue the final step's tiles again, into the pair
+    // no later step reads, so every step issues the same loads)
+    auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
+      issue(min(t + 2, nsteps - 1), kn, vn);
+      attn_step<D, BLK>(entry(t / NS) == i, kc, vc, (t % NS) * KT, qf, k_rd, v_rd, o, m_run,
+                        l_run, ref_mode, qi, hl);
+      wait_next(true);
+    };
+    if (nsteps > 0) {
+      issue(0, Ks0, Vs0);
+      issue(1, Ks1, Vs1);                        // every block has NS >= 2 steps
+      wait_next(true);
     }
+    for (int t = 0; t < nsteps; t += 3) {
+      step(t, Ks0, Vs0, Ks2, Vs2);
+      if (t + 1 < nsteps) step(t + 1, Ks1, Vs1, Ks0, Vs0);
+      if (t + 2 < nsteps) step(t + 2, Ks2, Vs2, Ks1, Vs1);
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);           // no tile load outlives the loop
   } else {
     // The merge of the heads' ascending lists: each merged block carries a
     // mask of the heads that selected it; a wave computes a step only if its
