@@ -9,9 +9,8 @@
 // loaded once.  A pre-pass writes V transposed per
 // block (keys in accumulator-row order) to a workspace.  The selected key
 // blocks are walked in steps of 32 keys: the K and V^T tiles stream from
-// memory straight into XOR-swizzled LDS tiles while earlier steps compute
-// (one barrier per step), two steps ahead through a ring of three tile pairs
-// in the one-head form, one step ahead through two pairs in the paired form.
+// memory straight into XOR-swizzled LDS tiles two steps ahead, through a ring
+// of three tile pairs (one barrier per step).
 // Each wave runs a FlashAttention-style
 // step on the matrix cores with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T          (A = K rows from LDS, B = this wave's Q in registers)
@@ -293,10 +292,10 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
   __shared__ __attribute__((aligned(16))) char Ks1[TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs0[TL::TILE];
   __shared__ __attribute__((aligned(16))) char Vs1[TL::TILE];
-  // the one-head form keeps a ring of three buffer pairs (tiles two steps
-  // ahead); the paired form alternates two
-  __shared__ __attribute__((aligned(16))) char Ks2[HP == 1 ? TL::TILE : 16];
-  __shared__ __attribute__((aligned(16))) char Vs2[HP == 1 ? TL::TILE : 16];
+  // a ring of three buffer pairs: the tiles of step t + 2 load while step t
+  // computes
+  __shared__ __attribute__((aligned(16))) char Ks2[TL::TILE];
+  __shared__ __attribute__((aligned(16))) char Vs2[TL::TILE];
 
   // Workgroup -> (query head(s), query block).  HP = 2 pairs query heads
   // 2p and 2p + 1 of one KV group (the last pair of an odd group holds one
@@ -399,13 +398,6 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vd + u * NT * 16 + wave_chunk), 16,
                                                (int)v_off[u], 0, 0, 0);
   };
-  // A step's tiles are complete for the workgroup once every wave has waited
-  // for its own loads and passed the barrier.
-  auto step_barrier = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
   // ---- per-lane LDS read offsets (bytes) of the MFMA A operands ----
   const int ksw = row_swizzle<TL::KCH>(l32);
   const int vsw = row_swizzle<TL::VCH>(l32);
@@ -434,32 +426,31 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     return idx ? idx + ((int64_t)hh * total_blocks + gb) * width : nullptr;
   };
 
+  // List entries come through the scalar cache: a vector-memory read would
+  // wait for every tile load in flight.
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  constexpr int NS = TL::NSUB;
+  constexpr int LPS = 2 * TL::LOADS;             // vector-memory loads per step per thread
+  // Step t + 1's tiles are complete for the workgroup once every wave has
+  // waited for its own loads of them (leaving step t + 2's in flight) and
+  // passed the barrier.  (s_waitcnt through the builtin, so the compiler's
+  // own wait placement knows which tile loads have completed; the immediate
+  // is vmcnt(LPS) with the other counters left open: expcnt 7, lgkmcnt 15.)
+  auto wait_next = [&]() {
+    static_assert(LPS < 16, "vmcnt in the low bits");
+    __builtin_amdgcn_s_waitcnt(0xF70 | LPS);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   if constexpr (HP == 1) {
     const int nb = list_len(h);
     const int32_t* lst = list_of(h);
-    // list entries through the scalar cache: a vector-memory read here would
-    // wait for every tile load in flight
-    typedef __attribute__((address_space(4))) const int32_t const_i32;
     auto entry = [&](int nn) {
       return lst ? min(max(((const_i32*)lst)[nn], 0), i) : nn;
     };
-    constexpr int NS = TL::NSUB;
-    constexpr int LPS = 2 * TL::LOADS;           // vector-memory loads per step per thread
     const int nsteps = nb * NS;                  // step t: block entry(t / NS), keys (t % NS) KT..
     auto issue = [&](int t, char* kd, char* vd) { load_step(entry(t / NS), t % NS, kd, vd); };
-    // Step t + 1's tiles are complete for the workgroup once every wave has
-    // waited for its own loads of them (leaving step t + 2's in flight) and
-    // passed the barrier.
-    // (s_waitcnt through the builtin, so the compiler's own wait placement
-    // knows which tile loads have completed; the immediate is vmcnt(n) with
-    // the other counters left open: expcnt 7, lgkmcnt 15)
-    auto wait_next = [&](bool ahead) {
-      static_assert(LPS < 16, "vmcnt in the low bits");
-      if (ahead) __builtin_amdgcn_s_waitcnt(0xF70 | LPS);
-      else __builtin_amdgcn_s_waitcnt(0xF70);
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
     // Step t computes from buffer pair t % 3 while the tiles of step t + 2
     // stream into pair (t + 2) % 3, the one step t - 1 used.
     // (the last two steps issue the final step's tiles again, into the pair
@@ -468,12 +459,12 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
       issue(min(t + 2, nsteps - 1), kn, vn);
       attn_step<D, BLK>(entry(t / NS) == i, kc, vc, (t % NS) * KT, qf, k_rd, v_rd, o, m_run,
                         l_run, ref_mode, qi, hl);
-      wait_next(true);
+      wait_next();
     };
     if (nsteps > 0) {
       issue(0, Ks0, Vs0);
       issue(1, Ks1, Vs1);                        // every block has NS >= 2 steps
-      wait_next(true);
+      wait_next();
     }
     for (int t = 0; t < nsteps; t += 3) {
       step(t, Ks0, Vs0, Ks2, Vs2);
@@ -485,46 +476,59 @@ void attn_prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __
     // The merge of the heads' ascending lists: each merged block carries a
     // mask of the heads that selected it; a wave computes a step only if its
     // head's bit is set, and every wave takes part in the loads and barriers.
-    // Each merge step consumes at least one entry, so the walk ends after at
-    // most nbA + nbB blocks whatever the lists hold.
+    // Each merged block consumes at least one entry, so the walk ends after
+    // at most nbA + nbB blocks whatever the lists hold.
+    static_assert(NS == 2, "the paired form takes 64-token blocks: two steps per block");
     const int nbA = list_len(hfirst);
     const int nbB = nheads > 1 ? list_len(hfirst + 1) : 0;
     const int32_t* lA = list_of(hfirst);
     const int32_t* lB = nheads > 1 ? list_of(hfirst + 1) : nullptr;
     constexpr int kEnd = 0x7fffffff;
-    auto peek = [&](int pa, int pb, int& j, int& mask) {
-      const int a = pa < nbA ? (lA ? min(max(lA[pa], 0), i) : pa) : kEnd;
-      const int b = pb < nbB ? (lB ? min(max(lB[pb], 0), i) : pb) : kEnd;
-      j = min(a, b);
-      mask = (a == j ? 1 : 0) | (b == j ? 2 : 0);
+    int pa = 0, pb = 0;
+    // the next merged block (kEnd past the end) and its head mask
+    auto next_block = [&](int& jj, int& mm) {
+      const int a = pa < nbA ? (lA ? min(max(((const_i32*)lA)[pa], 0), i) : pa) : kEnd;
+      const int b = pb < nbB ? (lB ? min(max(((const_i32*)lB)[pb], 0), i) : pb) : kEnd;
+      jj = min(a, b);
+      mm = (a == jj ? 1 : 0) | (b == jj ? 2 : 0);
+      pa += mm & 1;
+      pb += mm >> 1;
     };
     const int my_bit = 1 << hs;
-    int pa = 0, pb = 0, j, mask;
-    peek(pa, pb, j, mask);
+    int j, mask, jn, maskn;                      // the current block and the next
+    next_block(j, mask);
+    next_block(jn, maskn);
+    int sub = 0;
+    // Step (block j, sub) computes from one buffer pair while the tiles of
+    // (jn, sub), two steps ahead, load into the pair the step before used
+    // (past the last block the current block's tiles load again, into a pair
+    // no later step reads, so every step issues the same loads).
+    auto step = [&](const char* kc, const char* vc, char* kn, char* vn) {
+      load_step(jn != kEnd ? jn : j, sub, kn, vn);
+      if (mask & my_bit)                         // uniform over the wave
+        attn_step<D, BLK>(j == i, kc, vc, sub * KT, qf, k_rd, v_rd, o, m_run, l_run, ref_mode,
+                          qi, hl);
+      wait_next();
+      if (sub == 1) {
+        j = jn;
+        mask = maskn;
+        next_block(jn, maskn);
+      }
+      sub ^= 1;
+    };
     if (j != kEnd) {
       load_step(j, 0, Ks0, Vs0);
-      step_barrier();
-    }
-    while (j != kEnd) {
-      pa += mask & 1;
-      pb += mask >> 1;
-      int j_next, mask_next;
-      peek(pa, pb, j_next, mask_next);
-      const bool has_next = j_next != kEnd;
-      const bool mine = (mask & my_bit) != 0;        // uniform over the wave
-#pragma unroll
-      for (int sub = 0; sub < TL::NSUB; ++sub) {
-        const bool odd = sub & 1;
-        const bool last_sub = sub + 1 == TL::NSUB;
-        if (!last_sub) load_step(j, sub + 1, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
-        else if (has_next) load_step(j_next, 0, odd ? Ks0 : Ks1, odd ? Vs0 : Vs1);
-        if (mine)
-          attn_step<D, BLK>(j == i, odd ? Ks1 : Ks0, odd ? Vs1 : Vs0, sub * KT, qf, k_rd, v_rd,
-                            o, m_run, l_run, ref_mode, qi, hl);
-        step_barrier();
+      load_step(j, 1, Ks1, Vs1);
+      wait_next();
+      for (;;) {
+        step(Ks0, Vs0, Ks2, Vs2);
+        if (j == kEnd) break;
+        step(Ks1, Vs1, Ks0, Vs0);
+        if (j == kEnd) break;
+        step(Ks2, Vs2, Ks1, Vs1);
+        if (j == kEnd) break;
       }
-      j = j_next;
-      mask = mask_next;
+      __builtin_amdgcn_s_waitcnt(0xF70);         // no tile load outlives the loop
     }
   }
 
