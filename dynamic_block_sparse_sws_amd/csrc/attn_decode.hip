@@ -72,6 +72,15 @@ template <> struct QVec<float> {
   }
 };
 
+// A wave-uniform read of a list, mask or page-table entry through the scalar
+// cache: a vector load there would make the wave wait for every K / V load
+// it has in flight before it can issue the next ones.
+template <typename T>
+__device__ __forceinline__ T scalar_read(const T* p, int i) {
+  typedef __attribute__((address_space(4))) const T const_t;
+  return ((const_t*)p)[i];
+}
+
 __device__ __forceinline__ float exp2_or_zero(float x) {
   return x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x);
 }
@@ -232,7 +241,8 @@ __device__ __forceinline__ void decode_range(
   const int last_blk = (ctx - 1) / BLK;
   const int ntok = (b - a) * BLK;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar list reads
   const int ch = lane % TPL;           // feature chunk (8 features)
   const int slot = lane / TPL;         // row group of the wave
   const int64_t seq_off = table ? 0 : (int64_t)seq * L.seq;
@@ -258,14 +268,14 @@ __device__ __forceinline__ void decode_range(
       const int e = a + tb / BLK;
       // list entries are blocks of the context; a stray one is clamped so every
       // access stays inside this sequence's rows
-      const int blk = min(max(ul ? ul[e] : e, 0), last_blk);
-      const uint32_t mk = um ? um[e] : 0xffffffffu;
+      const int blk = min(max(ul ? scalar_read(ul, e) : e, 0), last_blk);
+      const uint32_t mk = um ? scalar_read(um, e) : 0xffffffffu;
       const int r0 = blk * BLK + tb % BLK + slot;      // this lane's first cache row
       // Paged: the batch lies in one logical block, so one page; out-of-range
       // table entries are clamped (the caller's error, never a stray access).
       int64_t pbase = 0;
       if (trow) {
-        const int pg = min(max(trow[min(blk, table_width - 1)], 0), num_pages - 1);
+        const int pg = min(max(scalar_read(trow, min(blk, table_width - 1)), 0), num_pages - 1);
         pbase = (int64_t)pg * L.seq - (int64_t)blk * BLK * L.row;
       }
       Row8<TK> kr[UNR], vr[UNR];
@@ -489,7 +499,8 @@ __device__ __forceinline__ void mfma_range(
   const int ctx = min(max(ctx_len[seq], 1), L.rows);
   const int last_blk = (ctx - 1) / BLK;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar list reads
   const int col = lane & 15, grp = lane >> 4;
   const float sl2 = scale_log2 * kscale;
   __bf16* vt = vt_all + wave * D * kVtStride;
@@ -535,12 +546,12 @@ __device__ __forceinline__ void mfma_range(
                    int& key0) {
     const int tt = min(t, nstep - 1);
     const int e = a + tt / (BLK / KT);
-    const int blk = min(max(ul ? ul[e] : e, 0), last_blk);
-    mk = um ? um[e] : 0xffffffffu;
+    const int blk = min(max(ul ? scalar_read(ul, e) : e, 0), last_blk);
+    mk = um ? scalar_read(um, e) : 0xffffffffu;
     key0 = blk * BLK + (tt % (BLK / KT)) * KT;
     int64_t pbase = 0;
     if (trow) {
-      const int pg = min(max(trow[min(blk, table_width - 1)], 0), num_pages - 1);
+      const int pg = min(max(scalar_read(trow, min(blk, table_width - 1)), 0), num_pages - 1);
       pbase = (int64_t)pg * L.seq - (int64_t)blk * BLK * L.row;
     }
 #pragma unroll
