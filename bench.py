@@ -331,7 +331,7 @@ def bench_tiny(torch, sws, gen, reps=50):
     us = e0.elapsed_time(e1) * 1e3 / reps
     return {"workload": cfg.name, "us_per_stack": us, "us_per_layer": us / cfg.layers,
             "layers": cfg.layers, "dtype": "f32",
-            "note": "eager launches (5 per layer, outputs allocated by the binding); launch-latency bound"}
+            "note": "eager launches (5 per layer, outputs allocated by the binding); the host launches take most of the time"}
 
 
 def bench_decode(args, torch, sws, gen, timer_cls):

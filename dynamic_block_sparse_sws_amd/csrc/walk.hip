@@ -493,52 +493,61 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
     if (st % ntiles == ntiles - 1) __syncthreads();
     else lds_barrier();
     if (!last && !late) fetch((st + 1) / ntiles, I - (st + 1) % ntiles);
-    // ---- M_J^T quadrant (rows j of 32 wj.., columns m of 32 wi..) ----
     floatx16_t acc;
+    // ---- M_J^T quadrant (rows j of 32 wj.., columns m of 32 wi..) ----
+    // (a single column tile: M_J is the same at every hop, formed once)
+    if (!late || st == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int t = 0; t < kWmK / 2; ++t)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[32 * wj + lc][16 * lh + t],
-                                                 Qs[32 * wi + lc][16 * lh + t], acc, 0, 0, 0);
+      for (int t = 0; t < kWmK / 2; ++t)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[32 * wj + lc][16 * lh + t],
+                                                   Qs[32 * wi + lc][16 * lh + t], acc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = 32 * wj + 8 * (r >> 2) + 4 * lh + (r & 3);
-      const int m = 32 * wi + lc;
-      Ms[j][m] = j <= m ? acc[r] : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int j = 32 * wj + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int m = 32 * wi + lc;
+        Ms[j][m] = j <= m ? acc[r] : 0.f;
+      }
+      lds_barrier();
     }
-    lds_barrier();
     // ---- Y quadrant (rows 32 wi.., columns 32 wj..) and the carry part ----
+    // (a single column tile has no later tiles: the carry is zero and unused)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll 8
     for (int t = 0; t < kWmRows / 2; ++t)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[32 * wi + lc][32 * lh + t],
                                                  Ms[32 * wj + lc][32 * lh + t], acc, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < kWmK / 2; ++t)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(
-          Cs[0][32 * wi + lc][16 * lh + t] + Cs[1][32 * wi + lc][16 * lh + t],
-          Ks[32 * wj + lc][16 * lh + t], acc, 0, 0, 0);
     floatx16_t cp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) cp[r] = 0.f;
+    if (!late) {
 #pragma unroll
-    for (int t = 0; t < kWmRows / 4; ++t)
-      cp = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[32 * wi + lc][32 * wj + 16 * lh + t],
-                                                QTs[lc][32 * wj + 16 * lh + t], cp, 0, 0, 0);
+      for (int t = 0; t < kWmK / 2; ++t)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(
+            Cs[0][32 * wi + lc][16 * lh + t] + Cs[1][32 * wi + lc][16 * lh + t],
+            Ks[32 * wj + lc][16 * lh + t], acc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < kWmRows / 4; ++t)
+        cp = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[32 * wi + lc][32 * wj + 16 * lh + t],
+                                                  QTs[lc][32 * wj + 16 * lh + t], cp, 0, 0, 0);
+    }
     lds_barrier();
     // carry partial wj of rows 32 wi.. (this wave's own block), Y into Xs
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * wi + 8 * (r >> 2) + 4 * lh + (r & 3);
-      Cs[wj][i][lc] += cp[r];
+      if (!late) Cs[wj][i][lc] += cp[r];
       const int j = 32 * wj + lc;
       const bool ok = i0 + i < b && jt * kWmRows + j <= i0 + i;
       Xs[i][j] = ok ? acc[r] * inv_sqrt_k : 0.f;
     }
     lds_barrier();
     // ---- write the tile back, row maxima ----
+    // (a single column tile keeps the hop's output in registers as the next
+    // hop's input, in the layout of the plain tile loads, and writes it to
+    // memory only after the last hop)
     {
       const int ig = i0 + sr;
       const int jg0 = jt * kWmRows + sp * 16;
@@ -550,7 +559,11 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)),
                              fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
       }
-      if (plain_rows && jt < I) {                 // uniform
+      if (late && !last) {                        // uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[e] = v[e];
+        xrow = false;
+      } else if (plain_rows && jt < I) {          // uniform
         float* dst = Rh + (int64_t)ig * b + jg0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) reinterpret_cast<float4*>(dst)[e] = v[e];
@@ -567,10 +580,6 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mx = fmaxf(mx, __shfl_xor(mx, 2));
       if (sp == 0) rmax[sr] = fmaxf(rmax[sr], mx);
-    }
-    if (!last && late) {
-      __syncthreads();
-      fetch((st + 1) / ntiles, I - (st + 1) % ntiles);
     }
     if (last) __syncthreads();        // the final pass reads other threads' stores
     else lds_barrier();

@@ -45,7 +45,7 @@ def test_bf16_gqa_ragged(d, B, seqlens, hq, hkv, rho):
     _print("worst", w)
 
 
-@pytest.mark.parametrize("d,B", [(128, 128), (64, 64)])
+@pytest.mark.parametrize("d,B", [(128, 128), (64, 64), (128, 64), (64, 128)])
 def test_fp32_path_ragged(d, B):
     cfg = gen.CONFIGS["C2"].with_(d=d, B=B, hq=4, hkv=2, k=16, dtype="f32")
     seqlens = (3 * B + 5, B - 3)
