@@ -29,7 +29,7 @@ LIB = os.path.join(PKG, "libsws.so")
 LIB_ASAN = os.path.join(PKG, "libsws_asan.so")
 PROBE = os.path.join(PKG, "ceiling_probe")
 SOURCES = ["sws_api.hip", "sketch.hip", "walk.hip", "walk_variant.hip", "select.hip",
-           "attn_prefill.hip", "attn_decode.hip"]
+           "attn_prefill.hip", "attn_prefill_f32.hip", "attn_decode.hip"]
 ARCH = os.environ.get("SWS_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [
