@@ -25,6 +25,8 @@
 // the wave totals in LDS.
 #include "sws_common.h"
 
+#include <type_traits>
+
 namespace sws {
 namespace {
 
@@ -308,7 +310,10 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kWmPad = 68;        // LDS row pitch of 64-wide tiles (floats)
 constexpr int kWmPadK = 36;       // LDS row pitch of 32-wide tiles
 
-template <bool K32>
+// ONE: every row tile has a single column tile (b <= 64 blocks); that form
+// keeps the walk state on chip across hops (see below) and is compiled
+// separately, so the multi-tile form's code is not disturbed by it.
+template <bool K32, bool ONE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ k_sk, int hq,
                       int hkv, int k, const int32_t* __restrict__ cu_blocks, int n_seqs,
@@ -358,6 +363,7 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   const bool plain_rows = i0 + kWmRows <= b && (b & 3) == 0;
   const int row0 = i0 + 16 * __builtin_amdgcn_readfirstlane(w);   // a wave's first row (xrow)
   bool xrow = false;
+  bool xin_lds = false;       // the next X is the last Y, left in Xs (ONE)
   auto fetch = [&](int hop, int jt) {
     const int ig = i0 + sr;
     const int jg0 = jt * kWmRows + sp * 16;
@@ -419,7 +425,20 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   };
   auto stash = [&]() {
     // the previous hop's output, scaled and cut to the walk floor
-    if (xrow) {
+    if (ONE && xin_lds) {
+      // still in Xs (a single column tile): this thread's 16 entries of row sr
+      const float sc = rsc[sr], th = rthr[sr];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float4 v = *reinterpret_cast<const float4*>(&Xs[sr][sp * 16 + 4 * e]);
+        v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+        v.x = fabsf(v.x) < th ? 0.f : v.x;
+        v.y = fabsf(v.y) < th ? 0.f : v.y;
+        v.z = fabsf(v.z) < th ? 0.f : v.z;
+        v.w = fabsf(v.w) < th ? 0.f : v.w;
+        *reinterpret_cast<float4*>(&Xs[sr][sp * 16 + 4 * e]) = v;
+      }
+    } else if (xrow) {
       float v[16];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -489,14 +508,14 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
     // the full barriers that open it.  With a single tile the fetch waits for
     // the write-back below instead.
     const bool last = st + 1 == nsteps;
-    const bool late = ntiles == 1;
+    const bool late = ONE || ntiles == 1;
     if (st % ntiles == ntiles - 1) __syncthreads();
     else lds_barrier();
     if (!last && !late) fetch((st + 1) / ntiles, I - (st + 1) % ntiles);
     floatx16_t acc;
     // ---- M_J^T quadrant (rows j of 32 wj.., columns m of 32 wi..) ----
-    // (a single column tile: M_J is the same at every hop, formed once)
-    if (!late || st == 0) {
+    // (ONE: M_J is the same at every hop, formed once)
+    if (!ONE || st == 0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
@@ -512,17 +531,17 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
       lds_barrier();
     }
     // ---- Y quadrant (rows 32 wi.., columns 32 wj..) and the carry part ----
-    // (a single column tile has no later tiles: the carry is zero and unused)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll 8
     for (int t = 0; t < kWmRows / 2; ++t)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[32 * wi + lc][32 * lh + t],
                                                  Ms[32 * wj + lc][32 * lh + t], acc, 0, 0, 0);
+    // (ONE: no later column tiles, so the carry is zero and unused)
     floatx16_t cp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) cp[r] = 0.f;
-    if (!late) {
+    if constexpr (!ONE) {
 #pragma unroll
       for (int t = 0; t < kWmK / 2; ++t)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(
@@ -538,16 +557,16 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * wi + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (!late) Cs[wj][i][lc] += cp[r];
+      if constexpr (!ONE) Cs[wj][i][lc] += cp[r];
       const int j = 32 * wj + lc;
       const bool ok = i0 + i < b && jt * kWmRows + j <= i0 + i;
       Xs[i][j] = ok ? acc[r] * inv_sqrt_k : 0.f;
     }
     lds_barrier();
     // ---- write the tile back, row maxima ----
-    // (a single column tile keeps the hop's output in registers as the next
-    // hop's input, in the layout of the plain tile loads, and writes it to
-    // memory only after the last hop)
+    // (ONE leaves the hop's output in Xs as the next hop's input, scaled and
+    // cut there by the stash, and writes it to memory only after the last
+    // hop)
     {
       const int ig = i0 + sr;
       const int jg0 = jt * kWmRows + sp * 16;
@@ -559,10 +578,8 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[e].x), fabsf(v[e].y)),
                              fmaxf(fabsf(v[e].z), fabsf(v[e].w))));
       }
-      if (late && !last) {                        // uniform
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xv[e] = v[e];
-        xrow = false;
+      if (ONE && !last) {
+        xin_lds = true;
       } else if (plain_rows && jt < I) {          // uniform
         float* dst = Rh + (int64_t)ig * b + jg0;
 #pragma unroll
@@ -580,6 +597,10 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mx = fmaxf(mx, __shfl_xor(mx, 2));
       if (sp == 0) rmax[sr] = fmaxf(rmax[sr], mx);
+    }
+    if (!ONE && !last && late) {
+      __syncthreads();
+      fetch((st + 1) / ntiles, I - (st + 1) % ntiles);
     }
     if (last) __syncthreads();        // the final pass reads other threads' stores
     else lds_barrier();
@@ -1150,14 +1171,20 @@ hipError_t launch_walk(const float* q_sk, const float* k_sk, int hq, int hkv, in
   if (k <= kWmK && (k & 3) == 0) {
     const int n_row_tiles = (max_blocks + kWmRows - 1) / kWmRows;
     dim3 grid(n_row_tiles * hq * n_seqs);
-    if (k == kWmK)
-      hipLaunchKernelGGL(walk_mfma_kernel<true>, grid, dim3(256), 0, st, q_sk, k_sk, hq, hkv, k,
-                         cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
-                         1.0f / sqrtf((float)k));
-    else
-      hipLaunchKernelGGL(walk_mfma_kernel<false>, grid, dim3(256), 0, st, q_sk, k_sk, hq, hkv,
-                         k, cu_blocks, n_seqs, total_blocks, n_row_tiles, s, R_prev, R_out,
-                         1.0f / sqrtf((float)k));
+    auto launch = [&](auto k32, auto one) {
+      hipLaunchKernelGGL((walk_mfma_kernel<decltype(k32)::value, decltype(one)::value>), grid,
+                         dim3(256), 0, st, q_sk, k_sk, hq, hkv, k, cu_blocks, n_seqs,
+                         total_blocks, n_row_tiles, s, R_prev, R_out, 1.0f / sqrtf((float)k));
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (k == kWmK) {
+      if (n_row_tiles == 1) launch(T_{}, T_{});
+      else launch(T_{}, F_{});
+    } else {
+      if (n_row_tiles == 1) launch(F_{}, T_{});
+      else launch(F_{}, F_{});
+    }
     return hipGetLastError();
   }
   if (k <= 16)
