@@ -134,9 +134,14 @@ __global__ __launch_bounds__(kThreads) void sketch_append_kernel(
     float v[8];
     load8_f32(a.x + base, v);
     float* rs = a.run_sum + base;
+    // the running sums are loaded whether or not the token opens a block, so
+    // the load does not wait for pos (an opening token then drops them)
+    const float4 r0 = reinterpret_cast<const float4*>(rs)[0];
+    const float4 r1 = reinterpret_cast<const float4*>(rs)[1];
+    const float old[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float sum = (off == 0) ? v[e] : rs[e] + v[e];
+      const float sum = (off == 0) ? v[e] : old[e] + v[e];
       rs[e] = sum;
       const int r = (col + e) % D;
       f[col + e] = (sum * inv_cnt) * (float)signs[r];
