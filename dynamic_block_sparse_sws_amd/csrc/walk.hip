@@ -104,6 +104,52 @@ __device__ __forceinline__ void walk_tile_of(int id, int P, int n_row_tiles, int
   I = slot < half ? n_row_tiles - 1 - slot : slot - half;
 }
 
+
+// Ragged batches: every (sequence, head, row tile) tile in descending length,
+// longest first across the sequences, the order a greedy schedule over the
+// CUs wants when tile lengths differ from sequence to sequence (the mapping
+// above pairs long and short tiles of equal-length rows instead).  Level L
+// holds the tiles I = L - 1 of the pairs whose sequence has at least L row
+// tiles (nt[s] = row tiles of sequence s, in LDS).  Returns false past the
+// last tile.
+__device__ __forceinline__ bool walk_tile_ragged(int id, int hq, int n_seqs, const int* nt,
+                                                 int n_row_tiles, int& p, int& I) {
+  int base = 0;
+  for (int L = n_row_tiles; L >= 1; --L) {
+    int cnt = 0;
+    for (int s = 0; s < n_seqs; ++s) cnt += nt[s] >= L;
+    if (id < base + cnt * hq) {
+      const int k = id - base;
+      int want = k / hq, s = 0;
+      for (; s < n_seqs; ++s)
+        if (nt[s] >= L && want-- == 0) break;
+      p = s * hq + k % hq;
+      I = L - 1;
+      return true;
+    }
+    base += cnt * hq;
+  }
+  return false;
+}
+constexpr int kRaggedMaxSeqs = 64;   // larger batches keep the mapping above
+
+// (sequence x head, row tile) of workgroup `id`: the ragged order for 2 to
+// kRaggedMaxSeqs sequences (all threads call it: it fills and syncs an LDS
+// table), else walk_tile_of.  False: no tile for this workgroup.
+__device__ __forceinline__ bool walk_tile(int id, int hq, int n_seqs,
+                                          const int32_t* __restrict__ cu_blocks, int n_row_tiles,
+                                          int tile_rows, int* s_nt, int& p, int& I) {
+  if (n_seqs > 1 && n_seqs <= kRaggedMaxSeqs) {
+    if ((int)threadIdx.x < n_seqs)
+      s_nt[threadIdx.x] =
+          (cu_blocks[threadIdx.x + 1] - cu_blocks[threadIdx.x] + tile_rows - 1) / tile_rows;
+    __syncthreads();
+    return walk_tile_ragged(id, hq, n_seqs, s_nt, n_row_tiles, p, I);
+  }
+  walk_tile_of(id, hq * n_seqs, n_row_tiles, p, I);
+  return true;
+}
+
 constexpr int kWalkThreads = 256;
 constexpr int kTileJ = 64;
 
@@ -129,7 +175,9 @@ void walk_kernel(
   __shared__ float smax[ROWS];
 
   int pid, tile;
-  walk_tile_of((int)blockIdx.x, hq * n_seqs, n_row_tiles, pid, tile);
+  __shared__ int s_nt[kRaggedMaxSeqs];
+  if (!walk_tile((int)blockIdx.x, hq, n_seqs, cu_blocks, n_row_tiles, ROWS, s_nt, pid, tile))
+    return;
   const int seq = pid / hq;
   const int h = pid % hq;
   const int b0 = cu_blocks[seq];
@@ -327,8 +375,10 @@ void walk_mfma_kernel(const float* __restrict__ q_sk, const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) float Cs[2][kWmRows][kWmPadK]; // carry partials
   __shared__ float rmax[kWmRows], rsc[kWmRows], rthr[kWmRows];
 
+  __shared__ int s_nt[kRaggedMaxSeqs];
   int pid, I;
-  walk_tile_of((int)blockIdx.x, hq * n_seqs, n_row_tiles, pid, I);
+  if (!walk_tile((int)blockIdx.x, hq, n_seqs, cu_blocks, n_row_tiles, kWmRows, s_nt, pid, I))
+    return;
   const int seq = pid / hq;
   const int h = pid % hq;
   const int b0 = cu_blocks[seq];
