@@ -55,6 +55,22 @@ def test_fp32_path_ragged(d, B):
     _print("worst", w)
 
 
+@pytest.mark.parametrize("nseq,lo,hi", [(12, 65, 200), (70, 1, 140)])
+def test_walk_ragged_tile_orders(nseq, lo, hi):
+    """Ragged batches whose rows span several 64-row walk tiles: the
+    longest-first tile order over 2 to 64 sequences (12 sequences here) and
+    the plain order past 64 sequences (70) must compute every tile exactly
+    once; every stage of two layers against the oracle."""
+    rng = np.random.default_rng(100 + nseq)
+    blocks = rng.integers(lo, hi + 1, size=nseq)
+    seqlens = tuple(max(1, int(b) * 64 - int(rng.integers(0, 64))) for b in blocks)
+    cfg = gen.CONFIGS["C2"].with_(hq=2, hkv=1, B=64, k=32)
+    _print("ragged walk tiles", nseq, max(seqlens), min(seqlens))
+    run = PrefillRun(cfg, seqlens, 2, 20, n_dense=0)
+    w = check_prefill_run(run, attn_rows_per_head=3)
+    _print("worst", w)
+
+
 def test_dense_null_lists_equal_full_lists():
     """idx == NULL (dense causal) gives the same output as explicit full
     lists, and both match the oracle's dense attention."""
