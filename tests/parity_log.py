@@ -1,7 +1,7 @@
 """Worst errors seen by the GPU parity tests, per workload and stage, plus
-per-layer drift curves; conftest.py writes them as JSON when the session
-ends (gpurun_out/parity_margins.json), so each run keeps its margins against
-the bars."""
+per-layer drift curves; conftest.py writes them as JSON (parity_margins.json
+in the run's output folder) when the session ends, so each run keeps its
+margins against the bars."""
 from __future__ import annotations
 
 import json
