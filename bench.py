@@ -1029,7 +1029,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1",
                           "n_gpus": max(args.gpus, world)}))
         sys.exit(2)
     import torch

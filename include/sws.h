@@ -50,7 +50,7 @@ typedef enum sws_status {
   SWS_OK = 0,
   SWS_ERR_NULL = 1,         /* a required pointer is NULL                        */
   SWS_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes                */
-  SWS_ERR_UNSUPPORTED = 3,  /* a size or dtype this build has no kernel for      */
+  SWS_ERR_UNSUPPORTED = 3,  /* a size or dtype the library has no kernel for     */
   SWS_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required           */
   SWS_ERR_LAUNCH = 5        /* the HIP runtime rejected a kernel launch          */
 } sws_status;
