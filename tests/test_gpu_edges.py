@@ -390,3 +390,53 @@ def test_prefill_softmax_reference_and_rescale(B, hq, hkv, jump):
             assert e <= TOL_ATTN_BF16, (h, i, "attn", e)
             assert e2 <= TOL_ATTN_BF16, (h, i, "lse", e2)
     _print("softmax paths", B, hq, hkv, jump, "worst", worst)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_zero_length_sequences(dtype):
+    """Sequences of no tokens inside a ragged batch: every stage (sketches,
+    walk state over two layers, lists, attention and lse) equals, bit for
+    bit, the same call on the batch without them, on the same tensors (the
+    empty sequences own no blocks and no walk rows); the sketches of the
+    others also match the oracle."""
+    cfg = gen.CONFIGS["C2"].with_(hq=4, hkv=2, B=64, k=32, dtype=dtype)
+    lens_with = [0, 300, 0, 129, 0, 64]
+    lens_without = [n for n in lens_with if n > 0]
+    signs, cols = gen.hadamard_tables(cfg.d, cfg.k)
+    sd, cd = torch.from_numpy(signs).cuda(), torch.from_numpy(cols).cuda()
+    layers = [gen.layer_inputs(cfg, l, device="cuda", seqlens=lens_without)[:3] for l in range(2)]
+    results = []
+    for lens in (lens_with, lens_without):
+        geo = sws.Geometry(lens, cfg.B)
+        R = torch.empty(geo.walk_numel(cfg.hq), dtype=torch.float32, device="cuda")
+        per_layer = []
+        for li, (q, k, v) in enumerate(layers):
+            lse = torch.empty((cfg.hq, geo.total_tokens), dtype=torch.float32, device="cuda")
+            r = sws.prefill_layer(q, k, v, geo, cfg.k, sd, cd, cfg.s, cfg.rho, False, R,
+                                  first_layer=li == 0)
+            r["out"] = sws.sparse_attn_prefill(q, k, v, geo, r["idx"], r["cnt"], lse=lse)
+            torch.cuda.synchronize()
+            per_layer.append({key: r[key].float().cpu().numpy() if key != "idx" and key != "cnt"
+                              else r[key].cpu().numpy()
+                              for key in ("q_sk", "k_sk", "R", "idx", "cnt", "out")}
+                             | {"lse": lse.cpu().numpy()})
+        results.append(per_layer)
+    for li in range(2):
+        a, b = results[0][li], results[1][li]
+        for key in ("q_sk", "k_sk", "R", "cnt", "out", "lse"):
+            assert np.array_equal(a[key], b[key]), (dtype, li, key)
+        # list entries up to each count (past it the lists are not defined)
+        for h in range(cfg.hq):
+            for g in range(a["cnt"].shape[1]):
+                c = int(a["cnt"][h, g])
+                assert np.array_equal(a["idx"][h, g, :c], b["idx"][h, g, :c]), (dtype, li, h, g)
+    # the remaining sequences' sketches against the oracle (first layer)
+    geo = sws.Geometry(lens_without, cfg.B)
+    q = f64(layers[0][0])
+    for s, n in enumerate(lens_without):
+        t0, b0, nb = int(geo.cu_seqlens_host[s]), int(geo.cu_blocks_host[s]), geo.blocks[s]
+        for h in range(cfg.hq):
+            want = O.sketch(q[t0:t0 + n, h], cfg.B, signs, cols)
+            got = results[0][0]["q_sk"][h, b0:b0 + nb]
+            assert rowwise_rel_err(got, want) <= 1e-4, (dtype, s, h)
+    _print("zero-length sequences", dtype, "ok")
