@@ -742,3 +742,61 @@ def test_decode_large_scores_across_splits(dtype, d, B, hq, hkv, lens):
     s2 = (Q[sl, 0] / 8.0) @ K[sl, :lens[sl], 0].T
     assert s2.max() - np.abs(s2[:32]).max() > 128
     _print("decode large scores", dtype, d, B, hq, hkv, lens, "worst", worst)
+
+
+def test_decode_at_the_pair_limit():
+    """The largest decode batch the C ABI takes: 1024 sequences x 8 KV heads
+    = 8192 (sequence, KV head) pairs (the split kernels' plan fills its whole
+    LDS table), short contexts of 1 to 200 tokens, random union lists with
+    random head masks (every head keeps the open block): every (sequence,
+    head) against the oracle.  One pair more is rejected on the host."""
+    ns, hq, hkv, d, B = 1024, 16, 8, 64, 64
+    grp = hq // hkv
+    rng = np.random.default_rng(2048)
+    lens = rng.integers(1, 201, size=ns)
+    max_ctx = int(lens.max())
+    uw = -(-max_ctx // B)
+    uidx = np.zeros((ns, hkv, uw), np.int32)
+    ucnt = np.zeros((ns, hkv), np.int32)
+    umask = np.zeros((ns, hkv, uw), np.int32)
+    for s in range(ns):
+        nb = -(-int(lens[s]) // B)
+        for g in range(hkv):
+            keep = [j for j in range(nb - 1) if rng.random() < 0.5] + [nb - 1]
+            ucnt[s, g] = len(keep)
+            uidx[s, g, :len(keep)] = keep
+            for e in range(len(keep)):
+                umask[s, g, e] = (1 << grp) - 1 if e == len(keep) - 1 else int(rng.integers(1, 1 << grp))
+    g_ = torch.Generator(device="cuda")
+    g_.manual_seed(gen.seed_for(17, ns, hkv))
+    kc = torch.randn((ns, max_ctx, hkv, d), generator=g_, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((ns, max_ctx, hkv, d), generator=g_, device="cuda").to(torch.bfloat16)
+    q = torch.randn((ns, hq, d), generator=g_, device="cuda").to(torch.bfloat16)
+    ctx = torch.from_numpy(lens.astype(np.int32)).cuda()
+    lse = torch.empty((ns, hq), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    out = sws.sparse_attn_decode(q, kc, vc, ctx, B, torch.from_numpy(uidx).cuda(),
+                                 torch.from_numpy(ucnt).cuda(), torch.from_numpy(umask).cuda(),
+                                 scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    Q, K, V, Og, Lg = f64(q), f64(kc), f64(vc), f64(out), f64(lse)
+    worst = 0.0
+    for s in range(ns):
+        n = int(lens[s])
+        for h in range(hq):
+            g, hb = h // grp, 1 << (h % grp)
+            lst = [int(uidx[s, g, e]) for e in range(ucnt[s, g]) if umask[s, g, e] & hb]
+            o_want, lse_want = O.query_attention(Q[s, h], K[s, :, g], V[s, :, g], lst, B, n - 1,
+                                                 scale)
+            e = float(np.abs(Og[s, h] - o_want).max())
+            worst = max(worst, e)
+            assert e <= TOL_ATTN_BF16, (s, h, e)
+            assert abs(Lg[s, h] - lse_want) <= TOL_ATTN_BF16, (s, h)
+    # one pair past the limit (8193 sequences x 1 KV head): rejected before any launch
+    q1 = torch.zeros((8193, hq, d), dtype=torch.bfloat16, device="cuda")
+    k1 = torch.zeros((8193, 1, 1, d), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sws.SwsError) as ei:
+        sws.sparse_attn_decode(q1, k1, k1, torch.ones(8193, dtype=torch.int32, device="cuda"), B,
+                               None, None, None, scale=scale)
+    assert ei.value.code == 3
+    _print("decode pair limit", ns * hkv, "worst", worst)
